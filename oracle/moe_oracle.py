@@ -1,0 +1,390 @@
+"""Plain CPU oracle of one Mixture-of-Experts layer's forward pass (numpy float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
+this module: only the test-suite, the package-level ``smoke()`` entry and the
+CPU-baseline leg of the benchmark use it.  It shares no code, constants or
+helpers with the HIP library; both sides only receive the same seeded inputs.
+
+Every function follows a passage of the source pages; citations name the page
+and its section:
+
+* [Book 14.2.1]  LLM Internals, section 14.2 "Mixture-of-Experts models", 14.2.1
+  "One MoE forward pass: six steps and shapes" (steps 1-6).
+* [Book 14.2.2]  same page, 14.2.2 "How active parameters are counted" (one
+  SwiGLU expert is three [7168, 2048] matrices).
+* [Book 14.2.3]  same page, 14.2.3 "Routing and load balancing": the balance
+  loss alpha*N*sum f_i p_i and its worked example; the bias-for-selection rule
+  (DeepSeek-V3 report eq. 16); capacity factor and token dropping.
+* [Book 14.2.4]  same page, 14.2.4 "Fine-grained MoE and shared experts".
+* [KMap router]  AI Knowledge Map, "Mixture of Experts (MoE)", the four router
+  steps: score W_r x, softmax, top-k hard selection, renormalise inside the
+  chosen set S and combine y = sum_{e in S} g^_e E_e(x).
+* [KMap capacity] same page, the capacity formula C = ceil(c*N*k/E) and its
+  6-token / 4-expert / top-2 worked example, overflow handling by drop.
+* [Study case 1] estelledc study note "Mixture of Experts (MoE)", practice
+  case 1: the minimal top-k routing pseudo-code (router -> top-k -> softmax
+  over the k kept scores -> weighted sum of the chosen experts).
+* [Study pitfalls] same note, "pitfalls": the router softmax runs in fp32.
+
+Readings where the pages are silent or ambiguous (each one also listed in the
+design notes of the repository):
+
+R1  SwiGLU expert: h = silu(x W1) * (x W3), y = h W2; W1 is the gate, W3 the up
+    projection, silu(z) = z / (1 + exp(-z)).  The pages give only "three
+    [d, F] matrices".
+R2  Logical weight shapes (the pages' notation): W_g[d, E], W1/W3[E, d, F],
+    W2[E, F, d].  The oracle works on these logical shapes.
+R3  Top-k order: key descending, ties to the lower expert id.
+R4  Softmax routers select on the logit (same set as selecting on p, free of
+    exp-rounding ties); sigmoid routers select on s + b (eq. 16).
+R5  Renormalisation happens over S before any capacity drop; kept gates are not
+    renormalised again after a drop.
+R6  Overflow priority: slot s = t*k + j; an expert keeps the first C slots in
+    increasing slot order (lowest token index first).
+R7  Capacity C = ceil(c*N*k/E) in exact rational arithmetic, c taken as the
+    decimal number its shortest repr spells.
+R8  f_e = pre-drop count_e / (T*k);  P_e = mean over tokens of the full-row
+    score (softmax p, or sigmoid s); statistic = E * sum_e f_e P_e (alpha
+    omitted).
+R9  bf16 mode: the activation h is rounded to bf16 (round-to-nearest-even)
+    before the down projection, mirroring a bf16 matrix-core input; all other
+    intermediates stay exact.
+R10 Shared expert: same width F, weight 1, added to every token's output.
+R11 Optional per-expert logit offset o_e is added to the logits before scoring.
+
+Parity status: every function here is pinned by the CPU tests (worked examples
+printed on the pages, closed forms, brute force and cross-tier agreement).  The
+bf16 rounding of h (R9) is a reading, pinned only by its own RNE unit test.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "capacity", "router_logits", "scores", "select_topk", "gates", "route",
+    "dispatch", "silu", "round_bf16", "expert_ffn", "forward",
+    "forward_token_loop", "forward_dense_masked", "balance_value",
+    "balance_stat", "expert_weight_shapes",
+]
+
+
+# ---------------------------------------------------------------- capacity --
+def capacity(cf: float, n_tokens: int, k: int, n_experts: int) -> int:
+    """C = ceil(c * N * k / E)  [KMap capacity]; GShard form [Book 14.2.3].
+
+    c is read as the exact decimal that its shortest repr spells (reading R7),
+    so 1.25 * 8192 * 2 / 64 is exactly 320 and 1.1 * 10 is exactly 11.
+    """
+    if not (cf > 0) or n_tokens < 0 or k < 1 or n_experts < 1:
+        raise ValueError("capacity needs cf > 0, N >= 0, k >= 1, E >= 1")
+    c = Fraction(repr(float(cf)))
+    return math.ceil(c * n_tokens * k / n_experts)
+
+
+# ----------------------------------------------------------------- routing --
+def router_logits(X, Wg, offset=None):
+    """Step 2 [Book 14.2.1]: s = X[T,d] x W_g[d,E]; [KMap router] step 1.
+
+    ``offset`` (length E) is an optional per-expert additive logit term (R11).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Wg = np.asarray(Wg, dtype=np.float64)
+    lg = X @ Wg
+    if offset is not None:
+        lg = lg + np.asarray(offset, dtype=np.float64)[None, :]
+    return lg
+
+
+def scores(logits, score_func: str):
+    """Per-row softmax over all E experts [KMap router] step 2, or the
+    per-cell sigmoid affinity of DeepSeek-V3 [Book 14.2.1] step 2."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if score_func == "softmax":
+        m = lg.max(axis=1, keepdims=True)
+        ex = np.exp(lg - m)
+        return ex / ex.sum(axis=1, keepdims=True)
+    if score_func == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-lg))
+    raise ValueError(score_func)
+
+
+def select_topk(logits, k: int, score_func: str, bias=None):
+    """Top-k hard selection [Book 14.2.1] step 3, [KMap router] step 3.
+
+    Key: the logit for a softmax router (R4); s + b for a sigmoid router with a
+    selection-only bias (eq. 16, [Book 14.2.3]).  Returns ids [T,k] ordered by
+    key descending, ties to the lower id (R3), and the keys themselves.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    if score_func == "softmax":
+        key = lg.copy()
+    else:
+        key = scores(lg, "sigmoid")
+        if bias is not None:
+            key = key + np.asarray(bias, dtype=np.float64)[None, :]
+    ids = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        # a stable sort of -key keeps equal keys in ascending id order
+        order = np.argsort(-key[t], kind="stable")
+        ids[t] = order[:k]
+    return ids, key
+
+
+def gates(logits, ids, score_func: str, renorm: bool):
+    """Gate weights of the chosen experts.
+
+    renorm: g^_e = g_e / sum_{e' in S} g_e' ([KMap router] step 4, eqs. 13-14 in
+    [Book 14.2.1] step 3); for a sigmoid router g is the raw affinity s, never
+    s + b (eq. 16, [Book 14.2.3]).  Without renorm the raw score is the gate.
+    """
+    p = scores(logits, score_func)
+    g = np.take_along_axis(p, np.asarray(ids), axis=1)
+    if renorm:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g
+
+
+def route(logits, k, score_func, renorm, bias=None):
+    """Steps 2-3 on given logits: ids [T,k], gates [T,k], full scores [T,E]."""
+    ids, _ = select_topk(logits, k, score_func, bias)
+    g = gates(logits, ids, score_func, renorm)
+    return ids, g, scores(logits, score_func)
+
+
+# ---------------------------------------------------------------- dispatch --
+def dispatch(ids, n_experts: int, cap=None):
+    """Step 4 [Book 14.2.1] with the capacity drop of [KMap capacity].
+
+    Slot s = t*k + j.  Its rank is the number of earlier slots that chose the
+    same expert (R6); it is kept iff rank < C.  Returns a dict with
+      counts[E]      pre-drop requests per expert
+      kept[E]        min(counts, C)
+      offsets[E+1]   exclusive scan of kept
+      sorted_slot[R] kept slots grouped by expert, increasing slot order inside
+      slot_row[T*k]  row of slot s in the sorted buffer, -1 if dropped
+      n_kept         R
+    Written as a plain first-come loop over slots.
+    """
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    E = int(n_experts)
+    counts = [0] * E
+    rank = [0] * flat.size
+    for s, e in enumerate(flat.tolist()):
+        if not 0 <= e < E:
+            raise ValueError("expert id out of range")
+        rank[s] = counts[e]
+        counts[e] += 1
+    C = None if cap is None or cap <= 0 else int(cap)
+    kept = [c if C is None else min(c, C) for c in counts]
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + kept[e])
+    R = offsets[-1]
+    sorted_slot = [-1] * R
+    slot_row = [-1] * flat.size
+    for s, e in enumerate(flat.tolist()):
+        if C is None or rank[s] < C:
+            row = offsets[e] + rank[s]
+            sorted_slot[row] = s
+            slot_row[s] = row
+    return {
+        "counts": np.array(counts, dtype=np.int64),
+        "kept": np.array(kept, dtype=np.int64),
+        "offsets": np.array(offsets, dtype=np.int64),
+        "sorted_slot": np.array(sorted_slot, dtype=np.int64),
+        "slot_row": np.array(slot_row, dtype=np.int64),
+        "n_kept": int(R),
+    }
+
+
+# ------------------------------------------------------------- expert FFN --
+def silu(z):
+    """silu(z) = z * sigmoid(z) (R1)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (8 significant bits),
+    ties to even (R9).  Written from the format definition: keep 8 bits of
+    significand, round-half-even via np.rint."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)              # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def expert_weight_shapes(d: int, F: int):
+    """Shapes of one SwiGLU expert's three matrices [Book 14.2.2] (R1, R2)."""
+    return {"W1": (d, F), "W3": (d, F), "W2": (F, d)}
+
+
+def expert_ffn(x, W1, W3, W2, bf16_h: bool = False):
+    """One SwiGLU expert on rows x[m,d]: (silu(x W1) * (x W3)) W2  (R1, R9).
+
+    Step 5 of [Book 14.2.1]: [m_i, d] x W_i[d, F] -> [m_i, F], projected back to d.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    h = silu(x @ np.asarray(W1, np.float64)) * (x @ np.asarray(W3, np.float64))
+    if bf16_h:
+        h = round_bf16(h)
+    return h @ np.asarray(W2, np.float64)
+
+
+# ----------------------------------------------------------------- forward --
+def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
+            bias=None, offset=None, cap=None, shared=None, bf16_h=False,
+            logits=None):
+    """Tier 1: the six steps of [Book 14.2.1] with per-expert matmuls.
+
+    X[T,d]; Wg[d,E]; W1,W3[E,d,F]; W2[E,F,d]; shared = (W1s[d,F], W3s[d,F],
+    W2s[F,d]) or None.  ``logits`` (e.g. the device's fp32 logits) replaces
+    the oracle's own scoring for the routing decision when given.
+    Returns a dict with every intermediate.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    T, d = X.shape
+    E = np.asarray(Wg).shape[1]
+    own = router_logits(X, Wg, offset)
+    lg = own if logits is None else np.asarray(logits, dtype=np.float64)
+    ids, g, p = route(lg, k, score_func, renorm, bias)
+    disp = dispatch(ids, E, cap)
+    rows = np.zeros((disp["n_kept"], d))
+    for e in range(E):
+        a, b = disp["offsets"][e], disp["offsets"][e + 1]
+        if b > a:
+            tok = disp["sorted_slot"][a:b] // k
+            rows[a:b] = expert_ffn(X[tok], W1[e], W3[e], W2[e], bf16_h)
+    # step 6: gate-weighted sum through the inverse permutation
+    Y = np.zeros((T, d))
+    for j in range(k):
+        r = disp["slot_row"].reshape(T, k)[:, j]
+        ok = r >= 0
+        Y[ok] += g[ok, j][:, None] * rows[r[ok]]
+    sh = None
+    if shared is not None:
+        sh = expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
+        Y = Y + sh
+    return {"logits": own, "route_logits": lg, "ids": ids, "gates": g,
+            "probs": p, "dispatch": disp, "rows": rows, "shared": sh, "Y": Y}
+
+
+def forward_token_loop(X, Wg, W1, W3, W2, *, k, score_func="softmax",
+                       renorm=True, bias=None, offset=None, cap=None,
+                       shared=None, bf16_h=False):
+    """Tier 0: a literal per-token loop in plain Python arithmetic.
+
+    Follows [Study case 1] (score -> keep top-k -> weights -> accumulate
+    w * expert(token)) with the renormalisation of [KMap router] step 4, the
+    sigmoid + bias rule of eq. 16, and capacity handled first-come per expert
+    as the tokens arrive (R6).  Only for tiny shapes.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Wg = np.asarray(Wg, dtype=np.float64)
+    T, d = X.shape
+    E = Wg.shape[1]
+    F = np.asarray(W1).shape[2]
+    C = None if cap is None or cap <= 0 else int(cap)
+    load = [0] * E
+
+    def run_expert(x, w1, w3, w2):
+        h = []
+        for f in range(F):
+            a = sum(x[i] * w1[i][f] for i in range(d))
+            u = sum(x[i] * w3[i][f] for i in range(d))
+            hv = a / (1.0 + math.exp(-a)) * u
+            if bf16_h:
+                hv = float(round_bf16(hv))
+            h.append(hv)
+        return [sum(h[f] * w2[f][j] for f in range(F)) for j in range(d)]
+
+    w1l, w3l, w2l = (np.asarray(W, np.float64).tolist() for W in (W1, W3, W2))
+    Y = []
+    for t in range(T):
+        x = X[t].tolist()
+        sc = [sum(x[i] * Wg[i][e] for i in range(d)) for e in range(E)]
+        if offset is not None:
+            sc = [sc[e] + float(offset[e]) for e in range(E)]
+        if score_func == "softmax":
+            mx = max(sc)
+            ex = [math.exp(v - mx) for v in sc]
+            z = sum(ex)
+            prob = [v / z for v in ex]
+            key = sc
+        else:
+            prob = [1.0 / (1.0 + math.exp(-v)) for v in sc]
+            key = [prob[e] + (0.0 if bias is None else float(bias[e]))
+                   for e in range(E)]
+        chosen = sorted(range(E), key=lambda e: (-key[e], e))[:k]
+        w = [prob[e] for e in chosen]
+        if renorm:
+            tot = sum(w)
+            w = [v / tot for v in w]
+        out = [0.0] * d
+        for wi, e in zip(w, chosen):
+            if C is not None and load[e] >= C:
+                load[e] += 1
+                continue                       # overflow: this path is dropped
+            load[e] += 1
+            y = run_expert(x, w1l[e], w3l[e], w2l[e])
+            out = [o + wi * v for o, v in zip(out, y)]
+        if shared is not None:
+            s1, s3, s2 = (np.asarray(W, np.float64).tolist() for W in shared)
+            y = run_expert(x, s1, s3, s2)
+            out = [o + v for o, v in zip(out, y)]
+        Y.append(out)
+    return np.array(Y, dtype=np.float64)
+
+
+def forward_dense_masked(X, Wg, W1, W3, W2, *, k, score_func="softmax",
+                         renorm=True, bias=None, offset=None, cap=None,
+                         shared=None, bf16_h=False):
+    """Tier B: run every expert on every token, then keep only the top-k (and
+    capacity-kept) contributions: y = sum_{i in TopK} g_i Expert_i(x)
+    ([Book 14.2.1] opening formula) evaluated densely."""
+    X = np.asarray(X, dtype=np.float64)
+    T, d = X.shape
+    E = np.asarray(Wg).shape[1]
+    lg = router_logits(X, Wg, offset)
+    ids, g, _ = route(lg, k, score_func, renorm, bias)
+    allout = np.stack([expert_ffn(X, W1[e], W3[e], W2[e], bf16_h)
+                       for e in range(E)])                 # [E, T, d]
+    keep = np.ones((T, k), dtype=bool)
+    if cap is not None and cap > 0:
+        seen = np.zeros(E, dtype=np.int64)
+        for t in range(T):
+            for j in range(k):
+                e = ids[t, j]
+                keep[t, j] = seen[e] < cap
+                seen[e] += 1
+    mask = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                mask[t, ids[t, j]] = g[t, j]
+    Y = np.einsum("te,etd->td", mask, allout)
+    if shared is not None:
+        Y = Y + expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
+    return Y
+
+
+# ----------------------------------------------------------------- balance --
+def balance_value(f, p):
+    """N * sum_i f_i p_i, the balance loss of [Book 14.2.3] without alpha."""
+    f = np.asarray(f, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    return float(f.size * np.sum(f * p))
+
+
+def balance_stat(counts, prob_sum, n_tokens: int, k: int):
+    """f_e = counts_e / (T*k) (pre-drop top-k counts), P_e = prob_sum_e / T
+    (R8); returns E * sum f_e P_e  [Book 14.2.3]."""
+    counts = np.asarray(counts, dtype=np.float64)
+    f = counts / float(n_tokens * k)
+    P = np.asarray(prob_sum, dtype=np.float64) / float(n_tokens)
+    return balance_value(f, P)

@@ -1,0 +1,361 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names its source: a worked example printed on a page (fixtures in
+tests/golden/), a closed form, an invariant, a library routine, or brute force.
+"""
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import moe_oracle as O
+
+GOLD = Path(__file__).parent / "golden"
+
+
+def _gold(name):
+    return json.loads((GOLD / name).read_text())
+
+
+# ------------------------------------------------------------- capacity ----
+def test_capacity_page_examples():
+    for c in _gold("capacity_examples.json")["cases"]:
+        assert O.capacity(c["cf"], c["N"], c["k"], c["E"]) == c["C"], c["where"]
+
+
+def test_capacity_switch_workload_values():
+    # top-1, 8192 tokens, 64 experts: 128 per expert at CF 1.0, 160 at 1.25
+    assert O.capacity(1.0, 8192, 1, 64) == 128
+    assert O.capacity(1.25, 8192, 1, 64) == 160
+
+
+def test_capacity_is_exact_rational():
+    # binary floating point gives 1.1*100 = 110.00000000000001 -> 111
+    assert 1.1 * 100 > 110 and math.ceil(1.1 * 100) == 111
+    assert O.capacity(1.1, 100, 1, 1) == 110
+    assert O.capacity(1.1, 50, 2, 1) == 110
+    assert O.capacity(1.0, 7, 2, 4) == 4           # ceil(3.5)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 64).map(lambda x: x / 16), st.integers(0, 5000),
+       st.integers(1, 8), st.integers(1, 300))
+def test_capacity_never_below_mean(cf16, N, k, E):
+    # ceil keeps C at or above the (scaled) mean load and less than one above
+    C = O.capacity(cf16, N, k, E)
+    exact = cf16 * N * k / E                      # cf16 is a dyadic rational
+    assert C >= exact - 1e-9 and C < exact + 1
+
+
+# ------------------------------------------------------------- dispatch ----
+def test_drop_six_token_example():
+    g = _gold("capacity_examples.json")["overflow"]["kmap_6_tokens"]
+    # The page's figure (which token chose which expert) is not in the text;
+    # this assignment has E1 (id 0) receiving 5 of the 12 requests.
+    ids = np.array([[0, 1], [0, 2], [0, 3], [1, 0], [0, 2], [1, 3]])
+    C = O.capacity(1.0, 6, 2, 4)
+    assert C == g["C"]
+    d = O.dispatch(ids, 4, C)
+    assert d["counts"].tolist() == [5, 3, 2, 2]
+    assert d["counts"][0] - d["kept"][0] == g["overflow"]
+    dropped = np.flatnonzero(d["slot_row"] < 0).tolist()
+    assert dropped == [7, 8]      # E1's 4th and 5th arrivals: (t3,j1), (t4,j0)
+    C2 = O.capacity(2.0, 6, 2, 4)
+    assert C2 == g["C_cf2"]
+    d2 = O.dispatch(ids, 4, C2)
+    assert (d2["slot_row"] >= 0).sum() == 12 and g["overflow_cf2"] == 0
+
+
+def test_drop_500_arrivals():
+    g = _gold("capacity_examples.json")["overflow"]["book_500_arrivals"]
+    T, k, E = 8192, 2, 64
+    t = np.arange(T)
+    first = np.where(t < 500, 0, 1 + t % 63)
+    second = np.where(t < 500, 1 + t % 63, 1 + (t + 1) % 63)
+    ids = np.stack([first, second], axis=1)
+    assert (ids == 0).sum() == g["arrivals"]
+    C = O.capacity(1.25, T, k, E)
+    assert C == g["C"]
+    d = O.dispatch(ids, E, C)
+    assert d["counts"][0] - d["kept"][0] == g["dropped"]
+    assert (d["counts"][1:] <= C).all()
+    assert (d["slot_row"] < 0).sum() == g["dropped"]
+
+
+def test_uniform_idle_slots():
+    g = _gold("capacity_examples.json")["overflow"]["book_uniform"]
+    T, k, E = 8192, 2, 64
+    slots = np.arange(T * k)
+    ids = (slots % E).reshape(T, k)
+    C = O.capacity(1.25, T, k, E)
+    d = O.dispatch(ids, E, C)
+    assert E * C == g["slots"]
+    assert E * C - d["n_kept"] == g["idle"]
+    assert (E * C - d["n_kept"]) / (E * C) == pytest.approx(g["idle_fraction"])
+
+
+def _dispatch_by_sort(ids, E, C):
+    """Brute force with a library stable sort: order slots by expert id."""
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    sorted_ids = flat[order]
+    keep = np.zeros(flat.size, bool)
+    rank_in = np.zeros(flat.size, np.int64)
+    for e in range(E):
+        sl = order[sorted_ids == e]
+        rank_in[sl] = np.arange(sl.size)
+    keep = rank_in < (C if C else flat.size + 1)
+    kept_sorted = order[keep[order]]
+    return kept_sorted, keep
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 12), st.data())
+def test_dispatch_structure_and_brute_force(T, E, data):
+    k = data.draw(st.integers(1, E))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    C = data.draw(st.sampled_from([None, 1, 2, 3, T * k]))
+    d = O.dispatch(ids, E, C)
+    flat = ids.reshape(-1)
+    assert d["counts"].sum() == T * k
+    assert d["counts"].tolist() == np.bincount(flat, minlength=E).tolist()
+    cap = C if C else T * k
+    assert d["kept"].tolist() == np.minimum(d["counts"], cap).tolist()
+    assert d["offsets"].tolist() == [0] + np.cumsum(d["kept"]).tolist()
+    ss, sr = d["sorted_slot"], d["slot_row"]
+    assert sorted(ss.tolist()) == sorted(np.flatnonzero(sr >= 0).tolist())
+    assert (sr[ss] == np.arange(d["n_kept"])).all()            # inverse maps
+    for e in range(E):
+        seg = ss[d["offsets"][e]:d["offsets"][e + 1]]
+        assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+    bf_sorted, bf_keep = _dispatch_by_sort(ids, E, C)
+    assert ss.tolist() == bf_sorted.tolist()
+    assert (sr >= 0).tolist() == bf_keep.tolist()
+
+
+# -------------------------------------------------------------- balance ----
+def test_balance_page_example():
+    g = _gold("balance_example.json")
+    ex = g["example"]
+    assert O.balance_value(ex["f"], ex["p"]) == pytest.approx(ex["N_sum_fp"], abs=1e-12)
+    assert O.balance_value(ex["f"], ex["p"]) / ex["N"] == pytest.approx(ex["sum_fp"], abs=1e-12)
+    assert O.balance_value(g["uniform"]["f"], g["uniform"]["p"]) == pytest.approx(1.0, abs=1e-12)
+    assert O.balance_value(g["collapsed"]["f"], g["collapsed"]["p"]) == pytest.approx(4.0, abs=1e-12)
+
+
+def test_balance_stat_from_counts():
+    # T=10 tokens, top-1: counts [7,1,1,1] give f = [.7,.1,.1,.1];
+    # per-expert probability sums [4,2,2,2] give P = [.4,.2,.2,.2] -> 1.36
+    assert O.balance_stat([7, 1, 1, 1], [4.0, 2.0, 2.0, 2.0], 10, 1) == pytest.approx(1.36, abs=1e-12)
+    # top-2: f counts both choices of every token, so f sums to 1 again
+    assert O.balance_stat([10, 5, 5, 0], [2.5] * 4, 10, 2) == pytest.approx(1.0, abs=1e-12)
+
+
+# ------------------------------------------------------ parameter count ----
+def test_expert_parameter_count():
+    g = _gold("param_count.json")
+    shapes = O.expert_weight_shapes(g["d"], g["F"])
+    per = sum(int(np.prod(s)) for s in shapes.values())
+    assert per == g["per_expert"]
+    assert per * g["per_layer_experts"] == g["per_layer"]
+    assert per * g["active_experts"] == g["active"]
+    assert round(g["per_layer"] / 1e9, 2) == 11.32
+    assert round(g["active"] / 1e6, 1) == 396.4
+
+
+# ----------------------------------------------------- scores and gates ----
+def test_softmax_and_sigmoid_closed_forms():
+    p = O.scores(np.zeros((1, 5)), "softmax")
+    assert np.allclose(p, 0.2, atol=0, rtol=1e-15)
+    lg = np.array([[0.0, math.log(3.0)]])
+    assert np.allclose(O.scores(lg, "softmax"), [[0.25, 0.75]], rtol=1e-15)
+    assert O.scores(np.zeros((1, 1)), "sigmoid")[0, 0] == 0.5
+    assert O.scores(np.array([[math.log(3.0)]]), "sigmoid")[0, 0] == pytest.approx(0.75, rel=1e-15)
+    big = O.scores(np.array([[1000.0, 0.0, -1000.0]]), "softmax")
+    assert big[0, 0] == 1.0 and big[0, 2] == 0.0
+
+
+def test_topk_order_and_ties():
+    lg = np.array([[1.0, 3.0, 3.0, 2.0]])
+    assert O.select_topk(lg, 2, "softmax")[0].tolist() == [[1, 2]]
+    assert O.select_topk(lg, 3, "softmax")[0].tolist() == [[1, 2, 3]]
+    assert O.select_topk(lg, 4, "softmax")[0].tolist() == [[1, 2, 3, 0]]
+    # sigmoid with a bias: key = s + b; the bias can promote an expert
+    lg2 = np.array([[2.0, 0.0, 1.0]])
+    assert O.select_topk(lg2, 1, "sigmoid")[0].tolist() == [[0]]
+    assert O.select_topk(lg2, 1, "sigmoid", bias=[0.0, 0.9, 0.0])[0].tolist() == [[1]]
+
+
+def test_gates_renorm_sum_to_one_and_topk_softmax_identity():
+    rng = np.random.default_rng(7)
+    lg = rng.normal(size=(50, 16)) * 2
+    for k in (1, 2, 5, 16):
+        ids, g, _ = O.route(lg, k, "softmax", True)
+        assert np.allclose(g.sum(axis=1), 1.0, atol=1e-12, rtol=0)
+        # the study note's form: softmax over only the k kept logits
+        kept = np.take_along_axis(lg, ids, axis=1)
+        ek = np.exp(kept - kept.max(axis=1, keepdims=True))
+        assert np.allclose(g, ek / ek.sum(axis=1, keepdims=True), atol=1e-14, rtol=0)
+    ids, g, _ = O.route(lg, 1, "softmax", True)
+    assert (g == 1.0).all()                                   # top-1 renorm
+    ids, g, p = O.route(lg, 2, "softmax", False)
+    assert np.array_equal(g, np.take_along_axis(p, ids, axis=1))
+
+
+def test_sigmoid_gate_uses_raw_affinity():
+    rng = np.random.default_rng(3)
+    lg = rng.normal(size=(40, 12))
+    ids0, g0, _ = O.route(lg, 4, "sigmoid", True)
+    tiny = rng.normal(size=12) * 1e-9          # too small to change any set
+    ids1, g1, _ = O.route(lg, 4, "sigmoid", True, bias=tiny)
+    assert np.array_equal(ids0, ids1) and np.array_equal(g0, g1)
+    # a bias that changes the set: the promoted expert's gate is its raw s
+    b = np.zeros(12); b[5] = 10.0
+    ids2, g2, p2 = O.route(lg, 4, "sigmoid", True, bias=b)
+    assert (ids2[:, 0] == 5).all()
+    s = p2[np.arange(40)[:, None], ids2]
+    assert np.allclose(g2, s / s.sum(axis=1, keepdims=True), rtol=1e-15)
+    assert np.allclose(g2.sum(axis=1), 1.0, atol=1e-12)
+
+
+# --------------------------------------------------------------- expert ----
+def test_swiglu_hand_example():
+    # x = [1, 0]: gate pre-activation 2, up pre-activation 3, so
+    # h = silu(2) * 3 = 6 / (1 + e^-2) = 5.284782467867294; W2 = [[1, -1]]
+    x = np.array([[1.0, 0.0]])
+    W1 = np.array([[2.0], [0.0]])
+    W3 = np.array([[3.0], [0.0]])
+    W2 = np.array([[1.0, -1.0]])
+    y = O.expert_ffn(x, W1, W3, W2)
+    assert y[0, 0] == pytest.approx(5.284782467867294, rel=1e-15)
+    assert y[0, 1] == pytest.approx(-5.284782467867294, rel=1e-15)
+    # swapping gate and up changes the value (silu(3) * 2 = 5.715...)
+    assert O.expert_ffn(x, W3, W1, W2)[0, 0] == pytest.approx(5.7154447609345995, rel=1e-15)
+
+
+def test_silu_values():
+    assert O.silu(0.0) == 0.0
+    assert O.silu(50.0) == pytest.approx(50.0, rel=1e-15)
+    assert abs(O.silu(-50.0)) < 1e-19
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+def test_round_bf16_against_format_and_torch():
+    torch = pytest.importorskip("torch")
+    assert O.round_bf16(1.0) == 1.0
+    assert O.round_bf16(1.0 + 2.0**-8) == 1.0                    # tie -> even
+    assert O.round_bf16(1.0 + 3 * 2.0**-8) == 1.0 + 2.0**-6      # tie -> even
+    assert O.round_bf16(1.0 + 2.0**-8 + 2.0**-20) == 1.0 + 2.0**-7
+    assert O.round_bf16(-3.0) == -3.0 and O.round_bf16(0.0) == 0.0
+    rng = np.random.default_rng(11)
+    x = (rng.normal(size=20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+# ------------------------------------------------------ tiers agree -------
+def _rand_layer(rng, T, d, E, F, shared):
+    X = rng.normal(size=(T, d))
+    Wg = rng.normal(size=(d, E)) / math.sqrt(d)
+    W1 = rng.normal(size=(E, d, F)) / math.sqrt(d)
+    W3 = rng.normal(size=(E, d, F)) / math.sqrt(d)
+    W2 = rng.normal(size=(E, F, d)) / math.sqrt(F)
+    sh = None
+    if shared:
+        sh = (rng.normal(size=(d, F)) / math.sqrt(d),
+              rng.normal(size=(d, F)) / math.sqrt(d),
+              rng.normal(size=(F, d)) / math.sqrt(F))
+    return X, Wg, W1, W3, W2, sh
+
+
+@settings(max_examples=25, deadline=None)
+@given(st.data())
+def test_three_tiers_agree(data):
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    T = data.draw(st.integers(1, 12))
+    d = data.draw(st.integers(1, 6))
+    E = data.draw(st.integers(1, 6))
+    F = data.draw(st.integers(1, 5))
+    k = data.draw(st.integers(1, E))
+    score = data.draw(st.sampled_from(["softmax", "sigmoid"]))
+    renorm = data.draw(st.booleans())
+    shared = data.draw(st.booleans())
+    bf16_h = data.draw(st.booleans())
+    C = data.draw(st.sampled_from([None, 1, 2, T * k]))
+    X, Wg, W1, W3, W2, sh = _rand_layer(rng, T, d, E, F, shared)
+    bias = rng.normal(size=E) * 0.1 if score == "sigmoid" else None
+    offset = rng.normal(size=E) if data.draw(st.booleans()) else None
+    kw = dict(k=k, score_func=score, renorm=renorm, bias=bias, offset=offset,
+              cap=C, shared=sh, bf16_h=bf16_h)
+    y1 = O.forward(X, Wg, W1, W3, W2, **kw)["Y"]
+    y0 = O.forward_token_loop(X, Wg, W1, W3, W2, **kw)
+    yb = O.forward_dense_masked(X, Wg, W1, W3, W2, **kw)
+    scale = max(1.0, np.abs(yb).max())
+    assert np.abs(y1 - yb).max() <= 1e-12 * scale
+    if bf16_h:
+        # the token loop rounds h computed in a different summation order; a
+        # value sitting on a bf16 rounding boundary may round differently
+        assert np.abs(y0 - yb).max() <= 1e-2 * scale
+    else:
+        assert np.abs(y0 - yb).max() <= 1e-12 * scale
+
+
+def test_single_expert_is_dense_swiglu():
+    rng = np.random.default_rng(5)
+    X, Wg, W1, W3, W2, _ = _rand_layer(rng, 9, 6, 1, 4, False)
+    Y = O.forward(X, Wg, W1, W3, W2, k=1)["Y"]
+    dense = (O.silu(X @ W1[0]) * (X @ W3[0])) @ W2[0]
+    assert np.allclose(Y, dense, atol=1e-13, rtol=0)
+
+
+def test_large_capacity_equals_no_capacity():
+    rng = np.random.default_rng(6)
+    X, Wg, W1, W3, W2, sh = _rand_layer(rng, 20, 8, 5, 6, True)
+    a = O.forward(X, Wg, W1, W3, W2, k=2, cap=None, shared=sh)
+    b = O.forward(X, Wg, W1, W3, W2, k=2, cap=40, shared=sh)
+    assert np.array_equal(a["Y"], b["Y"])
+    c = O.forward(X, Wg, W1, W3, W2, k=2, cap=1, shared=sh)
+    assert (c["dispatch"]["kept"] <= 1).all()
+
+
+def test_dropped_slot_contributes_zero():
+    # token 0 picks experts {0, 1}, token 1 picks {0, 2}; capacity 1 drops
+    # token 1's path to expert 0 (second arrival) and keeps its expert-2 path
+    X = np.array([[1.0, 0.0], [0.0, 1.0]])
+    Wg = np.array([[5.0, 1.0, 0.0], [5.0, 0.0, 1.0]])
+    rng = np.random.default_rng(2)
+    W1, W3, W2 = rng.normal(size=(3, 2, 3)), rng.normal(size=(3, 2, 3)), rng.normal(size=(3, 3, 2))
+    full = O.forward(X, Wg, W1, W3, W2, k=2)
+    cut = O.forward(X, Wg, W1, W3, W2, k=2, cap=1)
+    assert full["ids"].tolist() == [[0, 1], [0, 2]]
+    g = full["gates"]
+    e2 = O.expert_ffn(X[1:2], W1[2], W3[2], W2[2])[0]
+    assert cut["dispatch"]["slot_row"].tolist() == [0, 1, -1, 2]
+    # the kept path keeps its gate from before the drop (no second renorm)
+    assert np.allclose(cut["Y"][1], g[1, 1] * e2, atol=1e-14)
+    assert np.allclose(cut["Y"][0], full["Y"][0], atol=1e-14)
+
+
+# ----------------------------------------------- planted-mistake checks ----
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """A wrong oracle must fail the pins: plant mistakes and re-run them."""
+    # 1. gate and up swapped inside the expert
+    good = O.expert_ffn
+    monkeypatch.setattr(O, "expert_ffn", lambda x, a, b, c, bf16_h=False: good(x, b, a, c, bf16_h))
+    with pytest.raises(AssertionError):
+        test_swiglu_hand_example()
+    monkeypatch.setattr(O, "expert_ffn", good)
+    # 2. no renormalisation
+    good_gates = O.gates
+    monkeypatch.setattr(O, "gates", lambda lg, ids, sf, rn: good_gates(lg, ids, sf, False))
+    with pytest.raises(AssertionError):
+        test_gates_renorm_sum_to_one_and_topk_softmax_identity()
+    monkeypatch.setattr(O, "gates", good_gates)
+    # 3. floating-point capacity instead of the exact rational
+    monkeypatch.setattr(O, "capacity", lambda cf, N, k, E: math.ceil(cf * N * k / E))
+    with pytest.raises(AssertionError):
+        test_capacity_is_exact_rational()
