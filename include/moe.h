@@ -1,0 +1,197 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Mixture-of-Experts layer forward pass.
+ *
+ * The layer follows the six steps of LLM Internals section 14.2.1 ("one MoE
+ * forward pass: six steps and shapes") and the four router steps of the AI
+ * Knowledge Map page "Mixture of Experts (MoE)":
+ *   score     l = X W_g (+ optional per-expert offset)          -> moe_route
+ *   select    top-k, gates renormalised inside the chosen set   -> moe_route
+ *   dispatch  stable sort of token slots by expert, capacity    -> moe_dispatch
+ *   experts   grouped SwiGLU GEMM, m_i rows per expert          -> moe_grouped_ffn
+ *   combine   gate-weighted sum through the inverse permutation -> moe_combine
+ *   all       one fused call                                    -> moe_forward
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major.
+ *     The library never allocates, frees or synchronises; scratch memory is a
+ *     caller-provided workspace of at least the size the matching
+ *     *_workspace_size function returns (256-byte aligned).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call is asynchronous on that stream; data-dependent sizes (rows
+ *     per expert, kept rows) stay on the device.
+ *   - Weight storage: every matrix is stored with its reduction dimension
+ *     contiguous.  Router Wg[E][d] (logical W_g[d,E] transposed); gate/up
+ *     W1,W3[G][F][d] (logical [G,d,F] transposed); down W2[G][d][F] (logical
+ *     [G,F,d] transposed).  Activations X[T][d], H[rows][F], Y[T][d].
+ *   - dtype: MOE_BF16 (bf16 storage, fp32 accumulation, fp32 router scores)
+ *     or MOE_F32.  Integers are int32.
+ *   - Supported shapes: d and F multiples of 128, 1 <= E <= 256, 1 <= k <= E,
+ *     k <= 16, T >= 0.  Otherwise MOE_EUNSUPPORTED.
+ *   - Errors: arguments are validated on the host before anything is
+ *     launched; a negative return means nothing was enqueued (except
+ *     MOE_EHIP, which reports a failed launch).  moe_last_error() returns a
+ *     thread-local message describing the last failure.
+ *   - Results are bitwise reproducible run to run: no floating-point atomics.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* invalid argument (null pointer, k > E, ...)     */
+  MOE_EUNSUPPORTED = -2,  /* valid but unsupported shape or dtype            */
+  MOE_EWORKSPACE = -3,    /* workspace smaller than *_workspace_size()       */
+  MOE_EHIP = -4           /* HIP runtime error while launching               */
+};
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Capacity C = ceil(cf * N * k / E) (AI Knowledge Map "MoE", capacity
+ * formula; GShard form in LLM Internals 14.2.3).  cf is taken as the exact
+ * decimal its shortest round-trip representation spells, so the result is
+ * exact (1.25 * 8192 * 2 / 64 = 320).  Returns C >= 0, or a negative
+ * moe_status for cf <= 0, non-finite cf, N < 0, k < 1 or E < 1. */
+int64_t moe_capacity(double cf, int64_t N, int k, int E);
+
+/* ---------------------------------------------------------------- route --
+ * Router scoring and top-k (LLM Internals 14.2.1 steps 2-3; AI Knowledge Map
+ * "MoE" router steps 1-4; eq. 16 of the DeepSeek-V3 report as restated in
+ * LLM Internals 14.2.3 for the selection-only bias).
+ *   X[T][d] (dtype), Wg[E][d] (dtype)
+ *   bias[E]          fp32 selection-only bias (sigmoid router) or NULL
+ *   logit_offset[E]  fp32 added to every token's logits, or NULL
+ *   score            MOE_SOFTMAX: p = softmax(l) in fp32 over all E; the
+ *                    top-k key is the logit itself.
+ *                    MOE_SIGMOID: s = sigmoid(l) per cell; the key is s + b,
+ *                    evaluated in fp64; the gate uses the raw s.
+ *   renorm           1: gates g_e / sum_{chosen} g; 0: the raw p or s.
+ * Outputs (device):
+ *   logits[T][E]     fp32 logits (with the offset) or NULL
+ *   topk_ids[T][k]   int32, key descending, ties to the lower expert id
+ *   topk_w[T][k]     fp32 gates in the same order
+ *   prob_sum[E]      fp32 sum over tokens of the full-row p (or s), or NULL
+ */
+size_t moe_route_workspace_size(int64_t T, int d, int E);
+int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
+              int E, const float* bias, const float* logit_offset, int score,
+              int k, int renorm, float* logits, int32_t* topk_ids,
+              float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------- dispatch --
+ * Dispatch permutation with an optional capacity drop (LLM Internals 14.2.1
+ * step 4; AI Knowledge Map "MoE" capacity and overflow-by-drop).  Slot
+ * s = t*k + j.  rank(s) = number of earlier slots with the same expert; a
+ * slot is kept iff capacity <= 0 or rank(s) < capacity.
+ *   topk_ids[T][k]     int32 expert ids (0 <= id < E)
+ * Outputs (device, int32):
+ *   counts[E]          requests per expert before the drop
+ *   offsets[E+1]       exclusive scan of min(counts, capacity)
+ *   sorted_slot[T*k]   first n_kept entries: kept slots grouped by expert,
+ *                      increasing slot order inside an expert
+ *   slot_row[T*k]      row of slot s in the sorted order, -1 if dropped
+ *   n_kept[1]          number of kept slots R
+ * Optional gather (step 4's data movement): if X and X_sorted are non-NULL,
+ *   X_sorted[r][:] = X[sorted_slot[r] / k][:] for r < n_kept (dtype, [.,d]).
+ */
+size_t moe_dispatch_workspace_size(int64_t T, int k, int E);
+int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E,
+                 int64_t capacity, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_slot, int32_t* slot_row, int32_t* n_kept,
+                 const void* X, int dtype, int d, void* X_sorted, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------- grouped FFN --
+ * Grouped SwiGLU expert FFN (LLM Internals 14.2.1 step 5; one expert is the
+ * three matrices of 14.2.2): for every group g and row r in
+ * [offsets[g], offsets[g+1]):
+ *   h = silu(a_r W1_g) * (a_r W3_g)       (rounded to bf16 for MOE_BF16)
+ *   Yrows[r][:] = h W2_g                   (fp32)
+ * where a_r = A[row_token[r]] if row_token != NULL (A is then X[T][d]) and
+ * a_r = A[r] otherwise (A is X_sorted).
+ *   offsets[G+1]   device int32, non-decreasing, offsets[G] <= max_rows
+ *   W1, W3[G][F][d], W2[G][d][F] (dtype)
+ *   max_rows       host upper bound of offsets[G] (sizes the launch)
+ *   Yrows[max_rows][d] fp32 output; rows past offsets[G] are untouched.
+ */
+size_t moe_grouped_ffn_workspace_size(int64_t max_rows, int G, int d, int F,
+                                      int dtype);
+int moe_grouped_ffn(const void* A, const int32_t* row_token,
+                    const int32_t* offsets, int G, const void* W1,
+                    const void* W3, const void* W2, int dtype, int d, int F,
+                    int64_t max_rows, float* Yrows, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* -------------------------------------------------------------- combine --
+ * Combine (LLM Internals 14.2.1 step 6; AI Knowledge Map "MoE"
+ * y = sum_{e in S} g_e E_e(x)):
+ *   Y[t][:] = sum_{j: slot_row[t*k+j] >= 0} topk_w[t][j] * Yrows[slot_row[t*k+j]][:]
+ *             + shared[t][:]          (if shared != NULL)
+ * accumulated in fp32 and rounded once to dtype.  Dropped slots add nothing.
+ *   Yrows[.][d] fp32, slot_row[T*k], topk_w[T][k] fp32, shared[T][d] fp32.
+ */
+int moe_combine(const float* Yrows, const int32_t* slot_row,
+                const float* topk_w, int64_t T, int k, int d,
+                const float* shared, void* Y, int dtype, void* stream);
+
+/* Balance statistic E * sum_e f_e P_e (LLM Internals 14.2.3 balance loss
+ * without alpha): f_e = counts[e] / (T*k), P_e = prob_sum[e] / T.
+ * Writes one fp64 value to device memory `out`. */
+int moe_balance(const int32_t* counts, const float* prob_sum, int64_t T,
+                int k, int E, double* out, void* stream);
+
+/* -------------------------------------------------------------- forward --
+ * The whole layer in one call: route -> dispatch (+capacity) -> grouped
+ * SwiGLU (routed experts and the optional shared expert of LLM Internals
+ * 14.2.4, width F, weight 1) -> combine.  Y has X's shape (no residual). */
+typedef struct moe_layer {
+  int dtype;               /* MOE_BF16 or MOE_F32                           */
+  int score;               /* MOE_SOFTMAX or MOE_SIGMOID                    */
+  int renorm;              /* renormalise gates inside the chosen set        */
+  int d, E, k, F;
+  int n_shared;            /* 0 or 1                                         */
+  double capacity_factor;  /* <= 0: no capacity limit                        */
+  const void* Wg;          /* [E][d]                                         */
+  const float* bias;       /* [E] or NULL                                    */
+  const float* logit_offset; /* [E] or NULL                                  */
+  const void* W1;          /* [E][F][d]                                      */
+  const void* W3;          /* [E][F][d]                                      */
+  const void* W2;          /* [E][d][F]                                      */
+  const void* Ws1;         /* shared expert [F][d], or NULL                  */
+  const void* Ws3;         /* [F][d]                                         */
+  const void* Ws2;         /* [d][F]                                         */
+} moe_layer;
+
+/* Optional device outputs of moe_forward; any member may be NULL. */
+typedef struct moe_aux {
+  float* logits;           /* [T][E]  */
+  int32_t* topk_ids;       /* [T][k]  */
+  float* topk_w;           /* [T][k]  */
+  float* prob_sum;         /* [E]     */
+  int32_t* counts;         /* [E]     */
+  int32_t* offsets;        /* [E+1]   */
+  int32_t* sorted_slot;    /* [T*k]   */
+  int32_t* slot_row;       /* [T*k]   */
+  int32_t* n_kept;         /* [1]     */
+  float* Yrows;            /* [T*k + n_shared*T][d] expert output rows       */
+  double* balance;         /* [1]     */
+} moe_aux;
+
+size_t moe_forward_workspace_size(const moe_layer* L, int64_t T);
+int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y,
+                const moe_aux* aux, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,10 @@
+"""MI355X (gfx950) Mixture-of-Experts layer forward pass.
+
+The compute path is the HIP library ``libmoe.so`` (C ABI: include/moe.h);
+this package is its Python binding plus the seeded synthetic workloads.
+"""
+from ._lib import (MoeError, MoeLayer, Forward, balance, capacity, combine, dispatch,  # noqa: F401
+                   forward, grouped_ffn, last_error, layer_from_inputs, lib, route)
+
+__all__ = ["MoeError", "MoeLayer", "Forward", "balance", "capacity", "combine", "dispatch",
+           "forward", "grouped_ffn", "last_error", "layer_from_inputs", "lib", "route"]

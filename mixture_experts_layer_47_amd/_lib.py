@@ -1,0 +1,287 @@
+"""ctypes binding of libmoe.so (the C ABI in include/moe.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, outputs are allocated with torch.  Every step
+of the layer runs in the HIP library; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
+          -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
+
+EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_route",
+           "moe_dispatch_workspace_size", "moe_dispatch",
+           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
+           "moe_balance", "moe_forward_workspace_size", "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class MoeLayerC(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("score", ctypes.c_int), ("renorm", ctypes.c_int),
+                ("d", ctypes.c_int), ("E", ctypes.c_int), ("k", ctypes.c_int),
+                ("F", ctypes.c_int), ("n_shared", ctypes.c_int),
+                ("capacity_factor", ctypes.c_double),
+                ("Wg", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("logit_offset", ctypes.c_void_p), ("W1", ctypes.c_void_p),
+                ("W3", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("Ws1", ctypes.c_void_p), ("Ws3", ctypes.c_void_p), ("Ws2", ctypes.c_void_p)]
+
+
+class MoeAuxC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logits", "topk_ids", "topk_w", "prob_sum", "counts", "offsets",
+                 "sorted_slot", "slot_row", "n_kept", "Yrows", "balance")]
+
+
+_LIB = None
+
+
+def _declare(L):
+    P, I, I64, SZ, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    sig = {
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_capacity": (I64, [D, I64, I, I]),
+        "moe_route_workspace_size": (SZ, [I64, I, I]),
+        "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_dispatch_workspace_size": (SZ, [I64, I, I]),
+        "moe_dispatch": (I, [P, I64, I, I, I64, P, P, P, P, P, P, I, I, P, P, SZ, P]),
+        "moe_grouped_ffn_workspace_size": (SZ, [I64, I, I, I, I]),
+        "moe_grouped_ffn": (I, [P, P, P, I, P, P, P, I, I, I, I64, P, P, SZ, P]),
+        "moe_combine": (I, [P, P, P, I64, I, I, P, P, I, P]),
+        "moe_balance": (I, [P, P, I64, I, I, P, P]),
+        "moe_forward_workspace_size": (SZ, [ctypes.POINTER(MoeLayerC), I64]),
+        "moe_forward": (I, [ctypes.POINTER(MoeLayerC), P, I64, P, ctypes.POINTER(MoeAuxC), P,
+                            SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """Load libmoe.so (after torch, so both share torch's HIP runtime)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "mixture_experts_layer_47_amd.build.build()")
+        _LIB = ctypes.CDLL(LIB_PATH)
+        _declare(_LIB)
+    return _LIB
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _score_code(score: str) -> int:
+    return {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}[score]
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns >= 256-byte aligned blocks
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def capacity(cf: float, N: int, k: int, E: int) -> int:
+    c = lib().moe_capacity(float(cf), int(N), int(k), int(E))
+    if c < 0:
+        raise MoeError(int(c), last_error())
+    return int(c)
+
+
+def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
+          want_logits=True, want_prob_sum=True):
+    T, d = X.shape
+    E = Wg.shape[0]
+    dev = X.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    ps = torch.empty((E,), dtype=torch.float32, device=dev) if want_prob_sum else None
+    L = lib()
+    ws_n = L.moe_route_workspace_size(T, d, E)
+    ws = _workspace(ws_n, dev)
+    _check(L.moe_route(_ptr(X), _dtype_code(X), T, d, _ptr(Wg), E, _ptr(bias), _ptr(offset),
+                       _score_code(score), int(k), int(bool(renorm)), _ptr(lg), _ptr(ids),
+                       _ptr(w), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)))
+    return {"ids": ids, "w": w, "logits": lg, "prob_sum": ps}
+
+
+def dispatch(ids, E, capacity=0, X=None):
+    T, k = ids.shape
+    dev = ids.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = {"counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+           "sorted_slot": torch.empty(T * k, **i32), "slot_row": torch.empty(T * k, **i32),
+           "n_kept": torch.empty(1, **i32), "X_sorted": None}
+    d, dt = 0, MOE_BF16
+    if X is not None:
+        d = X.shape[1]
+        dt = _dtype_code(X)
+        out["X_sorted"] = torch.empty((T * k, d), dtype=X.dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.moe_dispatch_workspace_size(T, k, E), dev)
+    _check(L.moe_dispatch(_ptr(ids), T, k, E, int(capacity), _ptr(out["counts"]),
+                          _ptr(out["offsets"]), _ptr(out["sorted_slot"]), _ptr(out["slot_row"]),
+                          _ptr(out["n_kept"]), _ptr(X), dt, d, _ptr(out["X_sorted"]),
+                          _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def grouped_ffn(A, offsets, W1, W3, W2, max_rows, row_token=None):
+    G, F, d = W1.shape
+    dev = A.device
+    Y = torch.empty((max(int(max_rows), 1), d), dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _workspace(L.moe_grouped_ffn_workspace_size(max_rows, G, d, F, _dtype_code(A)), dev)
+    _check(L.moe_grouped_ffn(_ptr(A), _ptr(row_token), _ptr(offsets), G, _ptr(W1), _ptr(W3),
+                             _ptr(W2), _dtype_code(A), d, F, int(max_rows), _ptr(Y), _ptr(ws),
+                             ws.numel(), _stream(dev)))
+    return Y[:max_rows]
+
+
+def combine(Yrows, slot_row, w, out_dtype, shared=None):
+    T, k = w.shape
+    d = Yrows.shape[1]
+    dev = Yrows.device
+    Y = torch.empty((T, d), dtype=out_dtype, device=dev)
+    code = MOE_BF16 if out_dtype == torch.bfloat16 else MOE_F32
+    _check(lib().moe_combine(_ptr(Yrows), _ptr(slot_row), _ptr(w), T, k, d, _ptr(shared),
+                             _ptr(Y), code, _stream(dev)))
+    return Y
+
+
+def balance(counts, prob_sum, T, k):
+    out = torch.empty(1, dtype=torch.float64, device=counts.device)
+    _check(lib().moe_balance(_ptr(counts), _ptr(prob_sum), int(T), int(k), counts.numel(),
+                             _ptr(out), _stream(counts.device)))
+    return out
+
+
+@dataclass
+class MoeLayer:
+    """Weights and routing rule of one MoE layer (storage layout of moe.h)."""
+    Wg: torch.Tensor
+    W1: torch.Tensor
+    W3: torch.Tensor
+    W2: torch.Tensor
+    k: int
+    score: str = "softmax"
+    renorm: bool = True
+    bias: Optional[torch.Tensor] = None
+    offset: Optional[torch.Tensor] = None
+    shared: Optional[tuple] = None
+    capacity_factor: float = 0.0
+
+    def cstruct(self) -> MoeLayerC:
+        E, F, d = self.W1.shape
+        s = self.shared or (None, None, None)
+        self._keep = MoeLayerC(
+            _dtype_code(self.W1), _score_code(self.score), int(bool(self.renorm)), d, E,
+            int(self.k), F, 1 if self.shared else 0, float(self.capacity_factor or 0.0),
+            self.Wg.data_ptr(), _addr(self.bias), _addr(self.offset), self.W1.data_ptr(),
+            self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]))
+        return self._keep
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def layer_from_inputs(inp: dict) -> MoeLayer:
+    """Build a MoeLayer from a workload's drawn inputs."""
+    w = inp["workload"]
+    return MoeLayer(Wg=inp["Wg"], W1=inp["W1"], W3=inp["W3"], W2=inp["W2"], k=w.k,
+                    score=w.score, renorm=w.renorm, bias=inp["bias"], offset=inp["offset"],
+                    shared=inp["shared"], capacity_factor=w.cf or 0.0)
+
+
+class Forward:
+    """A prepared moe_forward call: struct, workspace and outputs allocated
+    once, so repeated calls launch kernels only."""
+
+    def __init__(self, layer: MoeLayer, X: torch.Tensor, aux: bool = False):
+        self.layer, self.X = layer, X
+        T, d = X.shape
+        E, F, _ = layer.W1.shape
+        k = layer.k
+        dev = X.device
+        self.cl = layer.cstruct()
+        L = lib()
+        self.ws = _workspace(L.moe_forward_workspace_size(ctypes.byref(self.cl), T), dev)
+        self.Y = torch.empty((T, d), dtype=X.dtype, device=dev)
+        self.aux = {}
+        self.caux = MoeAuxC()
+        if aux:
+            i32 = dict(dtype=torch.int32, device=dev)
+            rows = T * k + (T if layer.shared else 0)
+            self.aux = {
+                "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+                "topk_ids": torch.empty((T, k), **i32),
+                "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+                "prob_sum": torch.empty(E, dtype=torch.float32, device=dev),
+                "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+                "sorted_slot": torch.empty(T * k, **i32), "slot_row": torch.empty(T * k, **i32),
+                "n_kept": torch.empty(1, **i32),
+                "Yrows": torch.empty((max(rows, 1), d), dtype=torch.float32, device=dev),
+                "balance": torch.empty(1, dtype=torch.float64, device=dev),
+            }
+            for n, t in self.aux.items():
+                setattr(self.caux, n, t.data_ptr())
+        self.T = T
+
+    def __call__(self):
+        _check(lib().moe_forward(ctypes.byref(self.cl), _ptr(self.X), self.T, _ptr(self.Y),
+                                 ctypes.byref(self.caux), _ptr(self.ws), self.ws.numel(),
+                                 _stream(self.X.device)))
+        return self.Y
+
+
+def forward(layer: MoeLayer, X: torch.Tensor, aux: bool = False):
+    f = Forward(layer, X, aux)
+    Y = f()
+    return (Y, f.aux) if aux else Y

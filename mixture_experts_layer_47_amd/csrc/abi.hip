@@ -1,0 +1,324 @@
+// C-ABI entry points: host-side validation, workspace carving, launches.
+// Nothing here allocates, frees or synchronises device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+  return ok();
+}
+
+#define MOE_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_dtype(int dtype) {
+  MOE_REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", dtype);
+  return MOE_OK;
+}
+
+int check_router_dims(int64_t T, int d, int E, int k) {
+  MOE_REQUIRE(T >= 0, MOE_EINVAL, "T = %lld < 0", (long long)T);
+  MOE_REQUIRE(d > 0, MOE_EINVAL, "d = %d must be positive", d);
+  MOE_REQUIRE(E >= 1, MOE_EINVAL, "E = %d must be >= 1", E);
+  MOE_REQUIRE(k >= 1 && k <= E, MOE_EINVAL, "k = %d must satisfy 1 <= k <= E = %d", k, E);
+  MOE_REQUIRE(E <= 256, MOE_EUNSUPPORTED, "E = %d > 256 is not supported", E);
+  MOE_REQUIRE(k <= 16, MOE_EUNSUPPORTED, "k = %d > 16 is not supported", k);
+  MOE_REQUIRE(d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a multiple of 128", d);
+  MOE_REQUIRE(T * (int64_t)k + T <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large for int32 indices");
+  return MOE_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  MOE_REQUIRE(have >= need, MOE_EWORKSPACE, "workspace of %zu bytes < required %zu", have, need);
+  MOE_REQUIRE(need == 0 || ws != nullptr, MOE_EINVAL, "workspace pointer is NULL");
+  MOE_REQUIRE(((uintptr_t)ws & 255) == 0, MOE_EINVAL, "workspace is not 256-byte aligned");
+  return MOE_OK;
+}
+
+// Exact ceil(cf * N * k / E): cf is read as the shortest decimal that
+// round-trips to the same double, i.e. M * 10^e with integer M.
+int64_t exact_capacity(double cf, int64_t N, int k, int E) {
+  char buf[64];
+  int prec = 1;
+  for (; prec <= 17; ++prec) {
+    snprintf(buf, sizeof(buf), "%.*e", prec - 1, cf);
+    if (strtod(buf, nullptr) == cf) break;
+  }
+  // buf = "D.DDDDe[+-]XX"
+  unsigned long long M = 0;
+  int ndig = 0;
+  const char* p = buf;
+  for (; *p && *p != 'e'; ++p)
+    if (*p >= '0' && *p <= '9') { M = M * 10 + (unsigned)(*p - '0'); ++ndig; }
+  const int e10 = atoi(p + 1) - (ndig - 1);
+  typedef unsigned __int128 u128;
+  u128 num = (u128)M * (u128)N * (u128)k;
+  u128 den = (u128)E;
+  if (e10 >= 0) {
+    for (int i = 0; i < e10; ++i) num *= 10;
+  } else {
+    for (int i = 0; i < -e10; ++i) den *= 10;
+  }
+  const u128 c = (num + den - 1) / den;
+  return (int64_t)c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_capacity(double cf, int64_t N, int k, int E) {
+  if (!(cf > 0.0) || !isfinite(cf)) return fail(MOE_EINVAL, "capacity factor must be finite and > 0");
+  if (N < 0 || k < 1 || E < 1) return fail(MOE_EINVAL, "capacity needs N >= 0, k >= 1, E >= 1");
+  const long double est = (long double)cf * (long double)N * (long double)k / (long double)E;
+  if (est > 4.0e18L || cf > 1e15 || cf < 1e-15)
+    return fail(MOE_EINVAL, "capacity factor %g out of range", cf);
+  ok();
+  return exact_capacity(cf, N, k, E);
+}
+
+// ------------------------------------------------------------------- route
+size_t moe_route_workspace_size(int64_t T, int d, int E) {
+  if (T < 0 || d <= 0 || E <= 0) return 0;
+  return route_ws_bytes(T, d, E);
+}
+
+int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
+              const float* bias, const float* logit_offset, int score, int k, int renorm,
+              float* logits, int32_t* topk_ids, float* topk_w, float* prob_sum, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_router_dims(T, d, E, k))) return rc;
+  MOE_REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_EINVAL, "score %d unknown", score);
+  MOE_REQUIRE(T == 0 || (X && Wg && topk_ids && topk_w), MOE_EINVAL, "NULL X, Wg, topk_ids or topk_w");
+  MOE_REQUIRE(score == MOE_SIGMOID || bias == nullptr, MOE_EINVAL,
+              "a selection bias is only defined for the sigmoid router");
+  if ((rc = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E)))) return rc;
+  return hip_status(launch_route(X, dtype, T, d, Wg, E, bias, logit_offset, score, k, renorm,
+                                 logits, topk_ids, topk_w, prob_sum, ws, (hipStream_t)stream),
+                    "moe_route");
+}
+
+// ---------------------------------------------------------------- dispatch
+size_t moe_dispatch_workspace_size(int64_t T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return dispatch_ws_bytes(T, k, E);
+}
+
+int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E, int64_t capacity,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                 int32_t* n_kept, const void* X, int dtype, int d, void* X_sorted, void* ws,
+                 size_t ws_bytes, void* stream) {
+  MOE_REQUIRE(T >= 0, MOE_EINVAL, "T < 0");
+  MOE_REQUIRE(E >= 1 && k >= 1 && k <= E, MOE_EINVAL, "need 1 <= k <= E");
+  MOE_REQUIRE(E <= 256, MOE_EUNSUPPORTED, "E = %d > 256 is not supported", E);
+  MOE_REQUIRE(T * (int64_t)k <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large");
+  MOE_REQUIRE(counts && offsets && n_kept, MOE_EINVAL, "NULL counts, offsets or n_kept");
+  MOE_REQUIRE(T == 0 || (topk_ids && sorted_slot && slot_row), MOE_EINVAL,
+              "NULL topk_ids, sorted_slot or slot_row");
+  const bool gather = X_sorted != nullptr;
+  if (gather) {
+    int rc;
+    if ((rc = check_dtype(dtype))) return rc;
+    MOE_REQUIRE(X != nullptr, MOE_EINVAL, "X_sorted given without X");
+    MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a positive multiple of 128", d);
+  }
+  int rc;
+  if ((rc = check_ws(ws, ws_bytes, dispatch_ws_bytes(T, k, E)))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_dispatch(topk_ids, T, k, E, capacity, 0, counts, offsets, sorted_slot,
+                                 slot_row, n_kept, nullptr, ws, s);
+  if (e == hipSuccess && gather)
+    e = launch_gather(X, sorted_slot, n_kept, T * (int64_t)k, k, d, dtype == MOE_BF16 ? 2 : 4,
+                      X_sorted, s);
+  return hip_status(e, "moe_dispatch");
+}
+
+// ------------------------------------------------------------- grouped FFN
+size_t moe_grouped_ffn_workspace_size(int64_t max_rows, int G, int d, int F, int dtype) {
+  if (max_rows < 0 || G < 1 || d <= 0 || F <= 0) return 0;
+  return ffn_ws_bytes(max_rows, G, d, F, dtype);
+}
+
+int moe_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets, int G,
+                    const void* W1, const void* W3, const void* W2, int dtype, int d, int F,
+                    int64_t max_rows, float* Yrows, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  MOE_REQUIRE(G >= 1 && G <= 1024, MOE_EUNSUPPORTED, "G = %d must be in [1, 1024]", G);
+  MOE_REQUIRE(max_rows >= 0 && max_rows <= INT32_MAX, MOE_EINVAL, "max_rows out of range");
+  MOE_REQUIRE(d > 0 && F > 0, MOE_EINVAL, "d and F must be positive");
+  MOE_REQUIRE(d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
+              "d = %d and F = %d must be multiples of 128", d, F);
+  MOE_REQUIRE(offsets != nullptr, MOE_EINVAL, "NULL offsets");
+  MOE_REQUIRE(max_rows == 0 || (A && W1 && W3 && W2 && Yrows), MOE_EINVAL,
+              "NULL A, W1, W3, W2 or Yrows");
+  if ((rc = check_ws(ws, ws_bytes, ffn_ws_bytes(max_rows, G, d, F, dtype)))) return rc;
+  return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
+                                       nullptr, -1, dtype, d, F, max_rows, Yrows, ws,
+                                       (hipStream_t)stream),
+                    "moe_grouped_ffn");
+}
+
+// ----------------------------------------------------------------- combine
+int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w, int64_t T,
+                int k, int d, const float* shared, void* Y, int dtype, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  MOE_REQUIRE(T >= 0 && k >= 1, MOE_EINVAL, "need T >= 0 and k >= 1");
+  MOE_REQUIRE(k <= 16, MOE_EUNSUPPORTED, "k = %d > 16 is not supported", k);
+  MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a positive multiple of 128", d);
+  MOE_REQUIRE(T == 0 || (Yrows && slot_row && topk_w && Y), MOE_EINVAL,
+              "NULL Yrows, slot_row, topk_w or Y");
+  return hip_status(launch_combine(Yrows, slot_row, topk_w, T, k, d, shared, nullptr, Y, dtype,
+                                   (hipStream_t)stream),
+                    "moe_combine");
+}
+
+int moe_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E, double* out,
+                void* stream) {
+  MOE_REQUIRE(counts && prob_sum && out, MOE_EINVAL, "NULL counts, prob_sum or out");
+  MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1, MOE_EINVAL, "need T >= 0, k >= 1, E >= 1");
+  return hip_status(launch_balance(counts, prob_sum, T, k, E, out, (hipStream_t)stream),
+                    "moe_balance");
+}
+
+// ----------------------------------------------------------------- forward
+namespace {
+struct FwdLayout {
+  size_t route, ids, w, psum, counts, offsets, nkept, sorted, slotrow, rowtok, hist, yrows, ffn,
+      total;
+};
+
+FwdLayout fwd_layout(const moe_layer* L, int64_t T) {
+  FwdLayout o;
+  const int64_t Tk = T * (int64_t)L->k;
+  const int64_t rows = Tk + (L->n_shared ? T : 0);
+  const int G = L->E + (L->n_shared ? 1 : 0);
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align256(bytes > 0 ? bytes : 1);
+    return here;
+  };
+  o.route = take(route_ws_bytes(T, L->d, L->E));
+  o.ids = take((size_t)Tk * 4);
+  o.w = take((size_t)Tk * 4);
+  o.psum = take((size_t)L->E * 4);
+  o.counts = take((size_t)L->E * 4);
+  o.offsets = take((size_t)(L->E + 2) * 4);
+  o.nkept = take(4);
+  o.sorted = take((size_t)Tk * 4);
+  o.slotrow = take((size_t)Tk * 4);
+  o.rowtok = take((size_t)rows * 4);
+  o.hist = take(dispatch_ws_bytes(T, L->k, L->E));
+  o.yrows = take((size_t)rows * L->d * 4);
+  o.ffn = take(ffn_ws_bytes(rows, G, L->d, L->F, L->dtype));
+  o.total = at;
+  return o;
+}
+
+int check_layer(const moe_layer* L, int64_t T) {
+  MOE_REQUIRE(L != nullptr, MOE_EINVAL, "NULL layer");
+  int rc;
+  if ((rc = check_dtype(L->dtype))) return rc;
+  if ((rc = check_router_dims(T, L->d, L->E, L->k))) return rc;
+  MOE_REQUIRE(L->score == MOE_SOFTMAX || L->score == MOE_SIGMOID, MOE_EINVAL, "score %d unknown", L->score);
+  MOE_REQUIRE(L->n_shared == 0 || L->n_shared == 1, MOE_EUNSUPPORTED, "n_shared must be 0 or 1");
+  MOE_REQUIRE(L->F > 0 && L->F % 128 == 0, MOE_EUNSUPPORTED, "F = %d must be a positive multiple of 128", L->F);
+  MOE_REQUIRE(L->Wg && L->W1 && L->W3 && L->W2, MOE_EINVAL, "NULL router or expert weights");
+  MOE_REQUIRE(!L->n_shared || (L->Ws1 && L->Ws3 && L->Ws2), MOE_EINVAL, "NULL shared-expert weights");
+  MOE_REQUIRE(L->score == MOE_SIGMOID || L->bias == nullptr, MOE_EINVAL,
+              "a selection bias is only defined for the sigmoid router");
+  MOE_REQUIRE(!(L->capacity_factor > 0) || isfinite(L->capacity_factor), MOE_EINVAL,
+              "capacity factor must be finite");
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_forward_workspace_size(const moe_layer* L, int64_t T) {
+  if (!L || T < 0 || L->E < 1 || L->k < 1 || L->d <= 0 || L->F <= 0) return 0;
+  return fwd_layout(L, T).total;
+}
+
+int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe_aux* aux,
+                void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_layer(L, T))) return rc;
+  MOE_REQUIRE(T == 0 || (X && Y), MOE_EINVAL, "NULL X or Y");
+  const FwdLayout o = fwd_layout(L, T);
+  if ((rc = check_ws(ws, ws_bytes, o.total))) return rc;
+  int64_t cap = 0;
+  if (L->capacity_factor > 0) {
+    cap = moe_capacity(L->capacity_factor, T, L->k, L->E);
+    if (cap < 0) return (int)cap;
+  }
+  moe_aux none;
+  memset(&none, 0, sizeof(none));
+  const moe_aux& a = aux ? *aux : none;
+  char* w = (char*)ws;
+  auto pick = [&](void* user, size_t off) { return user ? user : (void*)(w + off); };
+  int32_t* ids = (int32_t*)pick(a.topk_ids, o.ids);
+  float* gw = (float*)pick(a.topk_w, o.w);
+  const bool need_ps = a.prob_sum || a.balance;
+  float* psum = need_ps ? (float*)pick(a.prob_sum, o.psum) : nullptr;
+  int32_t* counts = (int32_t*)pick(a.counts, o.counts);
+  int32_t* offsets = (int32_t*)(w + o.offsets);            // E + 2 entries
+  int32_t* nkept = (int32_t*)pick(a.n_kept, o.nkept);
+  int32_t* sorted = (int32_t*)pick(a.sorted_slot, o.sorted);
+  int32_t* slotrow = (int32_t*)pick(a.slot_row, o.slotrow);
+  int32_t* rowtok = (int32_t*)(w + o.rowtok);
+  float* yrows = (float*)pick(a.Yrows, o.yrows);
+  hipStream_t s = (hipStream_t)stream;
+  const int ns = L->n_shared ? 1 : 0;
+  const int64_t Tk = T * (int64_t)L->k;
+
+  hipError_t e = launch_route(X, L->dtype, T, L->d, L->Wg, L->E, L->bias, L->logit_offset,
+                              L->score, L->k, L->renorm, a.logits, ids, gw, psum, w + o.route, s);
+  if (e == hipSuccess)
+    e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,
+                        nkept, rowtok, w + o.hist, s);
+  if (e == hipSuccess)
+    e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
+                           L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
+                           w + o.ffn, s);
+  if (e == hipSuccess)
+    e = launch_combine(yrows, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
+                       L->dtype, s);
+  if (e == hipSuccess && a.offsets)
+    e = hipMemcpyAsync(a.offsets, offsets, (size_t)(L->E + 1) * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && a.balance) e = launch_balance(counts, psum, T, L->k, L->E, a.balance, s);
+  return hip_status(e, "moe_forward");
+}
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+// Dispatch ("moe_align"): per-expert histogram, exclusive scan, stable rank,
+// capacity drop, and the expert-sorted permutation; plus the row gather.
+//
+// LLM Internals 14.2.1 step 4 (sort token slots by expert so each expert's
+// rows are contiguous; steps 4 and 6 are mutually inverse permutations) and
+// the AI Knowledge Map "MoE" capacity rule C = ceil(c N k / E) with overflow
+// dropped.  Slot s = t*k + j keeps its place iff fewer than C earlier slots
+// chose the same expert.
+//
+// Atomic-free: a wave walks a fixed chunk of slots 64 at a time; lanes that
+// hold the same expert id find each other with one ballot per id bit (a wave
+// "multisplit"), so in-wave ranks come from popcounts, and per-expert running
+// counts live in the wave's own LDS row.  Results are identical run to run.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kAlignChunk = 1024;   // slots per wave (16 groups of 64)
+
+// Mask of active lanes whose expert id equals this lane's.
+__device__ __forceinline__ uint64_t match_id(int e, bool valid, int nbits) {
+  uint64_t eq = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(valid && bit);
+    eq &= bit ? bal : ~bal;
+  }
+  return valid ? eq : 0ull;
+}
+
+__device__ __forceinline__ int nbits_for(int E) {
+  return E <= 1 ? 0 : 32 - __clz(E - 1);
+}
+
+// Pass 1: chunk histograms hist[c][e].
+__global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__ ids,
+                                                     int64_t Tk, int E, int nchunks,
+                                                     int32_t* __restrict__ hist) {
+  __shared__ int32_t cnt_[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= nchunks) return;                           // no block sync below
+  // Each wave owns one LDS row; volatile keeps its in-order LDS traffic as written.
+  volatile int32_t* cnt = cnt_[wave];
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  const int nb = nbits_for(E);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < kAlignChunk / 64; ++g) {
+    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const bool v = s < Tk;
+    const int e = v ? ids[s] : 0;
+    const uint64_t eq = match_id(e, v, nb);
+    if (v && (eq & lt) == 0)                          // lowest lane of its id
+      cnt[e] = cnt[e] + __popcll(eq);
+  }
+  for (int e = lane; e < E; e += 64) hist[(size_t)c * E + e] = cnt[e];
+}
+
+// Pass 2: per-expert chunk bases, counts, capacity, offsets.  One block.
+// Thread e walks the chunks in order; experts are then scanned by the block.
+__global__ __launch_bounds__(256) void k_align_scan(int32_t* __restrict__ hist, int E,
+                                                    int nchunks, int64_t cap,
+                                                    int tail_rows,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ n_kept) {
+  __shared__ int32_t kept[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {          // hist becomes exclusive bases
+      const int h = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = run;
+      run += h;
+    }
+    counts[e] = run;
+  }
+  kept[e] = (e < E) ? (cap > 0 && run > cap ? (int)cap : run) : 0;
+  __syncthreads();
+  if (e == 0) {                                   // E <= 256: serial scan is cheap
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+      const int v = kept[i];
+      offsets[i] = acc;
+      acc += v;
+    }
+    offsets[E] = acc;
+    if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
+    n_kept[0] = acc;
+  }
+}
+
+// Pass 3: stable ranks, drop mask and the permutation.
+__global__ __launch_bounds__(256) void k_align_scatter(
+    const int32_t* __restrict__ ids, int64_t Tk, int k, int E, int nchunks,
+    int64_t cap, const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token) {
+  __shared__ int32_t cnt_[4][256];
+  __shared__ int32_t off[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) off[e] = offsets[e];
+  __syncthreads();
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= nchunks) return;
+  volatile int32_t* cnt = cnt_[wave];
+  for (int e = lane; e < E; e += 64) cnt[e] = base[(size_t)c * E + e];
+  const int nb = nbits_for(E);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < kAlignChunk / 64; ++g) {
+    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const bool v = s < Tk;
+    const int e = v ? ids[s] : 0;
+    const uint64_t eq = match_id(e, v, nb);
+    int rank = 0;
+    if (v) rank = cnt[e] + __popcll(eq & lt);
+    // every lane has read its base before any leader writes the update
+    __builtin_amdgcn_wave_barrier();
+    if (v && (eq & lt) == 0) cnt[e] = rank + __popcll(eq);
+    if (v) {
+      const bool keep = cap <= 0 || rank < cap;
+      const int row = keep ? off[e] + rank : -1;
+      slot_row[s] = row;
+      if (keep) {
+        sorted_slot[row] = (int32_t)s;
+        if (row_token) row_token[row] = (int32_t)(s / k);
+      }
+    }
+  }
+}
+
+// Rows of the shared expert: row_token[R + t] = t, R read on the device.
+__global__ __launch_bounds__(256) void k_tail_tokens(const int32_t* __restrict__ n_kept,
+                                                     int T_, int32_t* __restrict__ row_token) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < T_) row_token[n_kept[0] + t] = t;
+}
+
+// Gather: Xs[r] = X[sorted_slot[r] / k] for r < n_kept.  16-B vectors.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ X,
+                                                     const int32_t* __restrict__ sorted_slot,
+                                                     const int32_t* __restrict__ n_kept,
+                                                     int k, int vec_per_row,
+                                                     uint4* __restrict__ Xs) {
+  const int r = blockIdx.x;
+  if (r >= n_kept[0]) return;
+  const int t = sorted_slot[r] / k;
+  const uint4* src = X + (size_t)t * vec_per_row;
+  uint4* dst = Xs + (size_t)r * vec_per_row;
+  for (int i = threadIdx.x; i < vec_per_row; i += 256) dst[i] = src[i];
+}
+
+__global__ void k_zero_words(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// --------------------------------------------------------------- launchers
+int align_nchunks(int64_t Tk) { return (int)MOE_CEIL_DIV(Tk, kAlignChunk); }
+
+size_t dispatch_ws_bytes(int64_t T, int k, int E) {
+  const int64_t Tk = T * (int64_t)k;
+  return align256((size_t)(align_nchunks(Tk) > 0 ? align_nchunks(Tk) : 1) * E * sizeof(int32_t));
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)MOE_CEIL_DIV(n, 256)), dim3(256), 0, s,
+                     (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t cap,
+                           int tail_rows, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_slot, int32_t* slot_row, int32_t* n_kept,
+                           int32_t* row_token, void* ws, hipStream_t s) {
+  const int64_t Tk = T * (int64_t)k;
+  const int nch = align_nchunks(Tk);
+  int32_t* hist = (int32_t*)ws;
+  const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
+  if (nch > 0)
+    hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(256), 0, s, ids, Tk, E, nch, hist);
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(256), 0, s, hist, E, nch, cap, tail_rows,
+                     counts, offsets, n_kept);
+  if (nch > 0)
+    hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(256), 0, s, ids, Tk, k, E, nch, cap,
+                       hist, offsets, sorted_slot, slot_row, row_token);
+  if (row_token && tail_rows > 0)
+    hipLaunchKernelGGL(k_tail_tokens, dim3((unsigned)MOE_CEIL_DIV(tail_rows, 256)), dim3(256),
+                       0, s, n_kept, tail_rows, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_t* n_kept,
+                         int64_t Tk, int k, int d, int elem_bytes, void* Xs, hipStream_t s) {
+  if (Tk <= 0) return hipSuccess;
+  const int vpr = d * elem_bytes / 16;
+  hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)Tk), dim3(256), 0, s, (const uint4*)X,
+                     sorted_slot, n_kept, k, vpr, (uint4*)Xs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,67 @@
+// Combine: LLM Internals 14.2.1 step 6 and the AI Knowledge Map "MoE" output
+// y = sum_{e in S} g_e E_e(x): gate-weighted sum of each token's expert rows,
+// read back through the inverse permutation (slot_row), plus the shared
+// expert's row.  Dropped slots (row -1) add nothing.  fp32 accumulation in a
+// fixed order (j = 0..k-1, then the shared row), one rounding to the output
+// type, no atomics.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows,
+                                                 const int32_t* __restrict__ slot_row,
+                                                 const float* __restrict__ w, int k, int d,
+                                                 const float* __restrict__ shared,
+                                                 const int32_t* __restrict__ shared_row0,
+                                                 OutT* __restrict__ Y) {
+  const int t = blockIdx.x;
+  __shared__ int32_t rows[16];
+  __shared__ float gw[16];
+  if (threadIdx.x < (unsigned)k) {
+    rows[threadIdx.x] = slot_row[(size_t)t * k + threadIdx.x];
+    gw[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const float* sh = nullptr;
+  if (shared) sh = shared + (size_t)t * d;
+  else if (shared_row0) sh = Yrows + ((size_t)shared_row0[0] + t) * d;
+  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int r = rows[j];
+      if (r < 0) continue;
+      const float4 y = *(const float4*)(Yrows + (size_t)r * d + c);
+      const float g = gw[j];
+      acc.x += g * y.x; acc.y += g * y.y; acc.z += g * y.z; acc.w += g * y.w;
+    }
+    if (sh) {
+      const float4 y = *(const float4*)(sh + c);
+      acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
+    }
+    if constexpr (sizeof(OutT) == 2) {
+      uint2 o;
+      o.x = (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16);
+      o.y = (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16);
+      *(uint2*)(Y + (size_t)t * d + c) = o;
+    } else {
+      *(float4*)(Y + (size_t)t * d + c) = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
+                          int k, int d, const float* shared, const int32_t* shared_row0,
+                          void* Y, int dtype, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)T), dim3(256), 0, s, Yrows, slot_row,
+                       w, k, d, shared, shared_row0, (uint16_t*)Y);
+  else
+    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)T), dim3(256), 0, s, Yrows, slot_row, w,
+                       k, d, shared, shared_row0, (float*)Y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

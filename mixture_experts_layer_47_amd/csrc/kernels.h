@@ -1,0 +1,44 @@
+// Internal launchers shared by the C-ABI layer (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// router.hip
+int router_split(int d);
+size_t route_ws_bytes(int64_t T, int d, int E);
+hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
+                        const float* bias, const float* offset, int score, int k, int renorm,
+                        float* logits, int32_t* ids, float* w, float* prob_sum, void* ws,
+                        hipStream_t s);
+hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E,
+                          double* out, hipStream_t s);
+
+// align.hip
+size_t dispatch_ws_bytes(int64_t T, int k, int E);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t cap, int tail_rows,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                           int32_t* slot_row, int32_t* n_kept, int32_t* row_token, void* ws,
+                           hipStream_t s);
+hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_t* n_kept,
+                         int64_t Tk, int k, int d, int elem_bytes, void* Xs, hipStream_t s);
+
+// gemm.hip
+size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype);
+hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
+                              int G, const void* W1, const void* W3, const void* W2,
+                              const void* W1l, const void* W3l, const void* W2l, int g_last,
+                              int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
+                              hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
+                          int k, int d, const float* shared, const int32_t* shared_row0,
+                          void* Y, int dtype, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,262 @@
+// Router: logits = X W_g (+ offset), scores, top-k and gates.
+//
+// LLM Internals 14.2.1 steps 2-3 and the AI Knowledge Map "MoE" router steps:
+// a linear scoring layer, an fp32 softmax over all E experts (or DeepSeek-V3's
+// per-cell sigmoid affinity with a selection-only bias, eq. 16 as restated in
+// LLM Internals 14.2.3), hard top-k, then renormalisation inside the chosen
+// set.  The study note's pitfalls section fixes the router softmax to fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// --------------------------------------------------------------------------
+// Logits GEMM: part[z][t][e] = sum_{i in slice z} X[t][i] * Wg[e][i].
+// One wave owns a 16-token x 16-expert MFMA block and walks its d-slice,
+// reading both operands straight from global memory (each lane pulls 16 B of
+// a row; X is read once per expert group, Wg stays in L2).  Split-K slices
+// keep >= several thousand waves in flight for the skinny E = 8 / 64 cases.
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_logits(
+    const T* __restrict__ X, const T* __restrict__ Wg, float* __restrict__ part,
+    int T_, int d, int E, int dchunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e0 = blockIdx.y * 64 + wave * 16;
+  if (e0 >= E) return;                       // no block-level sync below
+  const int t0 = blockIdx.x * 16;
+  const int z = blockIdx.z;
+  const int kb = z * dchunk, ke = min(d, kb + dchunk);
+  const int row = lane & 15, grp = lane >> 4;       // 4 lane groups along K
+  const int tok = t0 + row, ex = e0 + row;
+  const bool tv = tok < T_, ev = ex < E;
+  const T* xa = X + (size_t)(tv ? tok : 0) * d;
+  const T* wb = Wg + (size_t)(ev ? ex : 0) * d;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int EPL = 16 / sizeof(T);              // elements per 16-B lane load
+  constexpr int KSTEP = EPL * 4;                   // K covered by one wave step
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int k = kb; k < ke; k += KSTEP) {
+    const int kk = k + grp * EPL;
+    u32x4 a = tv ? *(const u32x4*)(xa + kk) : zero;
+    u32x4 b = ev ? *(const u32x4*)(wb + kk) : zero;
+    if constexpr (sizeof(T) == 2) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, b),
+                                                     acc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]),
+                                                   acc, 0, 0, 0);
+    }
+  }
+  // C layout (16x16): lane holds column (lane & 15), rows 4*(lane>>4) + r.
+  const int col = e0 + (lane & 15);
+  if (col < E) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + grp * 4 + r;
+      if (t < T_) part[((size_t)z * T_ + t) * E + col] = acc[r];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Select: one wave per token.  Lane L holds experts L, L+64, L+128, L+192.
+__device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);   // key descending, lower id wins ties
+}
+
+template <int NE>
+__global__ __launch_bounds__(256) void k_router_select(
+    const float* __restrict__ part, int nsplit, int T_, int E,
+    const float* __restrict__ offset, const float* __restrict__ bias, int score,
+    int k, int renorm, float* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ wts, float* __restrict__ ps_part) {
+  __shared__ float sp[4][NE * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool tok_ok = t < T_;
+  float l[NE], p[NE];
+  double key[NE], s64[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    float v = -INFINITY;
+    if (tok_ok && e < E) {
+      v = 0.f;
+      for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T_ + t) * E + e];
+      if (offset) v += offset[e];
+      if (logits) logits[(size_t)t * E + e] = v;
+    }
+    l[i] = v;
+  }
+  if (score == MOE_SOFTMAX) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) m = fmaxf(m, l[i]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      p[i] = (e < E && tok_ok) ? expf(l[i] - m) : 0.f;
+      zs += p[i];
+    }
+    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
+    const float inv = 1.f / zs;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      p[i] *= inv;                       // full-row softmax probability
+      key[i] = (double)l[i];             // selection on the logit
+      s64[i] = (double)p[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = (e < E && tok_ok);
+      const double s = ok ? 1.0 / (1.0 + exp(-(double)l[i])) : 0.0;
+      s64[i] = s;
+      p[i] = (float)s;
+      key[i] = ok ? s + (bias ? (double)bias[e] : 0.0) : -INFINITY;
+    }
+  }
+  // Iterative wave arg-max, k rounds; lane j keeps the j-th winner.
+  uint32_t taken = 0;
+  int my_id = 0;
+  double my_val = 0.0, tot = 0.0;
+  for (int j = 0; j < k; ++j) {
+    double bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ok_ = __shfl_xor(bk, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ok_, oi, bk, bi)) { bk = ok_; bi = oi; }
+    }
+    // owner lane marks the winner; every lane fetches its score
+    const int oi = bi >> 6, ol = bi & 63;
+    double mine = 0.0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) if (i == oi) mine = s64[i];
+    const double val = __shfl(mine, ol);
+    if (lane == ol) taken |= 1u << oi;
+    if (lane == j) { my_id = bi; my_val = val; }
+    tot += val;                                  // fixed order j = 0..k-1
+  }
+  if (tok_ok && lane < k) {
+    ids[(size_t)t * k + lane] = my_id;
+    wts[(size_t)t * k + lane] = (float)(renorm ? my_val / tot : my_val);
+  }
+  if (ps_part) {   // per-block partial of sum_t p[t][e], fixed summation order
+#pragma unroll
+    for (int i = 0; i < NE; ++i) sp[wave][lane + 64 * i] = tok_ok ? p[i] : 0.f;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256)
+      ps_part[(size_t)blockIdx.x * E + e] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
+  }
+}
+
+// Final prob_sum: one block per expert, fixed-order tree over block partials.
+__global__ __launch_bounds__(256) void k_prob_sum(const float* __restrict__ ps_part,
+                                                  int nblk, int E,
+                                                  float* __restrict__ prob_sum) {
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  float acc = 0.f;
+  for (int b = threadIdx.x; b < nblk; b += 256) acc += ps_part[(size_t)b * E + e];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) prob_sum[e] = red[0];
+}
+
+// Balance statistic E * sum_e (counts_e / (T k)) (prob_sum_e / T), in fp64.
+__global__ __launch_bounds__(256) void k_balance(const int32_t* __restrict__ counts,
+                                                 const float* __restrict__ prob_sum,
+                                                 int64_t T_, int k, int E,
+                                                 double* __restrict__ out) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int e = threadIdx.x; e < E; e += 256)
+    acc += (double)counts[e] * (double)prob_sum[e];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double tk = (double)T_ * (double)k;
+    out[0] = (T_ > 0) ? (double)E * red[0] / (tk * (double)T_) : 0.0;
+  }
+}
+
+// --------------------------------------------------------------- launchers
+int router_split(int d) {
+  int s = d / 1024;
+  return s < 1 ? 1 : (s > 8 ? 8 : s);
+}
+
+size_t route_ws_bytes(int64_t T, int d, int E) {
+  const size_t split = (size_t)router_split(d);
+  size_t b = align256(split * (size_t)T * E * sizeof(float));      // partial logits
+  b += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));   // prob_sum partials
+  return b;
+}
+
+hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
+                        int E, const float* bias, const float* offset, int score,
+                        int k, int renorm, float* logits, int32_t* ids, float* w,
+                        float* prob_sum, void* ws, hipStream_t s) {
+  if (T == 0) {
+    if (prob_sum) return launch_zero_f32(prob_sum, E, s);
+    return hipSuccess;
+  }
+  const int split = router_split(d);
+  const int kstep = 128;   // keep slices a multiple of both lane steps
+  const int dchunk = MOE_CEIL_DIV(MOE_CEIL_DIV(d, split), kstep) * kstep;
+  char* p = (char*)ws;
+  float* part = (float*)p;  p += align256((size_t)split * T * E * sizeof(float));
+  float* ps_part = (float*)p;
+  dim3 g1((unsigned)MOE_CEIL_DIV(T, 16), (unsigned)MOE_CEIL_DIV(E, 64), (unsigned)split);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
+                       (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk);
+  else
+    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
+                       (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk);
+  const int nblk = (int)MOE_CEIL_DIV(T, 4);
+  float* psp = prob_sum ? ps_part : nullptr;
+  const int ne = MOE_CEIL_DIV(E, 64);
+#define MOE_SEL(NE_)                                                                 \
+  hipLaunchKernelGGL(k_router_select<NE_>, dim3(nblk), dim3(256), 0, s, part, split, \
+                     (int)T, E, offset, bias, score, k, renorm, logits, ids, w, psp)
+  switch (ne) {
+    case 1: MOE_SEL(1); break;
+    case 2: MOE_SEL(2); break;
+    case 3: MOE_SEL(3); break;
+    default: MOE_SEL(4); break;
+  }
+#undef MOE_SEL
+  if (prob_sum)
+    hipLaunchKernelGGL(k_prob_sum, dim3(E), dim3(256), 0, s, ps_part, nblk, E, prob_sum);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k,
+                          int E, double* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_balance, dim3(1), dim3(256), 0, s, counts, prob_sum, T, k, E, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -65,7 +65,7 @@ import numpy as np
 
 __all__ = [
     "capacity", "router_logits", "scores", "select_topk", "gates", "route",
-    "dispatch", "silu", "round_bf16", "expert_ffn", "forward",
+    "dispatch", "silu", "round_bf16", "expert_ffn", "combine", "forward",
     "forward_token_loop", "forward_dense_masked", "balance_value",
     "balance_stat", "expert_weight_shapes",
 ]
@@ -260,18 +260,33 @@ def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
         if b > a:
             tok = disp["sorted_slot"][a:b] // k
             rows[a:b] = expert_ffn(X[tok], W1[e], W3[e], W2[e], bf16_h)
-    # step 6: gate-weighted sum through the inverse permutation
-    Y = np.zeros((T, d))
-    for j in range(k):
-        r = disp["slot_row"].reshape(T, k)[:, j]
-        ok = r >= 0
-        Y[ok] += g[ok, j][:, None] * rows[r[ok]]
     sh = None
     if shared is not None:
         sh = expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
-        Y = Y + sh
+    Y = combine(rows, disp["slot_row"], g, sh)
     return {"logits": own, "route_logits": lg, "ids": ids, "gates": g,
             "probs": p, "dispatch": disp, "rows": rows, "shared": sh, "Y": Y}
+
+
+def combine(rows, slot_row, gates, shared_rows=None):
+    """Step 6 [Book 14.2.1]: Y[t] = sum_j g[t,j] * rows[slot_row[t*k+j]] over
+    kept slots (dropped slots, row -1, add nothing: [KMap capacity]), plus the
+    shared expert's output with weight 1 (R10)."""
+    g = np.asarray(gates, dtype=np.float64)
+    T, k = g.shape
+    rows = np.asarray(rows, dtype=np.float64)
+    sr = np.asarray(slot_row).reshape(T, k)
+    d = rows.shape[1] if rows.ndim == 2 else 0
+    if shared_rows is not None:
+        d = np.asarray(shared_rows).shape[1]
+    Y = np.zeros((T, d))
+    for j in range(k):
+        r = sr[:, j]
+        ok = r >= 0
+        Y[ok] += g[ok, j][:, None] * rows[r[ok]]
+    if shared_rows is not None:
+        Y = Y + np.asarray(shared_rows, dtype=np.float64)
+    return Y
 
 
 def forward_token_loop(X, Wg, W1, W3, W2, *, k, score_func="softmax",

@@ -1,0 +1,142 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every entry point that include/moe.h declares,
+compute capacities exactly, size workspaces, and reject invalid arguments on
+the host before anything is launched (so these calls never touch a device).
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from mixture_experts_layer_47_amd import _lib
+from oracle import moe_oracle as O
+
+ROOT = Path(__file__).resolve().parent.parent
+
+
+def _header_functions():
+    text = (ROOT / "include" / "moe.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _header_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("cf,N,k,E", [(1.0, 6, 2, 4), (2.0, 6, 2, 4), (1.25, 8192, 2, 64),
+                                      (1.0, 8192, 1, 64), (1.25, 8192, 1, 64), (1.1, 100, 1, 1),
+                                      (1.1, 50, 2, 1), (0.3, 10, 1, 1), (1.0, 7, 2, 4),
+                                      (0.7, 1000, 3, 7), (1.0, 0, 2, 4), (3.3, 12345, 8, 256)])
+def test_capacity_matches_oracle(L, cf, N, k, E):
+    assert _lib.capacity(cf, N, k, E) == O.capacity(cf, N, k, E)
+
+
+def test_capacity_rejects_bad_args(L):
+    for args in [(0.0, 6, 2, 4), (-1.0, 6, 2, 4), (float("nan"), 6, 2, 4),
+                 (float("inf"), 6, 2, 4), (1.0, -1, 2, 4), (1.0, 6, 0, 4), (1.0, 6, 2, 0)]:
+        assert L.moe_capacity(*args) < 0
+        assert _lib.last_error()
+
+
+def test_workspace_sizes_positive(L):
+    assert L.moe_route_workspace_size(4096, 7168, 256) > 4096 * 256 * 4
+    assert L.moe_dispatch_workspace_size(4096, 8, 256) >= 32 * 256 * 4
+    assert L.moe_grouped_ffn_workspace_size(32768, 256, 7168, 2048, 1) >= 32768 * 2048 * 2
+    lay = _lib.MoeLayerC(1, 1, 1, 7168, 256, 8, 2048, 1, 0.0, 1, None, None, 1, 1, 1, 1, 1, 1)
+    assert L.moe_forward_workspace_size(ctypes.byref(lay), 4096) > (32768 + 4096) * 7168 * 4
+
+
+def _route(L, **over):
+    a = dict(X=1, dtype=1, T=16, d=256, Wg=1, E=8, bias=None, off=None, score=0, k=2, renorm=1,
+             logits=None, ids=1, w=1, ps=None, ws=256, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return L.moe_route(a["X"], a["dtype"], a["T"], a["d"], a["Wg"], a["E"], a["bias"], a["off"],
+                       a["score"], a["k"], a["renorm"], a["logits"], a["ids"], a["w"], a["ps"],
+                       a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_route_validation(L):
+    assert _route(L, k=0) == -1
+    assert _route(L, k=9) == -1                 # k > E
+    assert _route(L, E=0) == -1
+    assert _route(L, T=-1) == -1
+    assert _route(L, dtype=7) == -1
+    assert _route(L, score=5) == -1
+    assert _route(L, X=None) == -1
+    assert _route(L, ids=None) == -1
+    assert _route(L, bias=1) == -1              # bias only with a sigmoid router
+    assert _route(L, d=200) == -2               # d not a multiple of 128
+    assert _route(L, E=300, k=2) == -2
+    assert _route(L, E=32, k=17) == -2
+    assert _route(L, ws_bytes=16) == -3
+    assert _route(L, ws=None) == -1
+    assert _route(L, ws=257) == -1              # misaligned workspace
+    assert "workspace" in _lib.last_error()
+
+
+def test_dispatch_validation(L):
+    base = dict(ids=1, T=16, k=2, E=8, cap=0, counts=1, offsets=1, sorted=1, slot=1, nk=1,
+                X=None, dt=1, d=0, Xs=None, ws=256, wsb=1 << 30)
+
+    def call(**o):
+        a = dict(base, **o)
+        return L.moe_dispatch(a["ids"], a["T"], a["k"], a["E"], a["cap"], a["counts"],
+                              a["offsets"], a["sorted"], a["slot"], a["nk"], a["X"], a["dt"],
+                              a["d"], a["Xs"], a["ws"], a["wsb"], None)
+    assert call(k=9) == -1
+    assert call(counts=None) == -1
+    assert call(ids=None) == -1
+    assert call(Xs=1) == -1                     # X_sorted without X
+    assert call(Xs=1, X=1, d=100) == -2
+    assert call(E=257, k=1) == -2
+    assert call(wsb=0) == -3
+
+
+def test_ffn_and_combine_validation(L):
+    def ffn(**o):
+        a = dict(A=1, rt=None, off=1, G=8, W1=1, W3=1, W2=1, dt=1, d=256, F=512, mr=64, Y=1,
+                 ws=256, wsb=1 << 30)
+        a.update(o)
+        return L.moe_grouped_ffn(a["A"], a["rt"], a["off"], a["G"], a["W1"], a["W3"], a["W2"],
+                                 a["dt"], a["d"], a["F"], a["mr"], a["Y"], a["ws"], a["wsb"], None)
+    assert ffn(G=0) == -2
+    assert ffn(F=500) == -2
+    assert ffn(off=None) == -1
+    assert ffn(W2=None) == -1
+    assert ffn(dt=3) == -1
+    assert ffn(wsb=10) == -3
+    assert L.moe_combine(1, 1, 1, 16, 0, 256, None, 1, 1, None) == -1
+    assert L.moe_combine(1, 1, 1, 16, 17, 256, None, 1, 1, None) == -2
+    assert L.moe_combine(None, 1, 1, 16, 2, 256, None, 1, 1, None) == -1
+    assert L.moe_balance(None, 1, 16, 2, 8, 1, None) == -1
+
+
+def test_forward_validation(L):
+    def lay(**o):
+        a = dict(dtype=1, score=0, renorm=1, d=256, E=8, k=2, F=512, ns=0, cf=0.0, Wg=1,
+                 bias=None, off=None, W1=1, W3=1, W2=1, Ws1=None, Ws3=None, Ws2=None)
+        a.update(o)
+        return _lib.MoeLayerC(*a.values())
+
+    def fwd(layer, T=16, X=1, Y=1, wsb=1 << 40):
+        return L.moe_forward(ctypes.byref(layer), X, T, Y, None, 256, wsb, None)
+    assert fwd(lay(k=0)) == -1
+    assert fwd(lay(ns=1)) == -1                 # shared expert without weights
+    assert fwd(lay(ns=2)) == -2
+    assert fwd(lay(F=200)) == -2
+    assert fwd(lay(bias=1)) == -1
+    assert fwd(lay(cf=float("inf"))) == -1
+    assert fwd(lay(W2=None)) == -1
+    assert fwd(lay(), X=None) == -1
+    assert fwd(lay(), wsb=100) == -3

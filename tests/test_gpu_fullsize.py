@@ -1,0 +1,100 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one moe_forward call through the C ABI).
+
+Integer results (ids, counts, offsets, permutation, drop mask) are checked
+bit-exactly on every token; float results on samples the oracle can compute
+one by one: router logits of sampled tokens, expert rows of sampled experts,
+shared-expert rows of sampled tokens, and the full combine recomputed by the
+oracle from the device's own expert rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_47_amd as moe
+from mixture_experts_layer_47_amd.workloads import WORKLOADS, make_inputs
+from oracle import moe_oracle as O
+from tests import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_fullsize_workload(name):
+    w = WORKLOADS[name]
+    print(f"[case] fullsize {name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
+    inp = make_inputs(w, DEV)
+    layer = moe.layer_from_inputs(inp)
+    Y, aux = moe.forward(layer, inp["X"], aux=True)
+    torch.cuda.synchronize()
+    bf16 = w.dtype == "bf16"
+    rng = np.random.default_rng(1234)
+    X = inp["X"]
+
+    # --- R1: logits of sampled tokens against fp64 dot products
+    lg = H.np64(aux["logits"])
+    ts = np.sort(rng.choice(w.T, size=min(64, w.T), replace=False))
+    xs = H.np64(X[torch.as_tensor(ts, device=DEV)])
+    off = None if inp["offset"] is None else H.np64(inp["offset"])
+    H.check_logits(lg[ts], O.router_logits(xs, H.np64(inp["Wg"]).T, off))
+
+    # --- R2: routing on every token (oracle top-k on the device's fp32 logits)
+    bias = None if inp["bias"] is None else H.np64(inp["bias"])
+    ids_ref, g_ref, p_ref = O.route(lg, w.k, w.score, w.renorm, bias)
+    _, keys = O.select_topk(lg, w.k, w.score, bias)
+    ids = H.np64(aux["topk_ids"]).astype(np.int64)
+    ties = H.check_ids(ids, ids_ref, keys if w.score == "sigmoid" else None)
+    print(f"[info] {name}: near-tie tokens {ties}", flush=True)
+    # downstream integer checks use the device ids (identical unless a near-tie)
+    H.check_gates(H.np64(aux["topk_w"]), O.gates(lg, ids, w.score, w.renorm))
+
+    # --- D1: dispatch on every slot, bit-exact
+    cap = O.capacity(w.cf, w.T, w.k, w.E) if w.cf else None
+    d = O.dispatch(ids, w.E, cap)
+    R = d["n_kept"]
+    assert int(aux["n_kept"].item()) == R
+    assert aux["counts"].cpu().numpy().tolist() == d["counts"].tolist()
+    assert aux["offsets"].cpu().numpy().tolist() == d["offsets"].tolist()
+    assert aux["slot_row"].cpu().numpy().tolist() == d["slot_row"].tolist()
+    assert aux["sorted_slot"].cpu().numpy()[:R].tolist() == d["sorted_slot"].tolist()
+
+    # --- G1/G2: sampled experts' rows (up to 8 rows from each of 3 touched experts)
+    touched = np.flatnonzero(d["kept"] > 0)
+    for e in rng.choice(touched, size=min(3, touched.size), replace=False):
+        a, b = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        rsel = np.sort(rng.choice(np.arange(a, b), size=min(8, b - a), replace=False))
+        tok = d["sorted_slot"][rsel] // w.k
+        xr = H.np64(X[torch.as_tensor(tok, device=DEV)])
+        W1, W3, W2 = H.expert_logical(inp, int(e))
+        ref = O.expert_ffn(xr, W1, W3, W2, bf16_h=bf16)
+        got = H.np64(aux["Yrows"][torch.as_tensor(rsel, device=DEV)])
+        H.check_rows(got, ref, bf16, f"{name} expert {e} rows")
+
+    # --- S: shared expert rows of sampled tokens
+    if inp["shared"] is not None:
+        s1, s3, s2 = (H.np64(t).T for t in inp["shared"])
+        ref = O.expert_ffn(xs, s1, s3, s2, bf16_h=bf16)
+        got = H.np64(aux["Yrows"][torch.as_tensor(R + ts, device=DEV)])
+        H.check_rows(got, ref, bf16, f"{name} shared rows")
+
+    # --- C: full combine from the device's expert rows
+    rows = H.np64(aux["Yrows"])
+    sh = rows[R:R + w.T] if inp["shared"] is not None else None
+    Yref = O.combine(rows[:R], d["slot_row"], H.np64(aux["topk_w"]), sh)
+    H.check_rows(H.np64(Y), Yref, bf16, f"{name} Y (combine)", output_rounding=True)
+
+    # --- B: balance statistic
+    ps = H.np64(aux["prob_sum"])
+    assert np.abs(ps - p_ref.sum(axis=0)).max() <= 1e-4 * max(1.0, ps.max())
+    bal = O.balance_stat(d["counts"], p_ref.sum(axis=0), w.T, w.k)
+    assert abs(aux["balance"].item() - bal) <= 1e-5 * max(1.0, bal)
+    print(f"[info] {name}: R={R} dropped={w.T * w.k - R} touched={touched.size} "
+          f"balance={bal:.4f}", flush=True)

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Reduced workloads (several tiles per expert, ragged tails) are compared
+element by element; the full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_47_amd as moe
+from mixture_experts_layer_47_amd.workloads import SMALL, Workload, make_inputs
+from oracle import moe_oracle as O
+from tests import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _oracle_forward(inp, lg_gpu):
+    w = inp["workload"]
+    L = H.logical(inp)
+    cap = O.capacity(w.cf, w.T, w.k, w.E) if w.cf else None
+    return O.forward(L["X"], L["Wg"], L["W1"], L["W3"], L["W2"], k=w.k, score_func=w.score,
+                     renorm=w.renorm, bias=L["bias"], offset=L["offset"], cap=cap,
+                     shared=L["shared"], bf16_h=(w.dtype == "bf16"), logits=lg_gpu), cap
+
+
+def _full_check(inp):
+    w = inp["workload"]
+    layer = moe.layer_from_inputs(inp)
+    Y, aux = moe.forward(layer, inp["X"], aux=True)
+    torch.cuda.synchronize()
+    lg = H.np64(aux["logits"])
+    ref, cap = _oracle_forward(inp, lg)
+    bf16 = w.dtype == "bf16"
+    # R1: logits against the oracle's own fp64 logits
+    H.check_logits(lg, ref["logits"])
+    # R2: ids exact (oracle top-k on the device's fp32 logits), gates within tolerance
+    _, keys = O.select_topk(lg, w.k, w.score, H.logical(inp)["bias"])
+    ties = H.check_ids(H.np64(aux["topk_ids"]).astype(np.int64), ref["ids"],
+                       keys if w.score == "sigmoid" else None)
+    assert ties == 0, "near-tie reordering in a small workload"
+    H.check_gates(H.np64(aux["topk_w"]), ref["gates"])
+    # D1: dispatch bit-exact
+    d = ref["dispatch"]
+    R = d["n_kept"]
+    assert int(aux["n_kept"].item()) == R
+    assert aux["counts"].cpu().numpy().tolist() == d["counts"].tolist()
+    assert aux["offsets"].cpu().numpy().tolist() == d["offsets"].tolist()
+    assert aux["slot_row"].cpu().numpy().tolist() == d["slot_row"].tolist()
+    assert aux["sorted_slot"].cpu().numpy()[:R].tolist() == d["sorted_slot"].tolist()
+    # G1/G2: expert rows; S: shared rows
+    rows = H.np64(aux["Yrows"])
+    if R:
+        H.check_rows(rows[:R], ref["rows"], bf16, f"{w.name} expert rows")
+    if ref["shared"] is not None:
+        H.check_rows(rows[R:R + w.T], ref["shared"], bf16, f"{w.name} shared rows")
+    # C: layer output
+    H.check_rows(H.np64(Y), ref["Y"], bf16, f"{w.name} Y", output_rounding=True)
+    # dropped-everything tokens are exactly zero
+    dead = (np.asarray(d["slot_row"]).reshape(w.T, w.k) < 0).all(axis=1)
+    if ref["shared"] is None and dead.any():
+        assert (H.np64(Y)[dead] == 0).all()
+    # B: prob_sum and the balance statistic
+    ps_ref = ref["probs"].sum(axis=0)
+    ps = H.np64(aux["prob_sum"])
+    assert np.abs(ps - ps_ref).max() <= 1e-5 * max(1.0, np.abs(ps_ref).max())
+    bal_ref = O.balance_stat(d["counts"], ps_ref, w.T, w.k)
+    assert abs(aux["balance"].item() - bal_ref) <= 1e-5 * max(1.0, abs(bal_ref))
+    return Y, aux
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_workloads(name):
+    w = SMALL[name]
+    _announce(f"forward {w.name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}")
+    inp = make_inputs(w, DEV)
+    _full_check(inp)
+
+
+EDGE = {
+    "T1": Workload("T1", T=1, d=256, E=8, k=2, F=256, seed=11),
+    "k_eq_E": Workload("k_eq_E", T=37, d=256, E=4, k=4, F=256, seed=12),
+    "E1_k1": Workload("E1_k1", T=70, d=128, E=1, k=1, F=128, seed=13),
+    "ragged_tk": Workload("ragged_tk", T=45, d=384, E=6, k=3, F=384, seed=14),
+    "cap_c1": Workload("cap_c1", T=50, d=256, E=8, k=2, F=256, cf=0.08, seed=15),
+    "cap_large": Workload("cap_large", T=50, d=256, E=8, k=2, F=256, cf=64.0, seed=16),
+    "sigmoid_norenorm": Workload("sigmoid_norenorm", T=64, d=256, E=16, k=4, F=256,
+                                 score="sigmoid", renorm=False, bias_std=0.01, seed=17),
+    "softmax_norenorm_f32": Workload("softmax_norenorm_f32", T=40, d=256, E=8, k=2, F=256,
+                                     dtype="f32", renorm=False, seed=18),
+    "shared_f32": Workload("shared_f32", T=33, d=256, E=8, k=2, F=256, dtype="f32",
+                           n_shared=1, seed=19),
+    "E256_k16": Workload("E256_k16", T=20, d=256, E=256, k=16, F=128, score="sigmoid",
+                         bias_std=0.01, seed=20),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_forward_edge_cases(name):
+    w = EDGE[name]
+    _announce(f"edge {name}")
+    inp = make_inputs(w, DEV)
+    if name == "E1_k1":
+        # a single expert: the layer reduces to one dense SwiGLU FFN
+        Y = moe.forward(moe.layer_from_inputs(inp), inp["X"])
+        L = H.logical(inp)
+        dense = O.expert_ffn(L["X"], L["W1"][0], L["W3"][0], L["W2"][0], bf16_h=True)
+        H.check_rows(H.np64(Y), dense, True, "E1 dense", output_rounding=True)
+    _full_check(inp)
+
+
+def test_collapse_all_tokens_to_one_expert():
+    """Router collapse: every token's top choice is expert 5; capacity keeps
+    only the first C of its slots and drops the rest."""
+    w = Workload("collapse", T=300, d=256, E=8, k=2, F=256, cf=1.0, seed=21)
+    _announce("collapse")
+    inp = make_inputs(w, DEV)
+    inp["Wg"].zero_()
+    off = torch.zeros(8, device=DEV)
+    off[5] = 10.0
+    off[2] = 5.0
+    inp["offset"] = off
+    Y, aux = _full_check(inp)
+    C = O.capacity(1.0, 300, 2, 8)
+    counts = aux["counts"].cpu().tolist()
+    assert counts[5] == 300 and counts[2] == 300
+    assert int(aux["n_kept"].item()) == 2 * C
+
+
+def test_empty_batch():
+    w = Workload("empty", T=0, d=256, E=8, k=2, F=256, seed=22)
+    _announce("empty batch")
+    inp = make_inputs(w, DEV)
+    Y, aux = moe.forward(moe.layer_from_inputs(inp), inp["X"], aux=True)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 256)
+    assert aux["counts"].cpu().tolist() == [0] * 8
+    assert int(aux["n_kept"].item()) == 0
+
+
+def test_deterministic_bitwise():
+    w = SMALL["dsv3_prefill"]
+    _announce("determinism")
+    inp = make_inputs(w, DEV)
+    f = moe.Forward(moe.layer_from_inputs(inp), inp["X"], aux=True)
+    Y1 = f().clone()
+    a1 = {k: v.clone() for k, v in f.aux.items()}
+    for _ in range(3):
+        Y2 = f()
+        torch.cuda.synchronize()
+        assert torch.equal(Y1, Y2)
+        for k in ("topk_ids", "topk_w", "slot_row", "sorted_slot", "counts", "Yrows",
+                  "prob_sum", "logits"):
+            assert torch.equal(a1[k], f.aux[k]), k
+
+
+# ---------------------------------------------------------- entry points --
+def test_route_entry_point():
+    w = SMALL["dsv3_prefill"].with_(T=333)
+    _announce("moe_route")
+    inp = make_inputs(w, DEV)
+    r = moe.route(inp["X"], inp["Wg"], w.k, w.score, w.renorm, bias=inp["bias"])
+    torch.cuda.synchronize()
+    L = H.logical(inp)
+    lg = H.np64(r["logits"])
+    H.check_logits(lg, O.router_logits(L["X"], L["Wg"]))
+    ids, g, p = O.route(lg, w.k, w.score, w.renorm, L["bias"])
+    _, keys = O.select_topk(lg, w.k, w.score, L["bias"])
+    H.check_ids(H.np64(r["ids"]).astype(np.int64), ids, keys)
+    H.check_gates(H.np64(r["w"]), g)
+    assert np.allclose(H.np64(r["prob_sum"]), p.sum(axis=0), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("T,k,E,C", [(1, 1, 1, 0), (100, 2, 8, 0), (1000, 8, 256, 0),
+                                     (1000, 8, 256, 20), (3000, 1, 64, 40), (777, 3, 5, 1),
+                                     (5000, 4, 17, 900)])
+def test_dispatch_entry_point(T, k, E, C):
+    _announce(f"moe_dispatch T={T} k={k} E={E} C={C}")
+    g = torch.Generator().manual_seed(T * 31 + E)
+    # skewed distinct ids per token
+    pri = torch.rand((T, E), generator=g) * torch.linspace(1.0, 3.0, E)
+    ids = torch.topk(pri, k, dim=1).indices.to(torch.int32)
+    X = torch.randn((T, 128), generator=g).to(torch.bfloat16)
+    out = moe.dispatch(ids.to(DEV), E, C, X=X.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.dispatch(ids.numpy(), E, C if C > 0 else None)
+    R = ref["n_kept"]
+    assert int(out["n_kept"].item()) == R
+    assert out["counts"].cpu().tolist() == ref["counts"].tolist()
+    assert out["offsets"].cpu().tolist() == ref["offsets"].tolist()
+    assert out["slot_row"].cpu().tolist() == ref["slot_row"].tolist()
+    assert out["sorted_slot"].cpu()[:R].tolist() == ref["sorted_slot"].tolist()
+    # D2: the gather is an exact copy of the chosen token rows
+    tok = torch.as_tensor(ref["sorted_slot"] // k)
+    assert torch.equal(out["X_sorted"][:R].cpu(), X[tok])
+
+
+FFN_SHAPES = {
+    # medium tiles: empty, single-row, multi-tile and ragged groups
+    "medium": (256, 384, [0, 1, 300, 31, 64, 129, 7], 5),
+    # large tiles, down projection with d % 256 != 0
+    "large_d384": (384, 256, [300, 257, 520], 5),
+    # large tiles, one empty group
+    "large_d512": (512, 512, [600, 0], 5),
+    # decode-sized groups (a few rows each)
+    "decode": (512, 256, [2, 0, 1, 3, 2, 2, 0, 1, 4, 2, 1, 2, 3, 1, 2, 2], 0),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("use_row_token", [False, True])
+@pytest.mark.parametrize("shape", list(FFN_SHAPES))
+def test_grouped_ffn_entry_point(dtype, use_row_token, shape):
+    _announce(f"moe_grouped_ffn {shape} {dtype} row_token={use_row_token}")
+    d, F, counts, slack = FFN_SHAPES[shape]
+    G = len(counts)
+    g = torch.Generator().manual_seed(5)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    T = 400
+    X = torch.randn((T, d), generator=g).to(tdt)
+    W1 = (torch.randn((G, F, d), generator=g) / d ** 0.5).to(tdt)
+    W3 = (torch.randn((G, F, d), generator=g) / d ** 0.5).to(tdt)
+    W2 = (torch.randn((G, d, F), generator=g) / F ** 0.5).to(tdt)
+    R = sum(counts)
+    offs = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32)
+    tok = torch.randint(0, T, (R,), generator=g, dtype=torch.int32)
+    A = X if use_row_token else X[tok.long()]
+    Y = moe.grouped_ffn(A.to(DEV), offs.to(DEV), W1.to(DEV), W3.to(DEV), W2.to(DEV), R + slack,
+                        row_token=tok.to(DEV) if use_row_token else None)
+    torch.cuda.synchronize()
+    Xr = X[tok.long()].double().numpy()
+    for e in range(G):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            continue
+        ref = O.expert_ffn(Xr[a:b], W1[e].double().numpy().T, W3[e].double().numpy().T,
+                           W2[e].double().numpy().T, bf16_h=(dtype == "bf16"))
+        H.check_rows(H.np64(Y[a:b]), ref, dtype == "bf16")
+
+
+def test_combine_entry_point():
+    _announce("moe_combine")
+    T, k, d = 257, 3, 384
+    g = torch.Generator().manual_seed(9)
+    R = 600
+    rows = torch.randn((R, d), generator=g)
+    sr = torch.randint(-1, R, (T * k,), generator=g, dtype=torch.int32)
+    w = torch.rand((T, k), generator=g)
+    sh = torch.randn((T, d), generator=g)
+    for dt in (torch.float32, torch.bfloat16):
+        Y = moe.combine(rows.to(DEV), sr.to(DEV), w.to(DEV), dt, shared=sh.to(DEV))
+        torch.cuda.synchronize()
+        ref = O.combine(rows.double().numpy(), sr.numpy(), w.double().numpy(),
+                        sh.double().numpy())
+        H.check_rows(H.np64(Y), ref, dt == torch.bfloat16, f"combine {dt}",
+                     output_rounding=True)
+        if dt == torch.float32:
+            assert H.rel_err(H.np64(Y), ref) <= 1e-6
+
+
+def test_balance_entry_point_page_example():
+    """The balance statistic kernel on the page's example values:
+    f = [.7,.1,.1,.1], P = [.4,.2,.2,.2] -> 1.36 (T = 10, top-1)."""
+    _announce("moe_balance")
+    counts = torch.tensor([7, 1, 1, 1], dtype=torch.int32, device=DEV)
+    ps = torch.tensor([4.0, 2.0, 2.0, 2.0], device=DEV)
+    out = moe.balance(counts, ps, 10, 1)
+    assert abs(out.item() - 1.36) < 1e-12
