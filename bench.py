@@ -1,0 +1,216 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+One step = one moe_forward call (router -> top-k -> capacity -> dispatch ->
+grouped SwiGLU -> combine) over one batch of synthetic, seeded input that is
+already resident in HBM.  Prints one JSON line:
+
+  value        tokens/s over the K timed steps (T * K / wall time between
+               two device synchronisations)
+  roofline     the dominant kernel (gate/up grouped GEMM + SwiGLU): its
+               algorithmic FLOPs or bytes per launch divided by its average
+               duration, measured with HIP events recorded on the launch
+               stream inside the timed region
+  cpu_baseline the CPU oracle (numpy float64) timed on a bounded token sample
+               of the same workload, on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM GB/s peak (decode)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_47_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def up_kernel_work(w, counts_kept, n_kept):
+    """Algorithmic work of one gate/up launch (real kept rows only).
+
+    FLOPs = 2 * rows * d * 2F (gate and up projections).
+    Bytes = W1 + W3 of every expert that has rows (each read once)
+          + the X rows the launch reads (T distinct tokens, each read once)
+          + H written (rows * F).
+    """
+    es = 2 if w.dtype == "bf16" else 4
+    rows = n_kept + (w.T if w.n_shared else 0)
+    touched = int((counts_kept > 0).sum()) + (1 if w.n_shared else 0)
+    flops = 4.0 * rows * w.d * w.F
+    bytes_ = touched * 2.0 * w.F * w.d * es + w.T * w.d * es + rows * w.F * es
+    return flops, bytes_, touched, rows
+
+
+def cpu_baseline(w, inp, target_s=15.0):
+    """Time the oracle on the first S tokens of the batch (S sized for ~target_s)."""
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+    log("cpu baseline: copying weights to host (untimed)")
+    Wg = f64(inp["Wg"]).T
+    W1 = f64(inp["W1"]).transpose(0, 2, 1)
+    W3 = f64(inp["W3"]).transpose(0, 2, 1)
+    W2 = f64(inp["W2"]).transpose(0, 2, 1)
+    sh = None if inp["shared"] is None else tuple(f64(t).T for t in inp["shared"])
+    bias = None if inp["bias"] is None else f64(inp["bias"])
+    off = None if inp["offset"] is None else f64(inp["offset"])
+    X = f64(inp["X"])
+
+    def run(S):
+        cap = O.capacity(w.cf, S, w.k, w.E) if w.cf else None
+        t0 = time.perf_counter()
+        O.forward(X[:S], Wg, W1, W3, W2, k=w.k, score_func=w.score, renorm=w.renorm,
+                  bias=bias, offset=off, cap=cap, shared=sh, bf16_h=(w.dtype == "bf16"))
+        return time.perf_counter() - t0
+    # grow the sample (doubling) until one run takes >= target_s / 4, then
+    # repeat it so the timed CPU work is about target_s
+    S = min(w.T, 64)
+    t = run(S)
+    while t < target_s / 4 and S < w.T:
+        S = min(w.T, 2 * S)
+        t = run(S)
+    reps = max(1, int(round(target_s / max(t, 1e-3))))
+    reps = min(reps, 8)
+    tot = t + sum(run(S) for _ in range(reps - 1))
+    return {"value": S * reps / tot, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of the {w.name} batch x {reps} runs, full "
+                      f"resident expert weights, numpy float64 oracle (tier 1), {tot:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mixture_experts_layer_47_amd as moe
+    from mixture_experts_layer_47_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: T={w.T} d={w.d} E={w.E}+{w.n_shared} k={w.k} F={w.F} "
+        f"dtype={w.dtype} cf={w.cf}")
+    inp = make_inputs(w, dev)
+    layer = moe.layer_from_inputs(inp)
+    # one call with the optional outputs for the per-expert row counts
+    probe = moe.Forward(layer, inp["X"], aux=True)
+    probe()
+    torch.cuda.synchronize()
+    kept = probe.aux["offsets"].diff().cpu().numpy()
+    n_kept = int(probe.aux["n_kept"].item())
+    balance = float(probe.aux["balance"].item())
+    del probe
+    torch.cuda.empty_cache()
+    fwd = moe.Forward(layer, inp["X"], aux=False)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+
+    moe.timing_enable(args.steps * 12 + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    marks = moe.timing_read()
+    moe.timing_enable(0)
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / args.steps
+    value = w.T * args.steps / elapsed
+
+    phases = {}
+    for name, ms in marks:
+        if ms is not None:
+            phases.setdefault(name, []).append(ms)
+    phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
+    up_ms = phase_ms.get("ffn_up", float("nan"))
+    flops, bytes_, touched, rows = up_kernel_work(w, kept, n_kept)
+    peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_mfma = flops / (peak_flops * 1e12)
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = flops / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": ach / peak_flops}
+    else:
+        ach = bytes_ / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS}
+    roof["kernel"] = "k_grouped_gemm gate/up + SwiGLU (ffn_up)"
+    roof["kernel_ms"] = up_ms
+    roof["algorithmic"] = {"flops": flops, "bytes": bytes_, "rows": rows,
+                           "touched_experts": touched}
+    roof["traffic"] = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("gemm_src_sha256_16") == kernel_hash():
+            roof["traffic"] = tr.get("ffn_up_hbm_bytes")
+
+    # whole-layer roofline of the step for context
+    layer_flops = 2.0 * w.T * w.d * w.E + 6.0 * rows * w.d * w.F
+    es = 2 if w.dtype == "bf16" else 4
+    layer_bytes = touched * 3.0 * w.d * w.F * es + w.E * w.d * es + 2.0 * w.T * w.d * es
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) tokens, N(0,1/sqrt(fan_in)) "
+                                  "random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "n_shared": w.n_shared, "router": w.score, "capacity_factor": w.cf,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"flops": layer_flops, "bytes": layer_bytes,
+                  "mfma_frac": layer_flops / (ms_step * 1e-3) / (peak_flops * 1e12),
+                  "hbm_frac": layer_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+                  "kept_rows": n_kept, "balance_stat": balance, "phases_ms": phase_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_target_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -191,6 +191,21 @@ size_t moe_forward_workspace_size(const moe_layer* L, int64_t T);
 int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y,
                 const moe_aux* aux, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------- timing --
+ * Optional event timing of moe_forward's phases, for benchmarks.
+ * moe_timing_enable(n): n > 0 creates a pool of n HIP events (runtime
+ *   objects, no device buffers) and makes later moe_forward calls record one
+ *   event on their stream at each phase boundary: begin, route, dispatch,
+ *   tile_map, ffn_up (gate/up GEMM + SwiGLU), ffn_down, combine, aux.  Marks
+ *   beyond the pool are dropped.  n = 0 stops timing and frees the pool.
+ * moe_timing_read(names, name_len, ms, max): waits for the recorded events,
+ *   writes up to `max` marks (name into names + i*name_len, NUL-terminated;
+ *   ms[i] = milliseconds since the previous mark of the same call, -1 for a
+ *   call's first mark), clears them and returns how many were written, or a
+ *   negative moe_status. */
+int moe_timing_enable(int n);
+int moe_timing_read(char* names, int name_len, float* ms, int max);
+
 #ifdef __cplusplus
 }
 #endif

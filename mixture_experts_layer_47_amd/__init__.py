@@ -4,7 +4,9 @@ The compute path is the HIP library ``libmoe.so`` (C ABI: include/moe.h);
 this package is its Python binding plus the seeded synthetic workloads.
 """
 from ._lib import (MoeError, MoeLayer, Forward, balance, capacity, combine, dispatch,  # noqa: F401
-                   forward, grouped_ffn, last_error, layer_from_inputs, lib, route)
+                   forward, grouped_ffn, last_error, layer_from_inputs, lib, route,
+                   timing_enable, timing_read)
 
 __all__ = ["MoeError", "MoeLayer", "Forward", "balance", "capacity", "combine", "dispatch",
-           "forward", "grouped_ffn", "last_error", "layer_from_inputs", "lib", "route"]
+           "forward", "grouped_ffn", "last_error", "layer_from_inputs", "lib", "route",
+           "timing_enable", "timing_read"]

@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
 EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
-           "moe_balance", "moe_forward_workspace_size", "moe_forward")
+           "moe_balance", "moe_forward_workspace_size", "moe_forward", "moe_timing_enable",
+           "moe_timing_read")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +70,8 @@ def _declare(L):
         "moe_forward_workspace_size": (SZ, [ctypes.POINTER(MoeLayerC), I64]),
         "moe_forward": (I, [ctypes.POINTER(MoeLayerC), P, I64, P, ctypes.POINTER(MoeAuxC), P,
                             SZ, P]),
+        "moe_timing_enable": (I, [I]),
+        "moe_timing_read": (I, [ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_float), I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -279,6 +282,27 @@ class Forward:
                                  ctypes.byref(self.caux), _ptr(self.ws), self.ws.numel(),
                                  _stream(self.X.device)))
         return self.Y
+
+
+def timing_enable(n: int):
+    """Start (n > 0 events) or stop (n = 0) phase timing of moe_forward."""
+    _check(lib().moe_timing_enable(int(n)))
+
+
+def timing_read(max_marks: int = 4096):
+    """Return [(phase, ms_since_previous_mark or None)] and clear the marks."""
+    nl = 32
+    names = ctypes.create_string_buffer(nl * max_marks)
+    ms = (ctypes.c_float * max_marks)()
+    m = lib().moe_timing_read(names, nl, ms, max_marks)
+    if m < 0:
+        raise MoeError(m, "moe_timing_read failed")
+    raw = names.raw
+    out = []
+    for i in range(m):
+        nm = raw[i * nl:(i + 1) * nl].split(b"\0", 1)[0].decode()
+        out.append((nm, None if ms[i] < 0 else float(ms[i])))
+    return out
 
 
 def forward(layer: MoeLayer, X: torch.Tensor, aux: bool = False):

@@ -303,11 +303,14 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   const int ns = L->n_shared ? 1 : 0;
   const int64_t Tk = T * (int64_t)L->k;
 
+  timing_mark("begin", s, 1);
   hipError_t e = launch_route(X, L->dtype, T, L->d, L->Wg, L->E, L->bias, L->logit_offset,
                               L->score, L->k, L->renorm, a.logits, ids, gw, psum, w + o.route, s);
+  timing_mark("route", s);
   if (e == hipSuccess)
     e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,
                         nkept, rowtok, w + o.hist, s);
+  timing_mark("dispatch", s);
   if (e == hipSuccess)
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
@@ -315,9 +318,11 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   if (e == hipSuccess)
     e = launch_combine(yrows, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
                        L->dtype, s);
+  timing_mark("combine", s);
   if (e == hipSuccess && a.offsets)
     e = hipMemcpyAsync(a.offsets, offsets, (size_t)(L->E + 1) * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess && a.balance) e = launch_balance(counts, psum, T, L->k, L->E, a.balance, s);
+  timing_mark("aux", s);
   return hip_status(e, "moe_forward");
 }
 

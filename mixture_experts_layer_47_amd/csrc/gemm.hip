@@ -353,20 +353,25 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   int32_t* ntiles = (int32_t*)q;
   const int mr = (int)max_rows;
   hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, offsets, G, p.BM, mr, tiles, ntiles);
+  timing_mark("tile_map", s);
   if (dtype == MOE_BF16) {
     using T = uint16_t;
     run_up_bf16<T>(p.cfg, (const T*)A, row_token, offsets, tiles, ntiles, (const T*)W1, (const T*)W3,
               (const T*)W1l, (const T*)W3l, g_last, d, F, (int)MT, mr, (T*)H, s);
+    timing_mark("ffn_up", s);
     run_down_bf16<T>(p.cfg, (const T*)H, offsets, tiles, ntiles, (const T*)W2, (const T*)W2l,
                      g_last, d, F, (int)MT, mr, Yrows, s);
+    timing_mark("ffn_down", s);
   } else {
     using T = float;
     run_gemm<T, 64, 128, 2, 4, true>((const T*)A, row_token, offsets, tiles, ntiles, (const T*)W1,
                                      (const T*)W3, (const T*)W1l, (const T*)W3l, g_last, d, F,
                                      (int)MT, mr, H, s);
+    timing_mark("ffn_up", s);
     run_gemm<T, 64, 128, 2, 4, false>((const T*)H, nullptr, offsets, tiles, ntiles, (const T*)W2,
                                       nullptr, (const T*)W2l, nullptr, g_last, F, d, (int)MT,
                                       mr, Yrows, s);
+    timing_mark("ffn_down", s);
   }
   return hipGetLastError();
 }

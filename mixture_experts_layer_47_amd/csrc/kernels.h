@@ -41,4 +41,7 @@ hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const flo
                           int k, int d, const float* shared, const int32_t* shared_row0,
                           void* Y, int dtype, hipStream_t s);
 
+// timing.hip: records a phase-boundary event when timing is enabled.
+void timing_mark(const char* name, hipStream_t s, int first = 0);
+
 }  // namespace moe
