@@ -6,19 +6,30 @@
 // (14.2.2): h = silu(x W1) * (x W3), y = h W2.
 //
 // Kernel shape (one launch per projection):
-//   * a device-built tile list maps each M-tile to (expert g, first row);
-//     the grid is sized from host bounds only, surplus blocks exit at once;
-//   * block tile BM x BNT, BK = 128 bytes of K per stage (64 bf16 / 32 fp32),
-//     two LDS stages filled through registers while the other is consumed;
-//   * LDS rows are 8 chunks of 16 B, chunk index XOR (row & 7) so both the
-//     16-B stores and the MFMA fragment loads are bank-conflict free;
+//   * a device-built work list holds one entry per (expert, M-tile, N-tile);
+//     it is ordered expert by expert, and inside an expert in runs of NG
+//     neighbouring N-tiles with the M-tiles fastest, so the tiles that run
+//     at the same time on one XCD share both their weight slices and their
+//     activation rows in that XCD's L2;
+//   * one block per list entry, one block per CU at a time; blocks are
+//     mapped to entries so that in each round of (CUs) blocks every XCD
+//     works on a contiguous run of the list;
+//   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
+//     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
+//     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
+//   * BK = 128 bytes of K per stage (64 bf16 / 32 fp32), two LDS stages;
+//     a software pipeline over k16 substeps with four fragment register
+//     slots: each iteration runs the previous stage's last two substeps and
+//     the current stage's first two while it reads the current stage's
+//     fragments, fetches the next stage into registers and stores it to the
+//     other LDS buffer; scheduling groups pin that interleave;
+//   * LDS rows are 8 chunks of 16 B, chunk c of row r at slot c ^ (r & 7):
+//     the 16-B stores and the fragment reads are bank-conflict free;
 //   * bf16: v_mfma_f32_32x32x16_bf16, each lane feeds 8 K-contiguous values
 //     per operand; fp32: four v_mfma_f32_32x32x2f32 per 16-B fragment;
 //   * gate/up fusion: the B tile holds BN rows of W1 then BN rows of W3, a
 //     wave owns matching gate and up columns, and SwiGLU runs on the fp32
-//     accumulators before one rounding of h to the storage type;
-//   * XCD-aware order: consecutive logical tiles (same weight slice,
-//     neighbouring M-tiles) land on the same XCD and share its L2.
+//     accumulators before one rounding of h to the storage type.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,7 +43,8 @@ __device__ __forceinline__ void mma_32x32(f32x16& acc, const u32x4& a, const u32
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), acc,
+                                                 0, 0, 0);
   }
 }
 
@@ -45,215 +57,282 @@ __device__ __forceinline__ void store_h<uint16_t>(uint16_t* p, float v) { *p = f
 template <>
 __device__ __forceinline__ void store_h<float>(float* p, float v) { *p = v; }
 
-// Global -> registers for one K stage (k0 = first element of the stage).
-template <typename T, int CA, int CB, bool GLU, int BN, int NT>
+constexpr int kThreads = 256;   // four waves per block
+
+// One K stage, global -> registers.  Thread t owns the 16-B chunk t%8 of
+// rows t/8, t/8 + 32, ... of the A tile and of the B tile.
+template <typename T, int CA, int CB, bool GLU, int BN>
 __device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB], const T* A,
-                                           const uint32_t (&oa)[CA], uint32_t vmask,
-                                           const T* pb0, const T* pb1, size_t bstep, bool bact,
-                                           int k0) {
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
+                                           const uint32_t (&oa)[CA], const T* pb0,
+                                           const T* pb1, size_t bstep, int k0) {
 #pragma unroll
-  for (int i = 0; i < CA; ++i)
-    ra[i] = ((vmask >> i) & 1u) ? *(const u32x4*)(A + oa[i] + k0) : z4;
-  if (bact) {
+  for (int i = 0; i < CA; ++i) ra[i] = *(const u32x4*)(A + oa[i] + k0);
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      constexpr int kSplit = BN / (NT / 8);     // first thread-row index in the W3 half
-      const T* p = (GLU && i >= kSplit) ? pb1 + (size_t)(i - kSplit) * bstep
-                                        : pb0 + (size_t)i * bstep;
-      rb[i] = *(const u32x4*)(p + k0);
-    }
+  for (int i = 0; i < CB; ++i) {
+    constexpr int kSplit = BN / (kThreads / 8);   // first thread-row index in the W3 half
+    const T* p = (GLU && i >= kSplit) ? pb1 + (size_t)(i - kSplit) * bstep
+                                      : pb0 + (size_t)i * bstep;
+    rb[i] = *(const u32x4*)(p + k0);
   }
 }
 
 // Registers -> one LDS stage; chunk c of row r lands in slot c ^ (r & 7).
-template <int BM, int CA, int CB, int NT>
+template <int BM, int CA, int CB>
 __device__ __forceinline__ void lstore_tile(u32x4* sm, const u32x4 (&ra)[CA],
-                                            const u32x4 (&rb)[CB], int tid, int c16, bool ast,
-                                            bool bact) {
-  if (ast) {
+                                            const u32x4 (&rb)[CB], int tid) {
+  const int c16 = tid & 7;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int r = (tid >> 3) + i * (NT / 8);
-      sm[r * 8 + (c16 ^ (r & 7))] = ra[i];
-    }
+  for (int i = 0; i < CA; ++i) {
+    const int r = (tid >> 3) + i * (kThreads / 8);
+    sm[r * 8 + (c16 ^ (r & 7))] = ra[i];
   }
-  if (bact) {
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int r = BM + (tid >> 3) + i * (NT / 8);
-      sm[r * 8 + (c16 ^ (r & 7))] = rb[i];
-    }
+  for (int i = 0; i < CB; ++i) {
+    const int r = BM + (tid >> 3) + i * (kThreads / 8);
+    sm[r * 8 + (c16 ^ (r & 7))] = rb[i];
   }
+}
+
+// Fragments of one k16 substep.  LDS rows are 8 chunks of 16 B with chunk c
+// of row r stored at slot c ^ (r & 7); a lane's fragment rows all have
+// r & 7 == lane & 7, so one swizzled chunk index per substep (cs) serves
+// every fragment: A rows are pa + 32 i rows, B rows pb + the wave's columns.
+template <int FM, int FN, int BN, bool GLU>
+__device__ __forceinline__ void load_frags(u32x4* f, const u32x4* pa, const u32x4* pb, int cs) {
+  constexpr int FNH = GLU ? FN / 2 : FN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) f[i] = pa[i * 32 * 8 + cs];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int rr = GLU ? ((j < FNH) ? j * 32 : BN + (j - FNH) * 32) : j * 32;
+    f[FM + j] = pb[rr * 8 + cs];
+  }
+}
+
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void mma_substep(f32x16 (&acc)[FM][FN], const u32x4* f) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) mma_32x32<T>(acc[i][j], f[i], f[FM + j]);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
+              kSchedDsWrite = 0x200;
+
+// Scheduling groups for one MFMA substep: NM MFMAs with ND fragment reads,
+// then NG global loads, then NW LDS stores threaded between them one per
+// MFMA; what does not fit follows.
+template <int NM, int ND, int NG, int NW>
+__device__ __forceinline__ void sched_substep() {
+  constexpr int P1 = ND < NM ? ND : NM;
+  constexpr int R1 = NM - P1;
+  constexpr int P2 = NG < R1 ? NG : R1;
+  constexpr int R2 = R1 - P2;
+  constexpr int P3 = NW < R2 ? NW : R2;
+  constexpr int R3 = R2 - P3;
+#pragma unroll
+  for (int i = 0; i < P1; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  if constexpr (ND - P1 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, ND - P1, 0);
+#pragma unroll
+  for (int i = 0; i < P2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+  }
+  if constexpr (NG - P2 > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, NG - P2, 0);
+#pragma unroll
+  for (int i = 0; i < P3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+  }
+  if constexpr (NW - P3 > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, NW - P3, 0);
+  if constexpr (R3 > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, R3, 0);
 }
 
 // GLU = true : out = H [rows][N] (type T),  h = silu(A W1^T) * (A W3^T)
 // GLU = false: out = Y [rows][N] (fp32),    y = A W2^T
+// Work entry: {g | n_idx << 10, first row of the M-tile inside group g}.
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
-__global__ __launch_bounds__(WM * WN * 64) void k_grouped_gemm(
+__global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const T* __restrict__ A, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ offsets, const int2* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const T* __restrict__ B0, const T* __restrict__ B1,
+    const int32_t* __restrict__ offsets, const int2* __restrict__ work,
+    const int32_t* __restrict__ nwork, const T* __restrict__ B0, const T* __restrict__ B1,
     const T* __restrict__ B0_last, const T* __restrict__ B1_last, int g_last, int K, int N,
-    int MT, int max_rows, void* __restrict__ out) {
-  constexpr int NT = WM * WN * 64;
+    int max_rows, int round, void* __restrict__ out) {
+  constexpr int NT = kThreads;
   constexpr int BNT = GLU ? 2 * BN : BN;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-B chunk
   constexpr int BK = 8 * EPC;                  // elements per stage (128 B)
-  // 16-B chunks per thread per stage; when a tile has fewer chunks than the
-  // block has threads, only the first BM*8 (BNT*8) threads load.
-  constexpr int CA = BM * 8 >= NT ? BM * 8 / NT : 1;
-  constexpr int CB = BNT * 8 >= NT ? BNT * 8 / NT : 1;
-  constexpr bool PA = BM * 8 < NT, PB = BNT * 8 < NT;
+  constexpr int CA = BM * 8 / NT, CB = BNT * 8 / NT;   // 16-B chunks per thread per stage
   constexpr int WROWS = BM / WM, WCOLS = BNT / WN;
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
   constexpr int FNH = GLU ? FN / 2 : FN;
-  static_assert((BM * 8) % NT == 0 || NT % (BM * 8) == 0, "A tile vs threads");
-  static_assert((BNT * 8) % NT == 0 || NT % (BNT * 8) == 0, "B tile vs threads");
+  constexpr int NF = FM + FN;                          // fragments per substep
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(BM % 32 == 0 && BNT % 32 == 0 && BN % 32 == 0, "32-row load blocks");
+
   static_assert(FM >= 1 && FN >= 1 && (!GLU || FN % 2 == 0), "wave tile");
-  static_assert(!GLU || (!PB && BN % (NT / 8) == 0), "gate/up halves split on thread rows");
+  static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BNT * 8) % NT == 0, "tile loads");
+  static_assert(!GLU || BN % (NT / 8) == 0, "gate/up halves split on thread rows");
   __shared__ u32x4 smem[2][(BM + BNT) * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int n_idx = L / MT, m_idx = L - n_idx * MT;
-  if (m_idx >= ntiles[0]) return;
-  const int2 tl = tiles[m_idx];
-  const int g = tl.x;
-  const int gbeg = min(max(offsets[g], 0), max_rows);
-  const int rbeg = gbeg + tl.y;
-  const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
-  const int n0 = n_idx * BN;
-
-  const T* w0 = (g == g_last) ? B0_last : B0 + (size_t)g * N * K;
-  const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) : nullptr;
-
-  // ---- per-thread global source rows (fixed for the whole K loop), kept as
-  // 32-bit element offsets (every operand here holds < 2^31 elements)
-  const int c16 = tid & 7;                     // 16-B chunk inside the 128-B row
-  uint32_t oa[CA];
-  uint32_t vmask = 0;
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int r = (tid >> 3) + i * (NT / 8);
-    const bool v = r < rows && (!PA || tid < BM * 8);
-    int src = rbeg + (v ? r : 0);
-    if (row_token) src = row_token[src];
-    oa[i] = (uint32_t)src * (uint32_t)K + c16 * EPC;
-    vmask |= (v ? 1u : 0u) << i;
-  }
-  // B rows: thread row r0 = tid/8 + i*NT/8; GLU tiles take W1 rows then W3 rows.
-  const bool bact = !PB || tid < BNT * 8;
-  const T* pb0;
-  const T* pb1 = nullptr;                      // W3 half (GLU only)
-  {
-    const int r0 = bact ? (tid >> 3) : 0;
-    pb0 = w0 + (size_t)(n0 + r0) * K + c16 * EPC;
-    if constexpr (GLU) pb1 = w1 + (size_t)(n0 + r0) * K + c16 * EPC;
-  }
-  const size_t bstep = (size_t)(NT / 8) * K;   // element distance between a thread's B rows
-
-  u32x4 ra[CA], rb[CB];
   const int wm = wave / WN, wn = wave % WN;
-  const int arow0 = wm * WROWS;                // wave's first A row in the tile
-  f32x16 acc[FM][FN];
+  const int arow0 = wm * WROWS;
+  const int c16 = tid & 7;
+  // this lane's fragment row bases (in 16-B chunks) and swizzled chunk per substep
+  const int fa = (arow0 + (lane & 31)) * 8;
+  const int fb = (BM + (GLU ? wn * (BN / WN) : wn * WCOLS) + (lane & 31)) * 8;
+  int cs[4];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // LDS row of the wave's j-th B fragment (lane's column = lane & 31).
-#define MOE_BROW(j)                                                                 \
-  (GLU ? BM + (((j) < FNH) ? wn * (BN / WN) + (j) * 32                             \
-                           : BN + wn * (BN / WN) + ((j) - FNH) * 32) + (lane & 31) \
-       : BM + wn * WCOLS + (j) * 32 + (lane & 31))
-
+  for (int q = 0; q < 4; ++q) cs[q] = (2 * q + (lane >> 5)) ^ (lane & 7);
+  // Blocks are dispatched round-robin over the 8 XCDs and run one per CU:
+  // the i-th block of XCD x takes list entry (i / cx) * round + x * cx + i % cx
+  // (cx = CUs per XCD, round = 8 cx), so in every round each XCD works on cx
+  // consecutive entries of the list.
+  const int cx = round >> 3;
+  const int xi = blockIdx.x >> 3;
+  const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
+  if (t >= nwork[0]) return;
   const int nk = K / BK;
-  const bool ast = !PA || tid < BM * 8;
-  gload_tile<T, CA, CB, GLU, BN, NT>(ra, rb, A, oa, vmask, pb0, pb1, bstep, bact, 0);
-  lstore_tile<BM, CA, CB, NT>(smem[0], ra, rb, tid, c16, ast, bact);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk)
-      gload_tile<T, CA, CB, GLU, BN, NT>(ra, rb, A, oa, vmask, pb0, pb1, bstep, bact, (kt + 1) * BK);
+  const size_t bstep = (size_t)(NT / 8) * K;   // element distance between a thread's B rows
+  {
+    const int2 wi = work[t];
+    const int g = wi.x & 1023;
+    const int n0 = (wi.x >> 10) * BN;
+    const int gbeg = min(max(offsets[g], 0), max_rows);
+    const int rbeg = gbeg + wi.y;
+    const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
+    const T* w0 = (g == g_last) ? B0_last : B0 + (size_t)g * N * K;
+    const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) : nullptr;
+
+    // per-thread source rows as 32-bit element offsets (operands hold < 2^31
+    // elements).  Rows past the tile's end re-read its first row: their
+    // outputs are never stored, and each output row depends only on its own
+    // A row.
+    uint32_t oa[CA];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kc = 2 * s + (lane >> 5);
-      u32x4 af[FM], bfr[FN];
+    for (int i = 0; i < CA; ++i) {
+      const int r = (tid >> 3) + i * (NT / 8);
+      int src = rbeg + (r < rows ? r : 0);
+      if (row_token) src = row_token[src];
+      oa[i] = (uint32_t)src * (uint32_t)K + c16 * EPC;
+    }
+    const T* pb0 = w0 + (size_t)(n0 + (tid >> 3)) * K + c16 * EPC;
+    const T* pb1 = GLU ? w1 + (size_t)(n0 + (tid >> 3)) * K + c16 * EPC : nullptr;
+
+    f32x16 acc[FM][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = arow0 + i * 32 + (lane & 31);
-        af[i] = smem[buf][r * 8 + (kc ^ (r & 7))];
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    u32x4 ra[CA], rb[CB];
+    gload_tile<T, CA, CB, GLU, BN>(ra, rb, A, oa, pb0, pb1, bstep, 0);
+    lstore_tile<BM, CA, CB>(smem[0], ra, rb, tid);
+    __syncthreads();
+
+    // Software pipeline over k16 substeps q = 4 kt + s with four fragment
+    // slots (slot = s).  Iteration kt runs the MFMAs of stage kt-1's
+    // substeps 2, 3 and stage kt's substeps 0, 1 while it reads stage kt's
+    // four fragment sets, fetches stage kt+1 into registers and stores it to
+    // the other LDS buffer; the barrier then publishes that buffer.  Slots 2
+    // and 3 start as zeros, so the first iteration's leading MFMAs add 0.
+    u32x4 f[4][NF];
+#pragma unroll
+    for (int q = 2; q < 4; ++q)
+#pragma unroll
+      for (int x = 0; x < NF; ++x) f[q][x] = u32x4{0u, 0u, 0u, 0u};
+    for (int kt = 0; kt < nk; ++kt) {
+      const u32x4* sm = smem[kt & 1];
+      // the last stage re-fetches itself (in bounds; stored to the idle buffer)
+      const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
+      gload_tile<T, CA, CB, GLU, BN>(ra, rb, A, oa, pb0, pb1, bstep, kn);
+      load_frags<FM, FN, BN, GLU>(f[0], sm + fa, sm + fb, cs[0]);
+      mma_substep<T, FM, FN>(acc, f[2]);
+      load_frags<FM, FN, BN, GLU>(f[1], sm + fa, sm + fb, cs[1]);
+      mma_substep<T, FM, FN>(acc, f[3]);
+      load_frags<FM, FN, BN, GLU>(f[2], sm + fa, sm + fb, cs[2]);
+      mma_substep<T, FM, FN>(acc, f[0]);
+      load_frags<FM, FN, BN, GLU>(f[3], sm + fa, sm + fb, cs[3]);
+      lstore_tile<BM, CA, CB>(smem[(kt + 1) & 1], ra, rb, tid);
+      mma_substep<T, FM, FN>(acc, f[1]);
+      if constexpr (sizeof(T) == 2) {
+        constexpr int NM = FM * FN;
+        constexpr int NL = CA + CB;
+        sched_substep<NM, NF, NL / 2, 0>();
+        sched_substep<NM, NF, NL - NL / 2, 0>();
+        sched_substep<NM, NF, 0, 0>();
+        sched_substep<NM, NF, 0, NL>();
       }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = MOE_BROW(j);
-        bfr[j] = smem[buf][r * 8 + (kc ^ (r & 7))];
-      }
+      __syncthreads();
+    }
+    mma_substep<T, FM, FN>(acc, f[2]);
+    mma_substep<T, FM, FN>(acc, f[3]);
+
+    // ---- epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
+    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.  Row offsets are compile-
+    // time constants compared with the tile's remaining rows, and addresses
+    // are formed from the tile's first row, so nothing here is hoisted out
+    // of the tile loop.
+    const int lrow0 = arow0 + (lane >> 5) * 4;          // this lane's first row
+    const int rem = rows - lrow0;                        // rows this lane may store
+    const size_t row0 = (size_t)(rbeg + lrow0);
+    if constexpr (GLU) {
+      T* H = (T*)out + row0 * N + n0 + wn * (BN / WN) + (lane & 31);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma_32x32<T>(acc[i][j], af[i], bfr[j]);
-    }
-    if (kt + 1 < nk) lstore_tile<BM, CA, CB, NT>(smem[buf ^ 1], ra, rb, tid, c16, ast, bact);
-    __syncthreads();
-  }
-
-#undef MOE_BROW
-  // ---- epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
-  // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
-  const int col_l = lane & 31;
-  const int rsub = (lane >> 5) * 4;
-  if constexpr (GLU) {
-    T* H = (T*)out;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FNH; ++j) {
-        const int col = n0 + wn * (BN / WN) + j * 32 + col_l;
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = arow0 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (row < rows) {
-            const float h = silu_f(acc[i][j][r]) * acc[i][j + FNH][r];
-            store_h<T>(H + (size_t)(rbeg + row) * N + col, h);
+          const int off = i * 32 + (r >> 2) * 8 + (r & 3);
+          if (off < rem) {
+#pragma unroll
+            for (int j = 0; j < FNH; ++j) {
+              const float h = silu_f(acc[i][j][r]) * acc[i][j + FNH][r];
+              store_h<T>(H + (size_t)off * N + j * 32, h);
+            }
           }
         }
-      }
-  } else {
-    float* Y = (float*)out;
+    } else {
+      float* Y = (float*)out + row0 * N + n0 + wn * WCOLS + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WCOLS + j * 32 + col_l;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = arow0 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (row < rows) Y[(size_t)(rbeg + row) * N + col] = acc[i][j][r];
+          const int off = i * 32 + (r >> 2) * 8 + (r & 3);
+          if (off < rem) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) Y[(size_t)off * N + j * 32] = acc[i][j][r];
+          }
         }
-      }
+    }
   }
 }
 
-// Tile list: for group g, ceil(rows_g / BM) tiles (g, i*BM).  One block.
-// Group row ranges are clamped to [0, max_rows), so malformed offsets can
-// never address rows outside the caller's buffers.
-__global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ offsets, int G,
-                                                   int BM, int max_rows, int2* __restrict__ tiles,
-                                                   int32_t* __restrict__ ntiles) {
+// Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
+// ceil(rows_g / BM) M-tiles times NN N-tiles, ordered by group, then by runs
+// of NG neighbouring N-tiles, then M-tile, then N-tile inside the run.
+__global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ offsets, int G,
+                                                    int BM, int max_rows, int NN, int NG,
+                                                    int2* __restrict__ work,
+                                                    int32_t* __restrict__ nwork) {
   __shared__ int32_t sc[1024];
+  __shared__ int32_t mts[1024];
   const int g = threadIdx.x;
-  int nt = 0;
+  int mt = 0;
   if (g < G) {
     const int a = min(max(offsets[g], 0), max_rows);
     const int b = min(max(offsets[g + 1], a), max_rows);
-    nt = MOE_CEIL_DIV(b - a, BM);
+    mt = MOE_CEIL_DIV(b - a, BM);
   }
-  sc[g] = nt;
+  mts[g] = mt;
+  sc[g] = mt * NN;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {       // inclusive Hillis-Steele scan
     const int v = (g >= o) ? sc[g - o] : 0;
@@ -261,9 +340,31 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
     sc[g] += v;
     __syncthreads();
   }
-  const int start = sc[g] - nt;        // total <= ceil(max_rows / BM) + G
-  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int2(g, i * BM);
-  if (g == 1023) ntiles[0] = sc[1023];
+  const int total = sc[1023];
+  const int nfull = NN / NG;
+  for (int e = g; e < total; e += 1024) {
+    int lo = 0, hi = G - 1;                     // first group with inclusive sum > e
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sc[mid] > e) hi = mid; else lo = mid + 1;
+    }
+    const int gg = lo;
+    const int m = mts[gg];
+    const int j = e - (sc[gg] - m * NN);
+    int mi, ni;
+    if (j < m * NG * nfull) {
+      const int run = j / (m * NG), r = j - run * m * NG;
+      mi = r / NG;
+      ni = run * NG + (r - mi * NG);
+    } else {
+      const int last = NN - nfull * NG;         // size of the final, shorter run
+      const int r = j - m * NG * nfull;
+      mi = r / last;
+      ni = nfull * NG + (r - mi * last);
+    }
+    work[e] = make_int2(gg | (ni << 10), mi * BM);
+  }
+  if (g == 0) nwork[0] = total;
 }
 
 // ------------------------------------------------------------------ launch
@@ -280,60 +381,66 @@ static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
   return {32, 2};
 }
 
-int64_t gemm_max_mtiles(int64_t max_rows, int G, int BM) {
-  return MOE_CEIL_DIV(max_rows, BM) + G;
+// Upper bound of work entries for one projection with N-tile width BN.
+static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN) {
+  return (MOE_CEIL_DIV(max_rows, BM) + G) * (int64_t)(N / BN);
 }
+
+static int up_bn(int cfg) { return cfg == 2 ? 256 : 128; }
+static int down_bn(int cfg, int d) { return (cfg == 3 || d % 256 != 0) ? 128 : 256; }
 
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
-  size_t b = align256((size_t)max_rows * F * es);                         // H
-  b += align256((size_t)gemm_max_mtiles(max_rows, G, p.BM) * sizeof(int2));  // tiles
-  b += align256(sizeof(int32_t));                                        // tile count
+  const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
+  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d));
+  size_t b = align256((size_t)max_rows * F * es);                       // H
+  b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
+  b += align256(2 * sizeof(int32_t));                                  // entry counts
   return b;
 }
 
+static int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+struct GemmArgs {
+  const void* A;
+  const int32_t* row_token;
+  const int32_t* offsets;
+  int G;
+  const void *B0, *B1, *B0l, *B1l;
+  int g_last, K, N, max_rows;
+  void* out;
+  int2* work;
+  int32_t* nwork;
+};
+
+static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s) {
+  const int NN = a.N / BN;
+  const int NG = glu ? 8 : 4;
+  hipLaunchKernelGGL(k_work_list, dim3(1), dim3(1024), 0, s, a.offsets, a.G, BM, a.max_rows, NN,
+                     NG < NN ? NG : NN, a.work, a.nwork);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
-static void run_gemm(const T* A, const int32_t* row_token, const int32_t* offsets,
-                     const int2* tiles, const int32_t* ntiles, const T* B0, const T* B1,
-                     const T* B0l, const T* B1l, int g_last, int K, int N, int MT, int max_rows,
-                     void* out, hipStream_t s) {
-  const int nn = N / BN;
-  const unsigned grid = (unsigned)((int64_t)nn * MT);
-  hipLaunchKernelGGL((k_grouped_gemm<T, BM, BN, WM, WN, GLU>), dim3(grid), dim3(WM * WN * 64), 0,
-                     s, A, row_token, offsets, tiles, ntiles, B0, B1, B0l, B1l, g_last, K, N, MT,
-                     max_rows, out);
-}
-
-template <typename T>
-static void run_up_bf16(int cfg, const T* A, const int32_t* rt, const int32_t* off, const int2* tl,
-                   const int32_t* nt, const T* W1, const T* W3, const T* W1l, const T* W3l,
-                   int gl, int d, int F, int MT, int mr, T* H, hipStream_t s) {
-  switch (cfg) {
-    case 0: run_gemm<T, 256, 128, 4, 2, true>(A, rt, off, tl, nt, W1, W3, W1l, W3l, gl, d, F, MT, mr, H, s); break;
-    case 1: run_gemm<T, 128, 128, 2, 4, true>(A, rt, off, tl, nt, W1, W3, W1l, W3l, gl, d, F, MT, mr, H, s); break;
-    default: run_gemm<T, 32, 256, 1, 8, true>(A, rt, off, tl, nt, W1, W3, W1l, W3l, gl, d, F, MT, mr, H, s); break;
-  }
-}
-
-template <typename T>
-static void run_down_bf16(int cfg, const T* H, const int32_t* off, const int2* tl, const int32_t* nt,
-                     const T* W2, const T* W2l, int gl, int d, int F, int MT, int mr,
-                     float* Y, hipStream_t s) {
-  const bool b256 = d % 256 == 0;
-  switch (cfg) {
-    case 0:
-      if (b256) run_gemm<T, 256, 256, 4, 2, false>(H, nullptr, off, tl, nt, W2, nullptr, W2l, nullptr, gl, F, d, MT, mr, Y, s);
-      else      run_gemm<T, 256, 128, 4, 2, false>(H, nullptr, off, tl, nt, W2, nullptr, W2l, nullptr, gl, F, d, MT, mr, Y, s);
-      break;
-    case 1:
-      if (b256) run_gemm<T, 128, 256, 2, 4, false>(H, nullptr, off, tl, nt, W2, nullptr, W2l, nullptr, gl, F, d, MT, mr, Y, s);
-      else      run_gemm<T, 128, 128, 2, 4, false>(H, nullptr, off, tl, nt, W2, nullptr, W2l, nullptr, gl, F, d, MT, mr, Y, s);
-      break;
-    default:
-      run_gemm<T, 32, 256, 1, 8, false>(H, nullptr, off, tl, nt, W2, nullptr, W2l, nullptr, gl, F, d, MT, mr, Y, s);
-      break;
-  }
+static void run_gemm(const GemmArgs& a, hipStream_t s) {
+  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN);
+  const int round = num_cus() & ~7;           // blocks per dispatch round, whole XCDs
+  const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
+  hipLaunchKernelGGL((k_moe_gemm<T, BM, BN, WM, WN, GLU>), dim3((unsigned)nb), dim3(kThreads), 0,
+                     s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork, (const T*)a.B0,
+                     (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last, a.K, a.N,
+                     a.max_rows, round, a.out);
 }
 
 // Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
@@ -346,31 +453,45 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
   const int es = dtype == MOE_BF16 ? 2 : 4;
+  const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
+  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d));
   char* q = (char*)ws;
-  void* H = q;             q += align256((size_t)max_rows * F * es);
-  const int64_t MT = gemm_max_mtiles(max_rows, G, p.BM);
-  int2* tiles = (int2*)q;  q += align256((size_t)MT * sizeof(int2));
-  int32_t* ntiles = (int32_t*)q;
+  void* H = q;               q += align256((size_t)max_rows * F * es);
+  int2* work_up = (int2*)q;  q += align256((size_t)wu * sizeof(int2));
+  int2* work_dn = (int2*)q;  q += align256((size_t)wd * sizeof(int2));
+  int32_t* nwork = (int32_t*)q;
   const int mr = (int)max_rows;
-  hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, offsets, G, p.BM, mr, tiles, ntiles);
+  GemmArgs up{A, row_token, offsets, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork};
+  GemmArgs dn{H, nullptr, offsets, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
+              nwork + 1};
+  run_work_list(up, p.BM, up_bn(p.cfg), true, s);
+  run_work_list(dn, p.BM, down_bn(p.cfg, d), false, s);
   timing_mark("tile_map", s);
   if (dtype == MOE_BF16) {
     using T = uint16_t;
-    run_up_bf16<T>(p.cfg, (const T*)A, row_token, offsets, tiles, ntiles, (const T*)W1, (const T*)W3,
-              (const T*)W1l, (const T*)W3l, g_last, d, F, (int)MT, mr, (T*)H, s);
+    switch (p.cfg) {
+      case 0: run_gemm<T, 256, 128, 2, 2, true>(up, s); break;
+      case 1: run_gemm<T, 128, 128, 2, 2, true>(up, s); break;
+      default: run_gemm<T, 32, 256, 1, 4, true>(up, s); break;
+    }
     timing_mark("ffn_up", s);
-    run_down_bf16<T>(p.cfg, (const T*)H, offsets, tiles, ntiles, (const T*)W2, (const T*)W2l,
-                     g_last, d, F, (int)MT, mr, Yrows, s);
+    const bool b256 = down_bn(p.cfg, d) == 256;
+    switch (p.cfg) {
+      case 0:
+        if (b256) run_gemm<T, 256, 256, 2, 2, false>(dn, s);
+        else run_gemm<T, 256, 128, 2, 2, false>(dn, s);
+        break;
+      case 1:
+        if (b256) run_gemm<T, 128, 256, 2, 2, false>(dn, s);
+        else run_gemm<T, 128, 128, 2, 2, false>(dn, s);
+        break;
+      default: run_gemm<T, 32, 256, 1, 4, false>(dn, s); break;
+    }
     timing_mark("ffn_down", s);
   } else {
-    using T = float;
-    run_gemm<T, 64, 128, 2, 4, true>((const T*)A, row_token, offsets, tiles, ntiles, (const T*)W1,
-                                     (const T*)W3, (const T*)W1l, (const T*)W3l, g_last, d, F,
-                                     (int)MT, mr, H, s);
+    run_gemm<float, 64, 128, 2, 2, true>(up, s);
     timing_mark("ffn_up", s);
-    run_gemm<T, 64, 128, 2, 4, false>((const T*)H, nullptr, offsets, tiles, ntiles, (const T*)W2,
-                                      nullptr, (const T*)W2l, nullptr, g_last, F, d, (int)MT,
-                                      mr, Yrows, s);
+    run_gemm<float, 64, 128, 2, 2, false>(dn, s);
     timing_mark("ffn_down", s);
   }
   return hipGetLastError();
