@@ -186,7 +186,7 @@ int moe_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offs
   if ((rc = check_ws(ws, ws_bytes, ffn_ws_bytes(max_rows, G, d, F, dtype)))) return rc;
   return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
                                        nullptr, -1, dtype, d, F, max_rows, Yrows, ws,
-                                       (hipStream_t)stream),
+                                       (hipStream_t)stream, true, nullptr),
                     "moe_grouped_ffn");
 }
 
@@ -200,8 +200,8 @@ int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w
   MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a positive multiple of 128", d);
   MOE_REQUIRE(T == 0 || (Yrows && slot_row && topk_w && Y), MOE_EINVAL,
               "NULL Yrows, slot_row, topk_w or Y");
-  return hip_status(launch_combine(Yrows, slot_row, topk_w, T, k, d, shared, nullptr, Y, dtype,
-                                   (hipStream_t)stream),
+  return hip_status(launch_combine(Yrows, nullptr, slot_row, topk_w, T, k, d, shared, nullptr, Y,
+                                   dtype, (hipStream_t)stream),
                     "moe_combine");
 }
 
@@ -311,12 +311,16 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
     e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,
                         nkept, rowtok, w + o.hist, s);
   timing_mark("dispatch", s);
+  // With a K-split down projection the combine adds the two partial slabs
+  // itself, unless the caller asked for the expert rows (then they are
+  // summed into Yrows first).
+  const float* part2 = nullptr;
   if (e == hipSuccess)
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
-                           w + o.ffn, s);
+                           w + o.ffn, s, a.Yrows != nullptr, &part2);
   if (e == hipSuccess)
-    e = launch_combine(yrows, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
+    e = launch_combine(yrows, part2, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
                        L->dtype, s);
   timing_mark("combine", s);
   if (e == hipSuccess && a.offsets)

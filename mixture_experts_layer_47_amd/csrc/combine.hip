@@ -11,6 +11,7 @@ namespace moe {
 
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows,
+                                                 const float* __restrict__ Yrows2,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ w, int k, int d,
                                                  const float* __restrict__ shared,
@@ -25,19 +26,32 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
   }
   __syncthreads();
   const float* sh = nullptr;
-  if (shared) sh = shared + (size_t)t * d;
-  else if (shared_row0) sh = Yrows + ((size_t)shared_row0[0] + t) * d;
+  const float* sh2 = nullptr;
+  if (shared) {
+    sh = shared + (size_t)t * d;
+  } else if (shared_row0) {
+    sh = Yrows + ((size_t)shared_row0[0] + t) * d;
+    if (Yrows2) sh2 = Yrows2 + ((size_t)shared_row0[0] + t) * d;
+  }
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int r = rows[j];
       if (r < 0) continue;
-      const float4 y = *(const float4*)(Yrows + (size_t)r * d + c);
+      float4 y = *(const float4*)(Yrows + (size_t)r * d + c);
+      if (Yrows2) {   // K-split partials are summed first, in split order
+        const float4 y2 = *(const float4*)(Yrows2 + (size_t)r * d + c);
+        y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
+      }
       const float g = gw[j];
       acc.x += g * y.x; acc.y += g * y.y; acc.z += g * y.z; acc.w += g * y.w;
     }
     if (sh) {
-      const float4 y = *(const float4*)(sh + c);
+      float4 y = *(const float4*)(sh + c);
+      if (sh2) {
+        const float4 y2 = *(const float4*)(sh2 + c);
+        y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
+      }
       acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
     }
     if constexpr (sizeof(OutT) == 2) {
@@ -51,16 +65,16 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
   }
 }
 
-hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
-                          int k, int d, const float* shared, const int32_t* shared_row0,
-                          void* Y, int dtype, hipStream_t s) {
+hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t* slot_row,
+                          const float* w, int64_t T, int k, int d, const float* shared,
+                          const int32_t* shared_row0, void* Y, int dtype, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)T), dim3(256), 0, s, Yrows, slot_row,
-                       w, k, d, shared, shared_row0, (uint16_t*)Y);
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)T), dim3(256), 0, s, Yrows, Yrows2,
+                       slot_row, w, k, d, shared, shared_row0, (uint16_t*)Y);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)T), dim3(256), 0, s, Yrows, slot_row, w,
-                       k, d, shared, shared_row0, (float*)Y);
+    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)T), dim3(256), 0, s, Yrows, Yrows2,
+                       slot_row, w, k, d, shared, shared_row0, (float*)Y);
   return hipGetLastError();
 }
 

@@ -17,19 +17,24 @@
 //   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
 //     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
 //     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
-//   * BK = 128 bytes of K per stage (64 bf16 / 32 fp32), two LDS stages;
-//     a software pipeline over k16 substeps with four fragment register
-//     slots: each iteration runs the previous stage's last two substeps and
-//     the current stage's first two while it reads the current stage's
-//     fragments, fetches the next stage into registers and stores it to the
-//     other LDS buffer; scheduling groups pin that interleave;
-//   * LDS rows are 8 chunks of 16 B, chunk c of row r at slot c ^ (r & 7):
-//     the 16-B stores and the fragment reads are bank-conflict free;
+//   * BK = 128 bytes of K per stage (64 bf16 / 32 fp32), two LDS stages
+//     and two register staging sets: a software pipeline over k16 substeps
+//     reads each substep's fragments while the previous substep's MFMAs
+//     run, and fetches stage k+2 from global memory while stage k+1 is
+//     stored to LDS, so loads have ~1.6 stages to arrive; scheduling groups
+//     pin the interleave;
+//   * LDS rows are 8 chunks of 16 B, chunk c of row r at slot
+//     c ^ ((r ^ (r/8 mod 4)) mod 8): the 16-B stores and the fragment reads
+//     are bank-conflict free whether the LDS serves 8 or 16 lanes per cycle;
+//   * a wave skips the MFMAs of its 32-row blocks that lie past the tile's
+//     last row (a ragged last M-tile of an expert computes only live rows);
 //   * bf16: v_mfma_f32_32x32x16_bf16, each lane feeds 8 K-contiguous values
 //     per operand; fp32: four v_mfma_f32_32x32x2f32 per 16-B fragment;
 //   * gate/up fusion: the B tile holds BN rows of W1 then BN rows of W3, a
 //     wave owns matching gate and up columns, and SwiGLU runs on the fp32
 //     accumulators before one rounding of h to the storage type.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -76,32 +81,35 @@ __device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB], con
   }
 }
 
-// Registers -> one LDS stage; chunk c of row r lands in slot c ^ (r & 7).
+// LDS swizzle: chunk c of row r is stored at slot c ^ swz(r).  swz depends on
+// r mod 32 only, and is a bijection on any 8 rows starting at a multiple of
+// 8 and on the even and on the odd rows of any 16 rows starting at a
+// multiple of 16, so 16-B accesses by 8 lanes on 8 rows or by 16 lanes on 16
+// rows (one chunk column), and by 8 or 16 lanes covering whole rows, all hit
+// distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
+// Registers -> one LDS stage.  Rows r and r + 32 i share swz(r).
 template <int BM, int CA, int CB>
 __device__ __forceinline__ void lstore_tile(u32x4* sm, const u32x4 (&ra)[CA],
                                             const u32x4 (&rb)[CB], int tid) {
-  const int c16 = tid & 7;
+  const int r0 = tid >> 3;
+  const int c = (tid & 7) ^ swz(r0);
 #pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int r = (tid >> 3) + i * (kThreads / 8);
-    sm[r * 8 + (c16 ^ (r & 7))] = ra[i];
-  }
+  for (int i = 0; i < CA; ++i) sm[(r0 + i * (kThreads / 8)) * 8 + c] = ra[i];
 #pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int r = BM + (tid >> 3) + i * (kThreads / 8);
-    sm[r * 8 + (c16 ^ (r & 7))] = rb[i];
-  }
+  for (int i = 0; i < CB; ++i) sm[(BM + r0 + i * (kThreads / 8)) * 8 + c] = rb[i];
 }
 
-// Fragments of one k16 substep.  LDS rows are 8 chunks of 16 B with chunk c
-// of row r stored at slot c ^ (r & 7); a lane's fragment rows all have
-// r & 7 == lane & 7, so one swizzled chunk index per substep (cs) serves
-// every fragment: A rows are pa + 32 i rows, B rows pb + the wave's columns.
-template <int FM, int FN, int BN, bool GLU>
+// Fragments of one k16 substep.  A lane's fragment rows are all congruent
+// to lane % 32 modulo 32, so they share swz(row) and one swizzled chunk index
+// per substep (cs) serves every fragment: A rows are pa + 32 i rows, B rows
+// pb + the wave's column rows.
+template <int NA, int FM, int FN, int BN, bool GLU>
 __device__ __forceinline__ void load_frags(u32x4* f, const u32x4* pa, const u32x4* pb, int cs) {
   constexpr int FNH = GLU ? FN / 2 : FN;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f[i] = pa[i * 32 * 8 + cs];
+  for (int i = 0; i < NA; ++i) f[i] = pa[i * 32 * 8 + cs];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int rr = GLU ? ((j < FNH) ? j * 32 : BN + (j - FNH) * 32) : j * 32;
@@ -109,10 +117,11 @@ __device__ __forceinline__ void load_frags(u32x4* f, const u32x4* pa, const u32x
   }
 }
 
-template <typename T, int FM, int FN>
+// MFMAs of one substep for the first NV 32-row blocks of the wave's tile.
+template <typename T, int NV, int FM, int FN>
 __device__ __forceinline__ void mma_substep(f32x16 (&acc)[FM][FN], const u32x4* f) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) mma_32x32<T>(acc[i][j], f[i], f[FM + j]);
 }
@@ -153,6 +162,81 @@ __device__ __forceinline__ void sched_substep() {
   if constexpr (R3 > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, R3, 0);
 }
 
+// Main K loop of one tile for a wave whose first NV (of FM) 32-row blocks
+// hold real rows; blocks past the tile's last row skip their MFMAs and
+// fragment reads (NV = 0: the wave only loads and stores its share of the
+// stages).  Every wave runs the same loads, stores and barriers.
+//
+// Software pipeline over k16 substeps with two fragment slots and two
+// register staging sets.  Iteration kt (stage kt in LDS buffer kt&1):
+//   issue global loads of stage kt+2 into staging set (kt+1)&1
+//   MFMA stage kt-1 substep 3 (slot 1)  | read stage kt substep 0 (slot 0)
+//   MFMA substep 0 (slot 0)             | read substep 1 (slot 1)
+//   MFMA substep 1 (slot 1)             | read substep 2 (slot 0),
+//                                          store staging set kt&1 (stage
+//                                          kt+1) to LDS buffer (kt+1)&1
+//   MFMA substep 2 (slot 0)             | read substep 3 (slot 1)
+//   barrier
+// so every global load has about 1.6 stages to arrive.  Loads past the last
+// stage re-fetch the last stage (in bounds, never used).  Slot 1 starts as
+// zeros: the first iteration's leading MFMAs add 0.  nk is even (K is a
+// multiple of 128 elements), so the loop advances two stages at a time and
+// the staging sets keep fixed names.
+template <typename T, int NV, int BM, int BN, int CA, int CB, int FM, int FN, bool GLU>
+__device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1], const T* Ak,
+                                          const uint32_t (&oa)[CA], const T* pb0, const T* pb1,
+                                          size_t bstep, int nk, int fa, int fb,
+                                          const int (&cs)[4], int tid) {
+  constexpr int NF = FM + FN;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int BK = 8 * EPC;
+  u32x4* sm0 = smem[0];
+  u32x4* sm1 = sm0 + (BM + (GLU ? 2 * BN : BN)) * 8;
+  u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+  gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, Ak, oa, pb0, pb1, bstep, 0);
+  gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, Ak, oa, pb0, pb1, bstep, (nk > 1 ? 1 : 0) * BK);
+  lstore_tile<BM, CA, CB>(sm0, ra1, rb1, tid);
+  __syncthreads();
+  u32x4 f0[NF], f1[NF];
+#pragma unroll
+  for (int x = 0; x < NF; ++x) f1[x] = u32x4{0u, 0u, 0u, 0u};
+  for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = kt + h;
+      const u32x4* sm = h ? sm1 : sm0;
+      const int kn = (k + 2 < nk ? k + 2 : nk - 1) * BK;
+      if (h == 0) gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, Ak, oa, pb0, pb1, bstep, kn);
+      else        gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, Ak, oa, pb0, pb1, bstep, kn);
+      if constexpr (NV > 0) {
+        load_frags<NV, FM, FN, BN, GLU>(f0, sm + fa, sm + fb, cs[0]);
+        mma_substep<T, NV, FM, FN>(acc, f1);
+        load_frags<NV, FM, FN, BN, GLU>(f1, sm + fa, sm + fb, cs[1]);
+        mma_substep<T, NV, FM, FN>(acc, f0);
+        load_frags<NV, FM, FN, BN, GLU>(f0, sm + fa, sm + fb, cs[2]);
+      }
+      if (h == 0) lstore_tile<BM, CA, CB>(sm1, ra0, rb0, tid);
+      else        lstore_tile<BM, CA, CB>(sm0, ra1, rb1, tid);
+      if constexpr (NV > 0) {
+        mma_substep<T, NV, FM, FN>(acc, f1);
+        load_frags<NV, FM, FN, BN, GLU>(f1, sm + fa, sm + fb, cs[3]);
+        mma_substep<T, NV, FM, FN>(acc, f0);
+      }
+      if constexpr (sizeof(T) == 2 && NV > 0) {
+        constexpr int NM = NV * FN;
+        constexpr int ND = NV + FN;
+        constexpr int NL = CA + CB;
+        sched_substep<NM, ND, NL / 2, 0>();
+        sched_substep<NM, ND, NL - NL / 2, 0>();
+        sched_substep<NM, ND, 0, NL>();
+        sched_substep<NM, ND, 0, 0>();
+      }
+      __syncthreads();
+    }
+  }
+  if constexpr (NV > 0) mma_substep<T, NV, FM, FN>(acc, f1);
+}
+
 // GLU = true : out = H [rows][N] (type T),  h = silu(A W1^T) * (A W3^T)
 // GLU = false: out = Y [rows][N] (fp32),    y = A W2^T
 // Work entry: {g | n_idx << 10, first row of the M-tile inside group g}.
@@ -162,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
     const int32_t* __restrict__ nwork, const T* __restrict__ B0, const T* __restrict__ B1,
     const T* __restrict__ B0_last, const T* __restrict__ B1_last, int g_last, int K, int N,
-    int max_rows, int round, void* __restrict__ out) {
+    int max_rows, int ksplit, int round, void* __restrict__ out, float* __restrict__ out2) {
   constexpr int NT = kThreads;
   constexpr int BNT = GLU ? 2 * BN : BN;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-B chunk
@@ -189,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
   const int fb = (BM + (GLU ? wn * (BN / WN) : wn * WCOLS) + (lane & 31)) * 8;
   int cs[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) cs[q] = (2 * q + (lane >> 5)) ^ (lane & 7);
+  for (int q = 0; q < 4; ++q) cs[q] = (2 * q + (lane >> 5)) ^ swz(lane & 31);
   // Blocks are dispatched round-robin over the 8 XCDs and run one per CU:
   // the i-th block of XCD x takes list entry (i / cx) * round + x * cx + i % cx
   // (cx = CUs per XCD, round = 8 cx), so in every round each XCD works on cx
@@ -198,17 +282,21 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
   const int xi = blockIdx.x >> 3;
   const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
   if (t >= nwork[0]) return;
-  const int nk = K / BK;
+  const int Kc = K / ksplit;                     // K range of one split (multiple of 2 BK)
+  const int nk = Kc / BK;
   const size_t bstep = (size_t)(NT / 8) * K;   // element distance between a thread's B rows
   {
     const int2 wi = work[t];
     const int g = wi.x & 1023;
-    const int n0 = (wi.x >> 10) * BN;
+    const int n0 = ((wi.x >> 10) & 16383) * BN;
+    const int ks = (int)((uint32_t)wi.x >> 24);   // K split of this entry
+    const int kbeg = ks * Kc;
     const int gbeg = min(max(offsets[g], 0), max_rows);
     const int rbeg = gbeg + wi.y;
     const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
-    const T* w0 = (g == g_last) ? B0_last : B0 + (size_t)g * N * K;
-    const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) : nullptr;
+    const T* w0 = ((g == g_last) ? B0_last : B0 + (size_t)g * N * K) + kbeg;
+    const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) + kbeg : nullptr;
+    const T* Ak = A + kbeg;
 
     // per-thread source rows as 32-bit element offsets (operands hold < 2^31
     // elements).  Rows past the tile's end re-read its first row: their
@@ -233,48 +321,22 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[CA], rb[CB];
-    gload_tile<T, CA, CB, GLU, BN>(ra, rb, A, oa, pb0, pb1, bstep, 0);
-    lstore_tile<BM, CA, CB>(smem[0], ra, rb, tid);
-    __syncthreads();
-
-    // Software pipeline over k16 substeps q = 4 kt + s with four fragment
-    // slots (slot = s).  Iteration kt runs the MFMAs of stage kt-1's
-    // substeps 2, 3 and stage kt's substeps 0, 1 while it reads stage kt's
-    // four fragment sets, fetches stage kt+1 into registers and stores it to
-    // the other LDS buffer; the barrier then publishes that buffer.  Slots 2
-    // and 3 start as zeros, so the first iteration's leading MFMAs add 0.
-    u32x4 f[4][NF];
-#pragma unroll
-    for (int q = 2; q < 4; ++q)
-#pragma unroll
-      for (int x = 0; x < NF; ++x) f[q][x] = u32x4{0u, 0u, 0u, 0u};
-    for (int kt = 0; kt < nk; ++kt) {
-      const u32x4* sm = smem[kt & 1];
-      // the last stage re-fetches itself (in bounds; stored to the idle buffer)
-      const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
-      gload_tile<T, CA, CB, GLU, BN>(ra, rb, A, oa, pb0, pb1, bstep, kn);
-      load_frags<FM, FN, BN, GLU>(f[0], sm + fa, sm + fb, cs[0]);
-      mma_substep<T, FM, FN>(acc, f[2]);
-      load_frags<FM, FN, BN, GLU>(f[1], sm + fa, sm + fb, cs[1]);
-      mma_substep<T, FM, FN>(acc, f[3]);
-      load_frags<FM, FN, BN, GLU>(f[2], sm + fa, sm + fb, cs[2]);
-      mma_substep<T, FM, FN>(acc, f[0]);
-      load_frags<FM, FN, BN, GLU>(f[3], sm + fa, sm + fb, cs[3]);
-      lstore_tile<BM, CA, CB>(smem[(kt + 1) & 1], ra, rb, tid);
-      mma_substep<T, FM, FN>(acc, f[1]);
-      if constexpr (sizeof(T) == 2) {
-        constexpr int NM = FM * FN;
-        constexpr int NL = CA + CB;
-        sched_substep<NM, NF, NL / 2, 0>();
-        sched_substep<NM, NF, NL - NL / 2, 0>();
-        sched_substep<NM, NF, 0, 0>();
-        sched_substep<NM, NF, 0, NL>();
-      }
-      __syncthreads();
+    // live 32-row blocks of this wave's part of the tile
+    const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
+    auto* sm2 = reinterpret_cast<u32x4 (*)[1]>(&smem[0][0]);
+#define MOE_MAIN_LOOP(NV_)                                                                   \
+  main_loop<T, NV_, BM, BN, CA, CB, FM, FN, GLU>(acc, sm2, Ak, oa, pb0, pb1, bstep, nk, fa, fb, \
+                                                 cs, tid)
+    if (nv >= FM) {
+      MOE_MAIN_LOOP(FM);
+    } else if (nv == 0) {
+      MOE_MAIN_LOOP(0);
+    } else {
+      if constexpr (FM > 1) { if (nv == 1) MOE_MAIN_LOOP(1); }
+      if constexpr (FM > 2) { if (nv == 2) MOE_MAIN_LOOP(2); }
+      if constexpr (FM > 3) { if (nv == 3) MOE_MAIN_LOOP(3); }
     }
-    mma_substep<T, FM, FN>(acc, f[2]);
-    mma_substep<T, FM, FN>(acc, f[3]);
+#undef MOE_MAIN_LOOP
 
     // ---- epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
     // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.  Row offsets are compile-
@@ -300,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
           }
         }
     } else {
-      float* Y = (float*)out + row0 * N + n0 + wn * WCOLS + (lane & 31);
+      // split 0 writes to `out`; split ks > 0 to slab ks - 1 of `out2`
+      float* Yb = ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N;
+      float* Y = Yb + row0 * N + n0 + wn * WCOLS + (lane & 31);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -316,11 +380,12 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 }
 
 // Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
-// ceil(rows_g / BM) M-tiles times NN N-tiles, ordered by group, then by runs
-// of NG neighbouring N-tiles, then M-tile, then N-tile inside the run.
+// ceil(rows_g / BM) M-tiles times NN N-tiles times ksplit K-splits, ordered
+// by group, then K-split, then runs of NG neighbouring N-tiles, then M-tile,
+// then N-tile inside the run.
 __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ offsets, int G,
                                                     int BM, int max_rows, int NN, int NG,
-                                                    int2* __restrict__ work,
+                                                    int ksplit, int2* __restrict__ work,
                                                     int32_t* __restrict__ nwork) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t mts[1024];
@@ -332,7 +397,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
     mt = MOE_CEIL_DIV(b - a, BM);
   }
   mts[g] = mt;
-  sc[g] = mt * NN;
+  sc[g] = mt * NN * ksplit;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {       // inclusive Hillis-Steele scan
     const int v = (g >= o) ? sc[g - o] : 0;
@@ -350,7 +415,9 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
     }
     const int gg = lo;
     const int m = mts[gg];
-    const int j = e - (sc[gg] - m * NN);
+    const int jk = e - (sc[gg] - m * NN * ksplit);
+    const int ks = jk / (m * NN);                // K split: slowest inside a group
+    const int j = jk - ks * m * NN;
     int mi, ni;
     if (j < m * NG * nfull) {
       const int run = j / (m * NG), r = j - run * m * NG;
@@ -362,7 +429,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
       mi = r / last;
       ni = nfull * NG + (r - mi * last);
     }
-    work[e] = make_int2(gg | (ni << 10), mi * BM);
+    work[e] = make_int2(gg | (ni << 10) | (ks << 24), mi * BM);
   }
   if (g == 0) nwork[0] = total;
 }
@@ -382,21 +449,41 @@ static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
 }
 
 // Upper bound of work entries for one projection with N-tile width BN.
-static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN) {
-  return (MOE_CEIL_DIV(max_rows, BM) + G) * (int64_t)(N / BN);
+static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN, int ksplit = 1) {
+  return (MOE_CEIL_DIV(max_rows, BM) + G) * (int64_t)(N / BN) * ksplit;
 }
 
 static int up_bn(int cfg) { return cfg == 2 ? 256 : 128; }
 static int down_bn(int cfg, int d) { return (cfg == 3 || d % 256 != 0) ? 128 : 256; }
+static int num_cus();
+
+// K-split of the down projection: with few, long tiles (large rows per
+// expert) the last dispatch round can leave most CUs idle.  Split K in two
+// when that fills the rounds clearly better; the two partial row blocks are
+// summed in a fixed order afterwards (by the combine, or a reduce pass).
+static int down_split(const GemmPlan& p, int64_t max_rows, int G, int d, int F) {
+  if (p.cfg != 0 || F % 256 != 0 || F / 2 < 2048) return 1;
+  const double cus = (double)(num_cus() & ~7);
+  const double est = ((double)max_rows / p.BM + 0.5 * G) * (d / down_bn(p.cfg, d));
+  auto eff = [&](double t) { return (t / cus) / std::ceil(t / cus); };
+  return eff(2 * est) > eff(est) + 0.05 ? 2 : 1;
+}
+
+int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype) {
+  if (max_rows <= 0 || G <= 0) return 1;
+  return down_split(plan_for(dtype, max_rows, G, d, F), max_rows, G, d, F);
+}
 
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
+  const int ks = down_split(p, max_rows, G, d, F);
   const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d));
+  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d), ks);
   size_t b = align256((size_t)max_rows * F * es);                       // H
   b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
   b += align256(2 * sizeof(int32_t));                                  // entry counts
+  b += align256((size_t)(ks - 1) * max_rows * d * sizeof(float));       // extra K-split partials
   return b;
 }
 
@@ -423,47 +510,75 @@ struct GemmArgs {
   void* out;
   int2* work;
   int32_t* nwork;
+  int ksplit;
+  float* out2;
 };
 
 static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s) {
   const int NN = a.N / BN;
   const int NG = glu ? 8 : 4;
   hipLaunchKernelGGL(k_work_list, dim3(1), dim3(1024), 0, s, a.offsets, a.G, BM, a.max_rows, NN,
-                     NG < NN ? NG : NN, a.work, a.nwork);
+                     NG < NN ? NG : NN, a.ksplit, a.work, a.nwork);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
 static void run_gemm(const GemmArgs& a, hipStream_t s) {
-  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN);
+  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;           // blocks per dispatch round, whole XCDs
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   hipLaunchKernelGGL((k_moe_gemm<T, BM, BN, WM, WN, GLU>), dim3((unsigned)nb), dim3(kThreads), 0,
                      s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork, (const T*)a.B0,
                      (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last, a.K, a.N,
-                     a.max_rows, round, a.out);
+                     a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
 // Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
 // g_last >= 0, group g_last uses the separate (shared-expert) matrices.
+// Sum the K-split partial slabs into Y, rows [0, offsets[G]), in split order.
+__global__ __launch_bounds__(256) void k_reduce_split(float* __restrict__ Y,
+                                                      const float* __restrict__ Y2,
+                                                      const int32_t* __restrict__ offsets, int G,
+                                                      int max_rows, int d, int ksplit) {
+  const int r = blockIdx.x;
+  if (r >= min(max(offsets[G], 0), max_rows)) return;
+  const size_t slab = (size_t)max_rows * d;
+  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+    float4 a = *(float4*)(Y + (size_t)r * d + c);
+    for (int k = 1; k < ksplit; ++k) {
+      const float4 b = *(const float4*)(Y2 + (k - 1) * slab + (size_t)r * d + c);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *(float4*)(Y + (size_t)r * d + c) = a;
+  }
+}
+
+// Yrows receives the down projection.  If the down GEMM is split along K,
+// the partial slabs are Yrows and the workspace slab(s) after it; with
+// reduce = true they are summed into Yrows here, otherwise *partial2 tells
+// the caller where the second slab is (NULL when there is no split).
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, bool reduce, const float** partial2) {
+  if (partial2) *partial2 = nullptr;
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
+  const int ks = down_split(p, max_rows, G, d, F);
   const int es = dtype == MOE_BF16 ? 2 : 4;
   const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d));
+  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d), ks);
   char* q = (char*)ws;
   void* H = q;               q += align256((size_t)max_rows * F * es);
   int2* work_up = (int2*)q;  q += align256((size_t)wu * sizeof(int2));
   int2* work_dn = (int2*)q;  q += align256((size_t)wd * sizeof(int2));
-  int32_t* nwork = (int32_t*)q;
+  int32_t* nwork = (int32_t*)q; q += align256(2 * sizeof(int32_t));
+  float* slabs = (float*)q;  // (ks - 1) extra partial slabs of [max_rows][d]
   const int mr = (int)max_rows;
-  GemmArgs up{A, row_token, offsets, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork};
-  GemmArgs dn{H, nullptr, offsets, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
-              nwork + 1};
+  GemmArgs up{A,  row_token, offsets, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork,
+              1,  nullptr};
+  GemmArgs dn{H,  nullptr, offsets, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
+              nwork + 1, ks, slabs};
   run_work_list(up, p.BM, up_bn(p.cfg), true, s);
   run_work_list(dn, p.BM, down_bn(p.cfg, d), false, s);
   timing_mark("tile_map", s);
@@ -493,6 +608,13 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     timing_mark("ffn_up", s);
     run_gemm<float, 64, 128, 2, 2, false>(dn, s);
     timing_mark("ffn_down", s);
+  }
+  if (ks > 1) {
+    if (reduce)
+      hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)max_rows), dim3(256), 0, s, Yrows, slabs,
+                         offsets, G, mr, d, ks);
+    else if (partial2)
+      *partial2 = slabs;
   }
   return hipGetLastError();
 }

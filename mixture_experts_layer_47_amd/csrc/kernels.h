@@ -30,16 +30,21 @@ hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_
 
 // gemm.hip
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype);
+int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype);
+// The down projection may be split along K (ffn_down_split() > 1): then the
+// partial sums are summed into Yrows if `reduce`, else *partial2 receives the
+// second partial slab ([max_rows][d], to be added to Yrows by the caller).
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s);
+                              hipStream_t s, bool reduce, const float** partial2);
 
 // combine.hip
-hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
-                          int k, int d, const float* shared, const int32_t* shared_row0,
-                          void* Y, int dtype, hipStream_t s);
+// Yrows2 (optional): second K-split partial of the rows, added to Yrows.
+hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t* slot_row,
+                          const float* w, int64_t T, int k, int d, const float* shared,
+                          const int32_t* shared_row0, void* Y, int dtype, hipStream_t s);
 
 // timing.hip: records a phase-boundary event when timing is enabled.
 void timing_mark(const char* name, hipStream_t s, int first = 0);

@@ -57,6 +57,21 @@ def test_workspace_sizes_positive(L):
     assert L.moe_forward_workspace_size(ctypes.byref(lay), 4096) > (32768 + 4096) * 7168 * 4
 
 
+def test_down_projection_split_decision(L):
+    """Long-reduction, few-tile shapes split the down projection along K; the
+    workspace then carries one extra fp32 partial slab of [max_rows][d]."""
+    # Mixtral-shaped prefill: 8192 rows, 8 experts, d 4096, F 14336 -> split
+    big = L.moe_grouped_ffn_workspace_size(8192, 8, 4096, 14336, 1)
+    base = 8192 * 14336 * 2                      # H
+    slab = 8192 * 4096 * 4
+    assert big >= base + slab
+    # the parity-test shape (rows 1130, d 768, F 4096) also splits
+    assert L.moe_grouped_ffn_workspace_size(1130, 4, 768, 4096, 1) >= 1130 * 4096 * 2 + 1130 * 768 * 4
+    # short reductions never split
+    small = L.moe_grouped_ffn_workspace_size(1200, 8, 512, 640, 1)
+    assert small < 1200 * 640 * 2 + 1200 * 512 * 4
+
+
 def _route(L, **over):
     a = dict(X=1, dtype=1, T=16, d=256, Wg=1, E=8, bias=None, off=None, score=0, k=2, renorm=1,
              logits=None, ids=1, w=1, ps=None, ws=256, ws_bytes=1 << 30, stream=None)

@@ -209,6 +209,8 @@ FFN_SHAPES = {
     "large_d512": (512, 512, [600, 0], 5),
     # decode-sized groups (a few rows each)
     "decode": (512, 256, [2, 0, 1, 3, 2, 2, 0, 1, 4, 2, 1, 2, 3, 1, 2, 2], 0),
+    # large tiles with a long reduction: the down projection is split along K
+    "large_ksplit": (768, 4096, [300, 260, 280, 290], 0),
 }
 
 
@@ -241,6 +243,21 @@ def test_grouped_ffn_entry_point(dtype, use_row_token, shape):
         ref = O.expert_ffn(Xr[a:b], W1[e].double().numpy().T, W3[e].double().numpy().T,
                            W2[e].double().numpy().T, bf16_h=(dtype == "bf16"))
         H.check_rows(H.np64(Y[a:b]), ref, dtype == "bf16")
+
+
+def test_forward_ksplit_paths_agree():
+    """A shape whose down projection is split along K: the forward path that
+    sums the two partial slabs inside the combine (no expert-row output) and
+    the one that reduces them into the expert rows first must give the same
+    bits, and both must match the oracle."""
+    w = Workload("ksplit", T=600, d=768, E=4, k=2, F=4096, seed=23)
+    _announce("forward K-split")
+    inp = make_inputs(w, DEV)
+    layer = moe.layer_from_inputs(inp)
+    Y_plain = moe.forward(layer, inp["X"]).clone()
+    Y_aux, aux = _full_check(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(Y_plain, Y_aux)
 
 
 def test_combine_entry_point():
