@@ -104,6 +104,21 @@ def cpu_baseline(w, inp, target_s=15.0):
                       f"resident expert weights, numpy float64 oracle (tier 1), {tot:.1f} s"}
 
 
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration(torch):
+    """Reads COPY_BYTES and writes COPY_BYTES per launch (elementwise negation)."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES,
+                      "copy_calibration_bytes_written": COPY_BYTES}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +127,9 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device copy (negation kernel), five times, "
+                         "to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -120,6 +138,9 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import mixture_experts_layer_47_amd as moe
     from mixture_experts_layer_47_amd.workloads import WORKLOADS, make_inputs
 

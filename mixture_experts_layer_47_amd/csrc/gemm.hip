@@ -552,6 +552,46 @@ __global__ __launch_bounds__(256) void k_reduce_split(float* __restrict__ Y,
   }
 }
 
+// ---------------------------------------------------------------- router
+// Router logits through the same tiled kernel: one group of T rows,
+// part[z][t][e] = sum over K-split z of X[t] . Wg[e].  Used when E is a
+// multiple of 128; the select kernel sums the splits in order.
+__global__ void k_set_range(int32_t* __restrict__ off, int n) {
+  off[0] = 0;
+  off[1] = n;
+}
+
+bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split) {
+  // row offsets inside the kernel are 32-bit element offsets: T * d < 2^31
+  return dtype == MOE_BF16 && T >= 256 && T * (int64_t)d < ((int64_t)1 << 31) && E % 128 == 0 &&
+         E / 128 < 16384 && split >= 1 && split < 256 && d % split == 0 && (d / split) % 128 == 0;
+}
+
+size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split) {
+  const int bn = E % 256 == 0 ? 256 : 128;
+  return align256(2 * sizeof(int32_t)) +
+         align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2)) +
+         align256(sizeof(int32_t));
+}
+
+hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, int E, int split,
+                              float* part, void* ws, hipStream_t s) {
+  char* q = (char*)ws;
+  int32_t* off = (int32_t*)q;  q += align256(2 * sizeof(int32_t));
+  const int bn = E % 256 == 0 ? 256 : 128;
+  int2* work = (int2*)q;       q += align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2));
+  int32_t* nwork = (int32_t*)q;
+  hipLaunchKernelGGL(k_set_range, dim3(1), dim3(1), 0, s, off, (int)T);
+  const int mr = (int)T;
+  GemmArgs a{X, nullptr, off, 1, Wg, nullptr, nullptr, nullptr, -1, d, E, mr, part, work, nwork,
+             split, part + (size_t)T * E};
+  run_work_list(a, 128, bn, false, s);
+  using Tb = uint16_t;
+  if (bn == 256) run_gemm<Tb, 128, 256, 2, 2, false>(a, s);
+  else run_gemm<Tb, 128, 128, 2, 2, false>(a, s);
+  return hipGetLastError();
+}
+
 // Yrows receives the down projection.  If the down GEMM is split along K,
 // the partial slabs are Yrows and the workspace slab(s) after it; with
 // reduce = true they are summed into Yrows here, otherwise *partial2 tells

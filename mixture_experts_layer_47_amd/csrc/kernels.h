@@ -31,6 +31,12 @@ hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_
 // gemm.hip
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype);
 int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype);
+// Router logits on the tiled GEMM kernel (bf16, E a multiple of 128):
+// part[z][T][E] for the `split` K-splits z.
+bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split);
+size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split);
+hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, int E, int split,
+                              float* part, void* ws, hipStream_t s);
 // The down projection may be split along K (ffn_down_split() > 1): then the
 // partial sums are summed into Yrows if `reduce`, else *partial2 receives the
 // second partial slab ([max_rows][d], to be added to Yrows by the caller).

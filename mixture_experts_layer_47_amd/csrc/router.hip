@@ -211,6 +211,7 @@ size_t route_ws_bytes(int64_t T, int d, int E) {
   const size_t split = (size_t)router_split(d);
   size_t b = align256(split * (size_t)T * E * sizeof(float));      // partial logits
   b += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));   // prob_sum partials
+  b += router_gemm_ws_bytes(T, d, E, (int)split);                    // tiled-GEMM work list
   return b;
 }
 
@@ -227,14 +228,20 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
   const int dchunk = MOE_CEIL_DIV(MOE_CEIL_DIV(d, split), kstep) * kstep;
   char* p = (char*)ws;
   float* part = (float*)p;  p += align256((size_t)split * T * E * sizeof(float));
-  float* ps_part = (float*)p;
-  dim3 g1((unsigned)MOE_CEIL_DIV(T, 16), (unsigned)MOE_CEIL_DIV(E, 64), (unsigned)split);
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
-                       (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk);
-  else
-    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
-                       (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk);
+  float* ps_part = (float*)p; p += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));
+  if (router_gemm_ok(dtype, T, d, E, split)) {
+    // many experts: the LDS-tiled GEMM reads X once and W_g once per M-tile
+    hipError_t e = launch_router_gemm(X, Wg, T, d, E, split, part, p, s);
+    if (e != hipSuccess) return e;
+  } else {
+    dim3 g1((unsigned)MOE_CEIL_DIV(T, 16), (unsigned)MOE_CEIL_DIV(E, 64), (unsigned)split);
+    if (dtype == MOE_BF16)
+      hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
+                         (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk);
+    else
+      hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
+                         (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk);
+  }
   const int nblk = (int)MOE_CEIL_DIV(T, 4);
   float* psp = prob_sum ? ps_part : nullptr;
   const int ne = MOE_CEIL_DIV(E, 64);
