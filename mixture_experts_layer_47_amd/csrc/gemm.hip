@@ -237,6 +237,53 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
   if constexpr (NV > 0) mma_substep<T, NV, FM, FN>(acc, f1);
 }
 
+// Tile epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
+// 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.  Row offsets are compile-
+// time constants compared with the tile's remaining rows, and addresses are
+// formed from the tile's first row.
+//   GLU : out = H (type T), h = silu(gate) * up rounded once
+//   else: split 0 writes fp32 to out, split ks > 0 to slab ks - 1 of out2
+template <typename T, int BN, int BNT, int WN, int FM, int FN, bool GLU>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __restrict__ out,
+                                           float* __restrict__ out2, int ks, int max_rows, int N,
+                                           int rbeg, int rows, int arow0, int n0, int wn,
+                                           int lane) {
+  constexpr int FNH = GLU ? FN / 2 : FN;
+  constexpr int WCOLS = BNT / WN;
+  const int lrow0 = arow0 + (lane >> 5) * 4;          // this lane's first row
+  const int rem = rows - lrow0;                        // rows this lane may store
+  const size_t row0 = (size_t)(rbeg + lrow0);
+  if constexpr (GLU) {
+    T* H = (T*)out + row0 * N + n0 + wn * (BN / WN) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = i * 32 + (r >> 2) * 8 + (r & 3);
+        if (off < rem) {
+#pragma unroll
+          for (int j = 0; j < FNH; ++j) {
+            const float h = silu_f(acc[i][j][r]) * acc[i][j + FNH][r];
+            store_h<T>(H + (size_t)off * N + j * 32, h);
+          }
+        }
+      }
+  } else {
+    float* Yb = ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N;
+    float* Y = Yb + row0 * N + n0 + wn * WCOLS + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = i * 32 + (r >> 2) * 8 + (r & 3);
+        if (off < rem) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Y[(size_t)off * N + j * 32] = acc[i][j][r];
+        }
+      }
+  }
+}
+
 // GLU = true : out = H [rows][N] (type T),  h = silu(A W1^T) * (A W3^T)
 // GLU = false: out = Y [rows][N] (fp32),    y = A W2^T
 // Work entry: {g | n_idx << 10, first row of the M-tile inside group g}.
@@ -254,7 +301,6 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
   constexpr int CA = BM * 8 / NT, CB = BNT * 8 / NT;   // 16-B chunks per thread per stage
   constexpr int WROWS = BM / WM, WCOLS = BNT / WN;
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
-  constexpr int FNH = GLU ? FN / 2 : FN;
   constexpr int NF = FM + FN;                          // fragments per substep
   static_assert(WM * WN == 4, "four waves");
   static_assert(BM % 32 == 0 && BNT % 32 == 0 && BN % 32 == 0, "32-row load blocks");
@@ -338,45 +384,233 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     }
 #undef MOE_MAIN_LOOP
 
-    // ---- epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.  Row offsets are compile-
-    // time constants compared with the tile's remaining rows, and addresses
-    // are formed from the tile's first row, so nothing here is hoisted out
-    // of the tile loop.
-    const int lrow0 = arow0 + (lane >> 5) * 4;          // this lane's first row
-    const int rem = rows - lrow0;                        // rows this lane may store
-    const size_t row0 = (size_t)(rbeg + lrow0);
-    if constexpr (GLU) {
-      T* H = (T*)out + row0 * N + n0 + wn * (BN / WN) + (lane & 31);
+    store_tile<T, BN, BNT, WN, FM, FN, GLU>(acc, out, out2, ks, max_rows, N, rbeg, rows, arow0,
+                                            n0, wn, lane);
+  }
+}
+
+// ------------------------------------------------------- LDS-DMA variant
+// bf16 tiles with BM, BNT multiples of 64.  A stage holds KB bytes of every
+// A and B row (KB = 64: 32 K-elements, KB = 128: 64); NBUF stages live in a
+// ring of distinct LDS arrays.  global_load_lds moves 16 B per lane from
+// global memory straight into LDS (lane L of one wave instruction fills
+// bytes [16 L, 16 L + 16) of a 1 KB block = 1024 / KB rows), so stages never
+// pass through registers.  LDS row r keeps chunk c (16 B) at slot
+// c ^ swz(r); the lane that fills a slot fetches the matching chunk, and
+// the 16-B fragment reads are bank-conflict free for 8- and 16-lane LDS
+// service.
+//
+// Iteration s (stage s in buffer s mod NBUF):
+//   wait until this wave's copies of stage s have landed (those of the
+//   NBUF - 2 later stages may still be in flight) and its LDS reads are done
+//   barrier: every wave's copies of stage s are visible, and buffer
+//   (s - 1) mod NBUF is no longer read
+//   start the copies of stage s + NBUF - 1 into buffer (s - 1) mod NBUF
+//   per k16 substep: MFMA the previous substep's fragments | read this one's
+// Copies past the last stage re-fetch it (in bounds, never read), so every
+// wave always has the same number of copies in flight.
+template <int KB>
+__device__ __forceinline__ int swz_kb(int r) {
+  if constexpr (KB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return swz(r);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Copies of one stage: instruction i of wave w fills A rows (w CA + i) RPI ..
+// + RPI and B rows BM + (w CB + i) RPI .. + RPI of the buffer.
+// pa[i], pb[i]: this lane's source of copy instruction i at stage 0.
+template <int BM, int CA, int CB, int KB>
+__device__ __forceinline__ void dma_stage(u32x4* buf, const uint16_t* const (&pa)[CA],
+                                          const uint16_t* const (&pb)[CB], int koff, int wave) {
+  constexpr int CPR = KB / 16, RPI = 64 / CPR;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < CA; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
+                                     (void*)(buf + ((wave * CA + i) * RPI) * CPR), 16, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = i * 32 + (r >> 2) * 8 + (r & 3);
-          if (off < rem) {
+  for (int i = 0; i < CB; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(pb[i] + koff),
+                                     (void*)(buf + (BM + (wave * CB + i) * RPI) * CPR), 16, 0, 0);
+}
+
+template <int NA, int FM, int FN, int BN, bool GLU, int CPR>
+__device__ __forceinline__ void load_frags_kb(u32x4* f, const u32x4* pa, const u32x4* pb, int cs) {
+  constexpr int FNH = GLU ? FN / 2 : FN;
 #pragma unroll
-            for (int j = 0; j < FNH; ++j) {
-              const float h = silu_f(acc[i][j][r]) * acc[i][j + FNH][r];
-              store_h<T>(H + (size_t)off * N + j * 32, h);
-            }
-          }
+  for (int i = 0; i < NA; ++i) f[i] = pa[i * 32 * CPR + cs];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int rr = GLU ? ((j < FNH) ? j * 32 : BN + (j - FNH) * 32) : j * 32;
+    f[FM + j] = pb[rr * CPR + cs];
+  }
+}
+
+__device__ __forceinline__ u32x4* ring(int h, u32x4* b0, u32x4* b1, u32x4* b2, u32x4* b3) {
+  return h == 0 ? b0 : h == 1 ? b1 : h == 2 ? b2 : b3;
+}
+
+template <int NV, int BM, int BN, int CA, int CB, int FM, int FN, bool GLU, int KB, int NBUF>
+__device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], u32x4* b0, u32x4* b1,
+                                              u32x4* b2, u32x4* b3,
+                                              const uint16_t* const (&pa)[CA],
+                                              const uint16_t* const (&pb)[CB], int nk, int fa,
+                                              int fb, const int (&cs)[4], int wave) {
+  constexpr int NF = FM + FN;
+  constexpr int BK = KB / 2;                 // K-elements per stage
+  constexpr int CPR = KB / 16;
+  constexpr int NSUB = KB / 32;              // k16 substeps per stage
+  // The last buffer first receives a throw-away copy (stage 0 again), so the
+  // copies in flight when the loop is entered target the same buffers, in
+  // the same order, as at the end of every loop iteration.
+  dma_stage<BM, CA, CB, KB>(ring(NBUF - 1, b0, b1, b2, b3), pa, pb, 0, wave);
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    dma_stage<BM, CA, CB, KB>(ring(p, b0, b1, b2, b3), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
+  u32x4 f0[NF], f1[NF];
+#pragma unroll
+  for (int x = 0; x < NF; ++x) f1[x] = u32x4{0u, 0u, 0u, 0u};
+  for (int s0 = 0; s0 < nk; s0 += NBUF) {
+#pragma unroll
+    for (int h = 0; h < NBUF; ++h) {
+      const int s = s0 + h;
+      wait_vm_lgkm<(NBUF - 2) * (CA + CB)>();
+      __builtin_amdgcn_s_barrier();
+      const int t = s + NBUF - 1;
+      dma_stage<BM, CA, CB, KB>(ring((h + NBUF - 1) % NBUF, b0, b1, b2, b3), pa, pb,
+                                (t < nk ? t : nk - 1) * BK, wave);
+      const u32x4* cur = ring(h, b0, b1, b2, b3);
+      if constexpr (NV > 0) {
+#pragma unroll
+        for (int q = 0; q < NSUB; q += 2) {
+          load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f0, cur + fa, cur + fb, cs[q]);
+          mma_substep<uint16_t, NV, FM, FN>(acc, f1);
+          load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f1, cur + fa, cur + fb, cs[q + 1]);
+          mma_substep<uint16_t, NV, FM, FN>(acc, f0);
         }
-    } else {
-      // split 0 writes to `out`; split ks > 0 to slab ks - 1 of `out2`
-      float* Yb = ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N;
-      float* Y = Yb + row0 * N + n0 + wn * WCOLS + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = i * 32 + (r >> 2) * 8 + (r & 3);
-          if (off < rem) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) Y[(size_t)off * N + j * 32] = acc[i][j][r];
-          }
+        constexpr int NM = NV * FN;
+        constexpr int ND = NV + FN;
+        constexpr int NG = CA + CB;
+        if constexpr (NSUB == 2) {
+          sched_substep<NM, ND, NG, 0>();
+          sched_substep<NM, ND, 0, 0>();
+        } else {
+          sched_substep<NM, ND, NG / 2, 0>();
+          sched_substep<NM, ND, NG - NG / 2, 0>();
+          sched_substep<NM, ND, 0, 0>();
+          sched_substep<NM, ND, 0, 0>();
         }
+      }
     }
   }
+  if constexpr (NV > 0) mma_substep<uint16_t, NV, FM, FN>(acc, f1);
+  wait_vm_lgkm<0>();   // no copy may still be landing when the block ends
+}
+
+template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF>
+__global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, const int2* __restrict__ work,
+    const int32_t* __restrict__ nwork, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B0_last,
+    const uint16_t* __restrict__ B1_last, int g_last, int K, int N, int max_rows, int ksplit,
+    int round, void* __restrict__ out, float* __restrict__ out2) {
+  using T = uint16_t;
+  constexpr int BNT = GLU ? 2 * BN : BN;
+  constexpr int CPR = KB / 16, RPI = 64 / CPR;
+  constexpr int CA = BM / (4 * RPI), CB = BNT / (4 * RPI);   // copies per wave per stage
+  constexpr int WROWS = BM / WM, WCOLS = BNT / WN;
+  constexpr int FM = WROWS / 32, FN = WCOLS / 32;
+  constexpr int SZ = (BM + BNT) * CPR;                       // 16-B slots per stage
+  static_assert(WM * WN == 4 && (KB == 64 || KB == 128), "four waves, 64- or 128-B rows");
+  // K / ksplit is a multiple of 128 elements: the ring advances NBUF stages
+  // per trip without a tail
+  static_assert((KB == 64 && NBUF == 4) || (KB == 128 && NBUF == 2), "stage ring");
+  static_assert(BM % (4 * RPI) == 0 && BNT % (4 * RPI) == 0 && FM >= 1 && FN >= 1 &&
+                (!GLU || FN % 2 == 0), "tile shape");
+  __shared__ u32x4 L0[SZ], L1[SZ], L2[NBUF > 2 ? SZ : 1], L3[NBUF > 3 ? SZ : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int arow0 = wm * WROWS;
+  const int fa = (arow0 + (lane & 31)) * CPR;
+  const int fb = (BM + (GLU ? wn * (BN / WN) : wn * WCOLS) + (lane & 31)) * CPR;
+  int cs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cs[q] = ((2 * q + (lane >> 5)) % CPR) ^ swz_kb<KB>(lane & 31);
+  const int cx = round >> 3;
+  const int xi = blockIdx.x >> 3;
+  const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
+  if (t >= nwork[0]) return;
+  const int Kc = K / ksplit;
+  const int nk = Kc / (KB / 2);
+  const int2 wi = work[t];
+  const int g = wi.x & 1023;
+  const int n0 = ((wi.x >> 10) & 16383) * BN;
+  const int ks = (int)((uint32_t)wi.x >> 24);
+  const int kbeg = ks * Kc;
+  const int gbeg = min(max(offsets[g], 0), max_rows);
+  const int rbeg = gbeg + wi.y;
+  const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
+  const T* w0 = ((g == g_last) ? B0_last : B0 + (size_t)g * N * K) + kbeg;
+  const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) + kbeg : nullptr;
+
+  // This lane's source of each copy: row (w C + i) RPI + lane / CPR of the
+  // tile, chunk (lane % CPR) ^ swz(row).  Rows past the tile's end re-read
+  // its first row: their outputs are never stored.
+  const int slot = lane % CPR;
+  const T* pa[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int r = (wave * CA + i) * RPI + lane / CPR;
+    int src = rbeg + (r < rows ? r : 0);
+    if (row_token) src = row_token[src];
+    pa[i] = A + (size_t)src * K + kbeg + ((slot ^ swz_kb<KB>(r & 31)) * 8);
+  }
+  const T* pb[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int r = (wave * CB + i) * RPI + lane / CPR;
+    const int c = (slot ^ swz_kb<KB>(r & 31)) * 8;
+    if constexpr (GLU)
+      pb[i] = (r < BN ? w0 + (size_t)(n0 + r) * K : w1 + (size_t)(n0 + r - BN) * K) + c;
+    else
+      pb[i] = w0 + (size_t)(n0 + r) * K + c;
+  }
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
+#define MOE_DMA_LOOP(NV_)                                                                   \
+  main_loop_dma<NV_, BM, BN, CA, CB, FM, FN, GLU, KB, NBUF>(acc, L0, L1, L2, L3, pa, pb, nk, fa, \
+                                                            fb, cs, wave)
+  if (nv >= FM) {
+    MOE_DMA_LOOP(FM);
+  } else if (nv == 0) {
+    MOE_DMA_LOOP(0);
+  } else {
+    if constexpr (FM > 1) { if (nv == 1) MOE_DMA_LOOP(1); }
+    if constexpr (FM > 2) { if (nv == 2) MOE_DMA_LOOP(2); }
+    if constexpr (FM > 3) { if (nv == 3) MOE_DMA_LOOP(3); }
+    if constexpr (FM > 4) { if (nv == 4) MOE_DMA_LOOP(4); }
+    if constexpr (FM > 5) { if (nv == 5) MOE_DMA_LOOP(5); }
+  }
+#undef MOE_DMA_LOOP
+  store_tile<T, BN, BNT, WN, FM, FN, GLU>(acc, out, out2, ks, max_rows, N, rbeg, rows, arow0, n0,
+                                          wn, lane);
 }
 
 // Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
@@ -435,6 +669,9 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ launch
+#ifndef MOE_CFG0_BM
+#define MOE_CFG0_BM 256
+#endif
 struct GemmPlan {
   int BM;
   int cfg;   // 0 = large, 1 = medium, 2 = small (decode), 3 = fp32
@@ -443,7 +680,7 @@ struct GemmPlan {
 static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
   if (dtype == MOE_F32) return {64, 3};
   const double avg = (double)max_rows / (double)(G > 0 ? G : 1);
-  if (avg >= 192.0) return {256, 0};
+  if (avg >= 192.0) return {MOE_CFG0_BM, 0};
   if (avg >= 48.0 || F % 256 != 0 || d % 256 != 0) return {128, 1};
   return {32, 2};
 }
@@ -530,6 +767,21 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork, (const T*)a.B0,
                      (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last, a.K, a.N,
                      a.max_rows, a.ksplit, round, a.out, a.out2);
+}
+
+#ifndef MOE_DMA_KB
+#define MOE_DMA_KB 128
+#endif
+template <int BM, int BN, int WM, int WN, bool GLU>
+static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
+  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
+  const int round = num_cus() & ~7;
+  const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
+  using T = uint16_t;
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, MOE_DMA_KB, MOE_DMA_KB == 64 ? 4 : 2>), dim3((unsigned)nb),
+                     dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
+                     (const T*)a.B0, (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last,
+                     a.K, a.N, a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
 // Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
@@ -625,7 +877,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   if (dtype == MOE_BF16) {
     using T = uint16_t;
     switch (p.cfg) {
-      case 0: run_gemm<T, 256, 128, 2, 2, true>(up, s); break;
+      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true>(up, s); break;
       case 1: run_gemm<T, 128, 128, 2, 2, true>(up, s); break;
       default: run_gemm<T, 32, 256, 1, 4, true>(up, s); break;
     }
@@ -633,8 +885,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_gemm<T, 256, 256, 2, 2, false>(dn, s);
-        else run_gemm<T, 256, 128, 2, 2, false>(dn, s);
+        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false>(dn, s);
+        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false>(dn, s);
         break;
       case 1:
         if (b256) run_gemm<T, 128, 256, 2, 2, false>(dn, s);
