@@ -312,6 +312,19 @@ def test_single_expert_is_dense_swiglu():
     assert np.allclose(Y, dense, atol=1e-13, rtol=0)
 
 
+def test_shared_expert_is_added_with_weight_one():
+    # one routed expert (top-1, renormalised gate = 1) plus the always-on shared
+    # expert [Book 14.2.4]: Y = SwiGLU_routed(x) + SwiGLU_shared(x), written out
+    rng = np.random.default_rng(8)
+    X, Wg, W1, W3, W2, sh = _rand_layer(rng, 7, 5, 1, 3, True)
+    Y = O.forward(X, Wg, W1, W3, W2, k=1, shared=sh)["Y"]
+
+    def swiglu(a, b, c):
+        g = X @ a
+        return ((g / (1.0 + np.exp(-g))) * (X @ b)) @ c
+    assert np.allclose(Y, swiglu(W1[0], W3[0], W2[0]) + swiglu(*sh), atol=1e-13, rtol=0)
+
+
 def test_large_capacity_equals_no_capacity():
     rng = np.random.default_rng(6)
     X, Wg, W1, W3, W2, sh = _rand_layer(rng, 20, 8, 5, 6, True)
@@ -356,6 +369,32 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         test_gates_renorm_sum_to_one_and_topk_softmax_identity()
     monkeypatch.setattr(O, "gates", good_gates)
     # 3. floating-point capacity instead of the exact rational
+    good_cap = O.capacity
     monkeypatch.setattr(O, "capacity", lambda cf, N, k, E: math.ceil(cf * N * k / E))
     with pytest.raises(AssertionError):
         test_capacity_is_exact_rational()
+    monkeypatch.setattr(O, "capacity", good_cap)
+    # 4. ties resolved towards the higher expert id
+    good_sel = O.select_topk
+
+    def ties_high(lg, k, sf, bias=None):
+        lg = np.asarray(lg, dtype=np.float64)
+        b = None if bias is None else np.asarray(bias, dtype=np.float64)[::-1]
+        ids, key = good_sel(lg[:, ::-1], k, sf, b)
+        return lg.shape[1] - 1 - ids, key[:, ::-1]
+    monkeypatch.setattr(O, "select_topk", ties_high)
+    with pytest.raises(AssertionError):
+        test_topk_order_and_ties()
+    monkeypatch.setattr(O, "select_topk", good_sel)
+    # 5. the shared expert's output left out of the combine
+    good_comb = O.combine
+    monkeypatch.setattr(O, "combine", lambda rows, sr, g, shared_rows=None: good_comb(rows, sr, g))
+    with pytest.raises(AssertionError):
+        test_shared_expert_is_added_with_weight_one()
+    monkeypatch.setattr(O, "combine", good_comb)
+    # 6. the drop rule off by one (rank <= C kept)
+    good_disp = O.dispatch
+    monkeypatch.setattr(O, "dispatch", lambda ids, E, cap=None: good_disp(ids, E, None if cap is None else cap + 1))
+    with pytest.raises(AssertionError):
+        test_drop_six_token_example()
+    monkeypatch.setattr(O, "dispatch", good_disp)
