@@ -452,61 +452,89 @@ __device__ __forceinline__ void load_frags_kb(u32x4* f, const u32x4* pa, const u
   }
 }
 
-__device__ __forceinline__ u32x4* ring(int h, u32x4* b0, u32x4* b1, u32x4* b2, u32x4* b3) {
-  return h == 0 ? b0 : h == 1 ? b1 : h == 2 ? b2 : b3;
+struct Ring {
+  u32x4 *b0, *b1, *b2, *b3, *b4, *b5;
+};
+__device__ __forceinline__ u32x4* ring(int h, const Ring& r) {
+  return h == 0 ? r.b0 : h == 1 ? r.b1 : h == 2 ? r.b2 : h == 3 ? r.b3 : h == 4 ? r.b4 : r.b5;
+}
+
+// MFMAs and fragment reads of one stage held in `cur`: per k16 substep, MFMA
+// the previous substep's fragments while reading this one's.
+template <int NV, int BN, int CA, int CB, int FM, int FN, bool GLU, int KB>
+__device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cur,
+                                          u32x4 (&f0)[FM + FN], u32x4 (&f1)[FM + FN], int fa,
+                                          int fb, const int (&cs)[4], bool with_copies) {
+  constexpr int CPR = KB / 16;
+  constexpr int NSUB = KB / 32;
+#pragma unroll
+  for (int q = 0; q < NSUB; q += 2) {
+    load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f0, cur + fa, cur + fb, cs[q]);
+    mma_substep<uint16_t, NV, FM, FN>(acc, f1);
+    load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f1, cur + fa, cur + fb, cs[q + 1]);
+    mma_substep<uint16_t, NV, FM, FN>(acc, f0);
+  }
+  constexpr int NM = NV * FN;
+  constexpr int ND = NV + FN;
+  constexpr int NG = CA + CB;
+  if (with_copies) {
+    if constexpr (NSUB == 2) {
+      sched_substep<NM, ND, NG, 0>();
+      sched_substep<NM, ND, 0, 0>();
+    } else {
+      sched_substep<NM, ND, NG / 2, 0>();
+      sched_substep<NM, ND, NG - NG / 2, 0>();
+      sched_substep<NM, ND, 0, 0>();
+      sched_substep<NM, ND, 0, 0>();
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) sched_substep<NM, ND, 0, 0>();
+  }
 }
 
 template <int NV, int BM, int BN, int CA, int CB, int FM, int FN, bool GLU, int KB, int NBUF>
-__device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], u32x4* b0, u32x4* b1,
-                                              u32x4* b2, u32x4* b3,
+__device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring& rb,
                                               const uint16_t* const (&pa)[CA],
                                               const uint16_t* const (&pb)[CB], int nk, int fa,
                                               int fb, const int (&cs)[4], int wave) {
   constexpr int NF = FM + FN;
   constexpr int BK = KB / 2;                 // K-elements per stage
-  constexpr int CPR = KB / 16;
-  constexpr int NSUB = KB / 32;              // k16 substeps per stage
   // The last buffer first receives a throw-away copy (stage 0 again), so the
   // copies in flight when the loop is entered target the same buffers, in
   // the same order, as at the end of every loop iteration.
-  dma_stage<BM, CA, CB, KB>(ring(NBUF - 1, b0, b1, b2, b3), pa, pb, 0, wave);
+  dma_stage<BM, CA, CB, KB>(ring(NBUF - 1, rb), pa, pb, 0, wave);
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
-    dma_stage<BM, CA, CB, KB>(ring(p, b0, b1, b2, b3), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
+    dma_stage<BM, CA, CB, KB>(ring(p, rb), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
   u32x4 f0[NF], f1[NF];
 #pragma unroll
   for (int x = 0; x < NF; ++x) f1[x] = u32x4{0u, 0u, 0u, 0u};
-  for (int s0 = 0; s0 < nk; s0 += NBUF) {
+  const int nfull = nk - nk % NBUF;
+  for (int s0 = 0; s0 < nfull; s0 += NBUF) {
 #pragma unroll
     for (int h = 0; h < NBUF; ++h) {
       const int s = s0 + h;
       wait_vm_lgkm<(NBUF - 2) * (CA + CB)>();
       __builtin_amdgcn_s_barrier();
       const int t = s + NBUF - 1;
-      dma_stage<BM, CA, CB, KB>(ring((h + NBUF - 1) % NBUF, b0, b1, b2, b3), pa, pb,
+      dma_stage<BM, CA, CB, KB>(ring((h + NBUF - 1) % NBUF, rb), pa, pb,
                                 (t < nk ? t : nk - 1) * BK, wave);
-      const u32x4* cur = ring(h, b0, b1, b2, b3);
-      if constexpr (NV > 0) {
+      if constexpr (NV > 0)
+        stage_mma<NV, BN, CA, CB, FM, FN, GLU, KB>(acc, ring(h, rb), f0, f1, fa, fb, cs, true);
+    }
+  }
+  // Tail (nk mod NBUF stages): their copies were all started inside the loop
+  // (copies are issued NBUF - 1 stages ahead), so only waits remain.
+  for (int s = nfull; s < nk; ++s) {
+    wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (NV > 0) {
+      const int h = s % NBUF;
 #pragma unroll
-        for (int q = 0; q < NSUB; q += 2) {
-          load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f0, cur + fa, cur + fb, cs[q]);
-          mma_substep<uint16_t, NV, FM, FN>(acc, f1);
-          load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f1, cur + fa, cur + fb, cs[q + 1]);
-          mma_substep<uint16_t, NV, FM, FN>(acc, f0);
-        }
-        constexpr int NM = NV * FN;
-        constexpr int ND = NV + FN;
-        constexpr int NG = CA + CB;
-        if constexpr (NSUB == 2) {
-          sched_substep<NM, ND, NG, 0>();
-          sched_substep<NM, ND, 0, 0>();
-        } else {
-          sched_substep<NM, ND, NG / 2, 0>();
-          sched_substep<NM, ND, NG - NG / 2, 0>();
-          sched_substep<NM, ND, 0, 0>();
-          sched_substep<NM, ND, 0, 0>();
-        }
-      }
+      for (int c = 0; c < NBUF; ++c)
+        if (h == c)
+          stage_mma<NV, BN, CA, CB, FM, FN, GLU, KB>(acc, ring(c, rb), f0, f1, fa, fb, cs, false);
     }
   }
   if constexpr (NV > 0) mma_substep<uint16_t, NV, FM, FN>(acc, f1);
@@ -529,12 +557,12 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
   constexpr int SZ = (BM + BNT) * CPR;                       // 16-B slots per stage
   static_assert(WM * WN == 4 && (KB == 64 || KB == 128), "four waves, 64- or 128-B rows");
-  // K / ksplit is a multiple of 128 elements: the ring advances NBUF stages
-  // per trip without a tail
-  static_assert((KB == 64 && NBUF == 4) || (KB == 128 && NBUF == 2), "stage ring");
+  static_assert(NBUF >= 2 && NBUF <= 6, "stage ring of 2..6 buffers");
   static_assert(BM % (4 * RPI) == 0 && BNT % (4 * RPI) == 0 && FM >= 1 && FN >= 1 &&
                 (!GLU || FN % 2 == 0), "tile shape");
-  __shared__ u32x4 L0[SZ], L1[SZ], L2[NBUF > 2 ? SZ : 1], L3[NBUF > 3 ? SZ : 1];
+  __shared__ u32x4 L0[SZ], L1[SZ], L2[NBUF > 2 ? SZ : 1], L3[NBUF > 3 ? SZ : 1],
+      L4[NBUF > 4 ? SZ : 1], L5[NBUF > 5 ? SZ : 1];
+  const Ring rb{L0, L1, L2, L3, L4, L5};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -595,8 +623,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 
   const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
 #define MOE_DMA_LOOP(NV_)                                                                   \
-  main_loop_dma<NV_, BM, BN, CA, CB, FM, FN, GLU, KB, NBUF>(acc, L0, L1, L2, L3, pa, pb, nk, fa, \
-                                                            fb, cs, wave)
+  main_loop_dma<NV_, BM, BN, CA, CB, FM, FN, GLU, KB, NBUF>(acc, rb, pa, pb, nk, fa, fb, cs, wave)
   if (nv >= FM) {
     MOE_DMA_LOOP(FM);
   } else if (nv == 0) {
@@ -769,16 +796,13 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
-#ifndef MOE_DMA_KB
-#define MOE_DMA_KB 128
-#endif
-template <int BM, int BN, int WM, int WN, bool GLU>
+template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, MOE_DMA_KB, MOE_DMA_KB == 64 ? 4 : 2>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
                      (const T*)a.B0, (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last,
                      a.K, a.N, a.max_rows, a.ksplit, round, a.out, a.out2);
@@ -838,9 +862,8 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
   GemmArgs a{X, nullptr, off, 1, Wg, nullptr, nullptr, nullptr, -1, d, E, mr, part, work, nwork,
              split, part + (size_t)T * E};
   run_work_list(a, 128, bn, false, s);
-  using Tb = uint16_t;
-  if (bn == 256) run_gemm<Tb, 128, 256, 2, 2, false>(a, s);
-  else run_gemm<Tb, 128, 128, 2, 2, false>(a, s);
+  if (bn == 256) run_gemm_dma<128, 256, 2, 2, false, 128, 3>(a, s);
+  else run_gemm_dma<128, 128, 2, 2, false, 128, 3>(a, s);
   return hipGetLastError();
 }
 
@@ -878,7 +901,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     using T = uint16_t;
     switch (p.cfg) {
       case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true>(up, s); break;
-      case 1: run_gemm<T, 128, 128, 2, 2, true>(up, s); break;
+      case 1: run_gemm_dma<128, 128, 2, 2, true, 128, 3>(up, s); break;
       default: run_gemm<T, 32, 256, 1, 4, true>(up, s); break;
     }
     timing_mark("ffn_up", s);
@@ -889,8 +912,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false>(dn, s);
         break;
       case 1:
-        if (b256) run_gemm<T, 128, 256, 2, 2, false>(dn, s);
-        else run_gemm<T, 128, 128, 2, 2, false>(dn, s);
+        if (b256) run_gemm_dma<128, 256, 2, 2, false, 128, 3>(dn, s);
+        else run_gemm_dma<128, 128, 2, 2, false, 128, 3>(dn, s);
         break;
       default: run_gemm<T, 32, 256, 1, 4, false>(dn, s); break;
     }
