@@ -46,10 +46,17 @@ __global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   const int nb = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int g = 0; g < kAlignChunk / 64; ++g) {
+  constexpr int NG = kAlignChunk / 64;
+  int ev[NG];                                         // all loads in flight at once
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
     const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
-    const bool v = s < Tk;
-    const int e = v ? ids[s] : 0;
+    ev[g] = s < Tk ? ids[s] : -1;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bool v = ev[g] >= 0;
+    const int e = v ? ev[g] : 0;
     const uint64_t eq = match_id(e, v, nb);
     if (v && (eq & lt) == 0)                          // lowest lane of its id
       cnt[e] = cnt[e] + __popcll(eq);
@@ -108,10 +115,18 @@ __global__ __launch_bounds__(256) void k_align_scatter(
   for (int e = lane; e < E; e += 64) cnt[e] = base[(size_t)c * E + e];
   const int nb = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int g = 0; g < kAlignChunk / 64; ++g) {
+  constexpr int NG = kAlignChunk / 64;
+  int ev[NG];                                         // all loads in flight at once
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
     const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
-    const bool v = s < Tk;
-    const int e = v ? ids[s] : 0;
+    ev[g] = s < Tk ? ids[s] : -1;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const bool v = ev[g] >= 0;
+    const int e = v ? ev[g] : 0;
     const uint64_t eq = match_id(e, v, nb);
     int rank = 0;
     if (v) rank = cnt[e] + __popcll(eq & lt);

@@ -831,20 +831,24 @@ __global__ __launch_bounds__(256) void k_reduce_split(float* __restrict__ Y,
 // ---------------------------------------------------------------- router
 // Router logits through the same tiled kernel: one group of T rows,
 // part[z][t][e] = sum over K-split z of X[t] . Wg[e].  Used when E is a
-// multiple of 128; the select kernel sums the splits in order.
+// multiple of 64; the select kernel sums the splits in order.
 __global__ void k_set_range(int32_t* __restrict__ off, int n) {
   off[0] = 0;
   off[1] = n;
 }
 
+static int router_bn(int E) { return E % 256 == 0 ? 256 : E % 128 == 0 ? 128 : 64; }
+
 bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split) {
   // row offsets inside the kernel are 32-bit element offsets: T * d < 2^31
-  return dtype == MOE_BF16 && T >= 256 && T * (int64_t)d < ((int64_t)1 << 31) && E % 128 == 0 &&
-         E / 128 < 16384 && split >= 1 && split < 256 && d % split == 0 && (d / split) % 128 == 0;
+  return dtype == MOE_BF16 && T >= 256 && T * (int64_t)d < ((int64_t)1 << 31) && E % 64 == 0 &&
+         E / 64 < 16384 && split >= 1 && split < 256 && d % split == 0 && (d / split) % 128 == 0;
 }
 
+int router_gemm_tiles(int64_t T, int E) { return (int)MOE_CEIL_DIV(T, 128) * (E / router_bn(E)); }
+
 size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split) {
-  const int bn = E % 256 == 0 ? 256 : 128;
+  const int bn = router_bn(E);
   return align256(2 * sizeof(int32_t)) +
          align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2)) +
          align256(sizeof(int32_t));
@@ -854,7 +858,7 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
                               float* part, void* ws, hipStream_t s) {
   char* q = (char*)ws;
   int32_t* off = (int32_t*)q;  q += align256(2 * sizeof(int32_t));
-  const int bn = E % 256 == 0 ? 256 : 128;
+  const int bn = router_bn(E);
   int2* work = (int2*)q;       q += align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2));
   int32_t* nwork = (int32_t*)q;
   hipLaunchKernelGGL(k_set_range, dim3(1), dim3(1), 0, s, off, (int)T);
@@ -863,7 +867,8 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
              split, part + (size_t)T * E};
   run_work_list(a, 128, bn, false, s);
   if (bn == 256) run_gemm_dma<128, 256, 2, 2, false, 128, 3>(a, s);
-  else run_gemm_dma<128, 128, 2, 2, false, 128, 3>(a, s);
+  else if (bn == 128) run_gemm_dma<128, 128, 2, 2, false, 128, 3>(a, s);
+  else run_gemm_dma<128, 64, 2, 2, false, 128, 3>(a, s);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ namespace moe {
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // router.hip
-int router_split(int d);
+int router_split(int64_t T, int d, int E, int dtype);
 size_t route_ws_bytes(int64_t T, int d, int E);
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
                         const float* bias, const float* offset, int score, int k, int renorm,
@@ -31,9 +31,10 @@ hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_
 // gemm.hip
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype);
 int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype);
-// Router logits on the tiled GEMM kernel (bf16, E a multiple of 128):
+// Router logits on the tiled GEMM kernel (bf16, E a multiple of 64):
 // part[z][T][E] for the `split` K-splits z.
 bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split);
+int router_gemm_tiles(int64_t T, int E);
 size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split);
 hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, int E, int split,
                               float* part, void* ws, hipStream_t s);

@@ -14,16 +14,17 @@ namespace moe {
 // Logits GEMM: part[z][t][e] = sum_{i in slice z} X[t][i] * Wg[e][i].
 // One wave owns a 16-token x 16-expert MFMA block and walks its d-slice,
 // reading both operands straight from global memory (each lane pulls 16 B of
-// a row; X is read once per expert group, Wg stays in L2).  Split-K slices
-// keep >= several thousand waves in flight for the skinny E = 8 / 64 cases.
+// a row; Wg stays in L2).  The four waves of a block cover wpt = min(4,
+// ceil(E/16)) expert blocks of 4/wpt token groups, so small E still keeps
+// every wave busy; split-K slices add parallelism.
 template <typename T>
 __global__ __launch_bounds__(256) void k_router_logits(
     const T* __restrict__ X, const T* __restrict__ Wg, float* __restrict__ part,
-    int T_, int d, int E, int dchunk) {
+    int T_, int d, int E, int dchunk, int wpt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = blockIdx.y * 64 + wave * 16;
+  const int e0 = blockIdx.y * 16 * wpt + (wave % wpt) * 16;
   if (e0 >= E) return;                       // no block-level sync below
-  const int t0 = blockIdx.x * 16;
+  const int t0 = (blockIdx.x * (4 / wpt) + wave / wpt) * 16;
   const int z = blockIdx.z;
   const int kb = z * dchunk, ke = min(d, kb + dchunk);
   const int row = lane & 15, grp = lane >> 4;       // 4 lane groups along K
@@ -202,13 +203,25 @@ __global__ __launch_bounds__(256) void k_balance(const int32_t* __restrict__ cou
 }
 
 // --------------------------------------------------------------- launchers
-int router_split(int d) {
+// K-split of the logits: about one slice per 1024 of d.  On the tiled-GEMM
+// path it is doubled while that leaves fewer tiles than CUs, slices stay
+// multiples of 128 elements and the partial logits the select pass reads
+// stay small (<= 16 MB).
+int router_split(int64_t T, int d, int E, int dtype) {
   int s = d / 1024;
-  return s < 1 ? 1 : (s > 8 ? 8 : s);
+  s = s < 1 ? 1 : (s > 8 ? 8 : s);
+  if (router_gemm_ok(dtype, T, d, E, s)) {
+    while ((int64_t)router_gemm_tiles(T, E) * s < 256 && s * 2 <= 16 && d % (2 * s) == 0 &&
+           (d / (2 * s)) % 128 == 0 && 2 * s * T * (int64_t)E * 4 <= ((int64_t)16 << 20))
+      s *= 2;
+  }
+  return s;
 }
 
+// Sized for the larger split of the two dtypes, so one size serves both.
 size_t route_ws_bytes(int64_t T, int d, int E) {
-  const size_t split = (size_t)router_split(d);
+  const int s0 = router_split(T, d, E, MOE_BF16), s1 = router_split(T, d, E, MOE_F32);
+  const size_t split = (size_t)(s0 > s1 ? s0 : s1);
   size_t b = align256(split * (size_t)T * E * sizeof(float));      // partial logits
   b += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));   // prob_sum partials
   b += router_gemm_ws_bytes(T, d, E, (int)split);                    // tiled-GEMM work list
@@ -223,7 +236,7 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
   }
-  const int split = router_split(d);
+  const int split = router_split(T, d, E, dtype);
   const int kstep = 128;   // keep slices a multiple of both lane steps
   const int dchunk = MOE_CEIL_DIV(MOE_CEIL_DIV(d, split), kstep) * kstep;
   char* p = (char*)ws;
@@ -234,13 +247,15 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
     hipError_t e = launch_router_gemm(X, Wg, T, d, E, split, part, p, s);
     if (e != hipSuccess) return e;
   } else {
-    dim3 g1((unsigned)MOE_CEIL_DIV(T, 16), (unsigned)MOE_CEIL_DIV(E, 64), (unsigned)split);
+    const int wpt = E > 48 ? 4 : E > 16 ? 2 : 1;   // waves per token group (divides 4)
+    dim3 g1((unsigned)MOE_CEIL_DIV(T, 16 * (4 / wpt)), (unsigned)MOE_CEIL_DIV(E, 16 * wpt),
+            (unsigned)split);
     if (dtype == MOE_BF16)
       hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
-                         (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk);
+                         (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk, wpt);
     else
       hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
-                         (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk);
+                         (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk, wpt);
   }
   const int nblk = (int)MOE_CEIL_DIV(T, 4);
   float* psp = prob_sum ? ps_part : nullptr;
