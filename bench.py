@@ -43,19 +43,27 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def weight_elem_bytes(w):
+    from mixture_experts_layer_47_amd.workloads import weight_elem_bytes as web
+    return web(w)
+
+
 def up_kernel_work(w, counts_kept, n_kept):
     """Algorithmic work of one gate/up launch (real kept rows only).
 
     FLOPs = 2 * rows * d * 2F (gate and up projections).
-    Bytes = W1 + W3 of every expert that has rows (each read once)
+    Bytes = W1 + W3 of every expert that has rows (each read once; FP8
+            weights: one byte per element plus one fp32 scale per row)
           + the X rows the launch reads (T distinct tokens, each read once)
           + H written (rows * F).
     """
     es = 2 if w.dtype == "bf16" else 4
+    ew = weight_elem_bytes(w)
     rows = n_kept + (w.T if w.n_shared else 0)
     touched = int((counts_kept > 0).sum()) + (1 if w.n_shared else 0)
     flops = 4.0 * rows * w.d * w.F
-    bytes_ = touched * 2.0 * w.F * w.d * es + w.T * w.d * es + rows * w.F * es
+    wbytes = 2.0 * w.F * w.d * ew + (2.0 * w.F * 4 if w.wdtype == "fp8" else 0.0)
+    bytes_ = touched * wbytes + w.T * w.d * es + rows * w.F * es
     return flops, bytes_, touched, rows
 
 
@@ -71,14 +79,19 @@ def cpu_baseline(w, inp, target_s=15.0):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
 
-    def f64(t):
+    def f64(t, scale=None):
+        if t.dtype == torch.uint8:       # E4M3 codes: the oracle decodes them
+            return O.dequantize_rows(t.cpu().numpy(), scale.cpu().numpy())
         return t.detach().to("cpu", torch.float64).numpy()
     log("cpu baseline: copying weights to host (untimed)")
+    sc = inp.get("scales") or (None, None, None)
     Wg = f64(inp["Wg"]).T
-    W1 = f64(inp["W1"]).transpose(0, 2, 1)
-    W3 = f64(inp["W3"]).transpose(0, 2, 1)
-    W2 = f64(inp["W2"]).transpose(0, 2, 1)
-    sh = None if inp["shared"] is None else tuple(f64(t).T for t in inp["shared"])
+    W1 = f64(inp["W1"], sc[0]).transpose(0, 2, 1)
+    W3 = f64(inp["W3"], sc[1]).transpose(0, 2, 1)
+    W2 = f64(inp["W2"], sc[2]).transpose(0, 2, 1)
+    ss = inp.get("shared_scales") or (None, None, None)
+    sh = (None if inp["shared"] is None else
+          tuple(f64(t, q).T for t, q in zip(inp["shared"], ss)))
     bias = None if inp["bias"] is None else f64(inp["bias"])
     off = None if inp["offset"] is None else f64(inp["offset"])
     X = f64(inp["X"])
@@ -211,7 +224,8 @@ def main():
     # whole-layer roofline of the step for context
     layer_flops = 2.0 * w.T * w.d * w.E + 6.0 * rows * w.d * w.F
     es = 2 if w.dtype == "bf16" else 4
-    layer_bytes = touched * 3.0 * w.d * w.F * es + w.E * w.d * es + 2.0 * w.T * w.d * es
+    layer_bytes = (touched * 3.0 * w.d * w.F * weight_elem_bytes(w) + w.E * w.d * es
+                   + 2.0 * w.T * w.d * es)
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -220,6 +234,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) tokens, N(0,1/sqrt(fan_in)) "
                                   "random-init weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "expert_weights": "fp8 e4m3 + per-channel fp32 scales" if w.wdtype == "fp8"
+                   else w.dtype,
                    "n_shared": w.n_shared, "router": w.score, "capacity_factor": w.cf,
                    "parallelism": "single GPU"},
         "roofline": roof,

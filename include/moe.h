@@ -44,6 +44,9 @@ extern "C" {
 #endif
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+/* Expert-weight storage: the layer dtype, or FP8 E4M3 codes with one fp32
+ * scale per output channel (W = value(code) * scale; bf16 layers only). */
+enum moe_wtype { MOE_W_DTYPE = 0, MOE_W_FP8 = 1 };
 enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
 enum moe_status {
   MOE_OK = 0,
@@ -132,6 +135,20 @@ int moe_grouped_ffn(const void* A, const int32_t* row_token,
                     int64_t max_rows, float* Yrows, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* Same computation with FP8 expert weights (the DeepSeek-V3 weight format
+ * of LLM Internals 14.2.5's intensity model): A is bf16, W1/W3/W2 hold OCP
+ * FP8 E4M3 codes in the layout above, and every output channel has one fp32
+ * scale: W1_scale, W3_scale [G][F], W2_scale [G][d].  The weights used are
+ * value(code) * scale; codes are widened to bf16 exactly inside the kernel
+ * and the scales multiply the fp32 accumulators.  The workspace size is
+ * moe_grouped_ffn_workspace_size(max_rows, G, d, F, MOE_BF16). */
+int moe_grouped_ffn_fp8(const void* A, const int32_t* row_token,
+                        const int32_t* offsets, int G, const uint8_t* W1,
+                        const uint8_t* W3, const uint8_t* W2,
+                        const float* W1_scale, const float* W3_scale,
+                        const float* W2_scale, int d, int F, int64_t max_rows,
+                        float* Yrows, void* ws, size_t ws_bytes, void* stream);
+
 /* -------------------------------------------------------------- combine --
  * Combine (LLM Internals 14.2.1 step 6; AI Knowledge Map "MoE"
  * y = sum_{e in S} g_e E_e(x)):
@@ -170,6 +187,14 @@ typedef struct moe_layer {
   const void* Ws1;         /* shared expert [F][d], or NULL                  */
   const void* Ws3;         /* [F][d]                                         */
   const void* Ws2;         /* [d][F]                                         */
+  int wtype;               /* MOE_W_DTYPE, or MOE_W_FP8 (dtype MOE_BF16):
+                              W1..Ws2 then hold E4M3 codes with the scales: */
+  const float* W1_scale;   /* [E][F]                                         */
+  const float* W3_scale;   /* [E][F]                                         */
+  const float* W2_scale;   /* [E][d]                                         */
+  const float* Ws1_scale;  /* [F]  (shared expert)                           */
+  const float* Ws3_scale;  /* [F]                                            */
+  const float* Ws2_scale;  /* [d]                                            */
 } moe_layer;
 
 /* Optional device outputs of moe_forward; any member may be NULL. */

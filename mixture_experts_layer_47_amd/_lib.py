@@ -17,13 +17,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_W_DTYPE, MOE_W_FP8 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
           -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch",
-           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
+           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_fp8",
+           "moe_combine",
            "moe_balance", "moe_forward_workspace_size", "moe_forward", "moe_timing_enable",
            "moe_timing_read")
 
@@ -42,7 +44,11 @@ class MoeLayerC(ctypes.Structure):
                 ("Wg", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("logit_offset", ctypes.c_void_p), ("W1", ctypes.c_void_p),
                 ("W3", ctypes.c_void_p), ("W2", ctypes.c_void_p),
-                ("Ws1", ctypes.c_void_p), ("Ws3", ctypes.c_void_p), ("Ws2", ctypes.c_void_p)]
+                ("Ws1", ctypes.c_void_p), ("Ws3", ctypes.c_void_p), ("Ws2", ctypes.c_void_p),
+                ("wtype", ctypes.c_int),
+                ("W1_scale", ctypes.c_void_p), ("W3_scale", ctypes.c_void_p),
+                ("W2_scale", ctypes.c_void_p), ("Ws1_scale", ctypes.c_void_p),
+                ("Ws3_scale", ctypes.c_void_p), ("Ws2_scale", ctypes.c_void_p)]
 
 
 class MoeAuxC(ctypes.Structure):
@@ -65,6 +71,7 @@ def _declare(L):
         "moe_dispatch": (I, [P, I64, I, I, I64, P, P, P, P, P, P, I, I, P, P, SZ, P]),
         "moe_grouped_ffn_workspace_size": (SZ, [I64, I, I, I, I]),
         "moe_grouped_ffn": (I, [P, P, P, I, P, P, P, I, I, I, I64, P, P, SZ, P]),
+        "moe_grouped_ffn_fp8": (I, [P, P, P, I, P, P, P, P, P, P, I, I, I64, P, P, SZ, P]),
         "moe_combine": (I, [P, P, P, I64, I, I, P, P, I, P]),
         "moe_balance": (I, [P, P, I64, I, I, P, P]),
         "moe_forward_workspace_size": (SZ, [ctypes.POINTER(MoeLayerC), I64]),
@@ -175,15 +182,23 @@ def dispatch(ids, E, capacity=0, X=None):
     return out
 
 
-def grouped_ffn(A, offsets, W1, W3, W2, max_rows, row_token=None):
+def grouped_ffn(A, offsets, W1, W3, W2, max_rows, row_token=None, scales=None):
+    """Expert FFN rows; uint8 weights are E4M3 codes and need ``scales`` =
+    (W1_scale [G,F], W3_scale [G,F], W2_scale [G,d])."""
     G, F, d = W1.shape
     dev = A.device
     Y = torch.empty((max(int(max_rows), 1), d), dtype=torch.float32, device=dev)
     L = lib()
     ws = _workspace(L.moe_grouped_ffn_workspace_size(max_rows, G, d, F, _dtype_code(A)), dev)
-    _check(L.moe_grouped_ffn(_ptr(A), _ptr(row_token), _ptr(offsets), G, _ptr(W1), _ptr(W3),
-                             _ptr(W2), _dtype_code(A), d, F, int(max_rows), _ptr(Y), _ptr(ws),
-                             ws.numel(), _stream(dev)))
+    if W1.dtype == torch.uint8:
+        s1, s3, s2 = scales
+        _check(L.moe_grouped_ffn_fp8(_ptr(A), _ptr(row_token), _ptr(offsets), G, _ptr(W1),
+                                     _ptr(W3), _ptr(W2), _ptr(s1), _ptr(s3), _ptr(s2), d, F,
+                                     int(max_rows), _ptr(Y), _ptr(ws), ws.numel(), _stream(dev)))
+    else:
+        _check(L.moe_grouped_ffn(_ptr(A), _ptr(row_token), _ptr(offsets), G, _ptr(W1), _ptr(W3),
+                                 _ptr(W2), _dtype_code(A), d, F, int(max_rows), _ptr(Y),
+                                 _ptr(ws), ws.numel(), _stream(dev)))
     return Y[:max_rows]
 
 
@@ -219,15 +234,22 @@ class MoeLayer:
     offset: Optional[torch.Tensor] = None
     shared: Optional[tuple] = None
     capacity_factor: float = 0.0
+    scales: Optional[tuple] = None         # E4M3 weights: (W1_scale, W3_scale, W2_scale)
+    shared_scales: Optional[tuple] = None  # and the shared expert's three scale vectors
 
     def cstruct(self) -> MoeLayerC:
         E, F, d = self.W1.shape
         s = self.shared or (None, None, None)
+        fp8 = self.W1.dtype == torch.uint8
+        q = self.scales if fp8 else (None, None, None)
+        qs = self.shared_scales if (fp8 and self.shared) else (None, None, None)
         self._keep = MoeLayerC(
-            _dtype_code(self.W1), _score_code(self.score), int(bool(self.renorm)), d, E,
+            _dtype_code(self.Wg), _score_code(self.score), int(bool(self.renorm)), d, E,
             int(self.k), F, 1 if self.shared else 0, float(self.capacity_factor or 0.0),
             self.Wg.data_ptr(), _addr(self.bias), _addr(self.offset), self.W1.data_ptr(),
-            self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]))
+            self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]),
+            MOE_W_FP8 if fp8 else MOE_W_DTYPE, _addr(q[0]), _addr(q[1]), _addr(q[2]),
+            _addr(qs[0]), _addr(qs[1]), _addr(qs[2]))
         return self._keep
 
 
@@ -240,7 +262,8 @@ def layer_from_inputs(inp: dict) -> MoeLayer:
     w = inp["workload"]
     return MoeLayer(Wg=inp["Wg"], W1=inp["W1"], W3=inp["W3"], W2=inp["W2"], k=w.k,
                     score=w.score, renorm=w.renorm, bias=inp["bias"], offset=inp["offset"],
-                    shared=inp["shared"], capacity_factor=w.cf or 0.0)
+                    shared=inp["shared"], capacity_factor=w.cf or 0.0,
+                    scales=inp.get("scales"), shared_scales=inp.get("shared_scales"))
 
 
 class Forward:

@@ -190,6 +190,30 @@ int moe_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offs
                     "moe_grouped_ffn");
 }
 
+int moe_grouped_ffn_fp8(const void* A, const int32_t* row_token, const int32_t* offsets, int G,
+                        const uint8_t* W1, const uint8_t* W3, const uint8_t* W2,
+                        const float* W1_scale, const float* W3_scale, const float* W2_scale,
+                        int d, int F, int64_t max_rows, float* Yrows, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc;
+  MOE_REQUIRE(G >= 1 && G <= 1024, MOE_EUNSUPPORTED, "G = %d must be in [1, 1024]", G);
+  MOE_REQUIRE(max_rows >= 0 && max_rows <= INT32_MAX, MOE_EINVAL, "max_rows out of range");
+  MOE_REQUIRE(d > 0 && F > 0, MOE_EINVAL, "d and F must be positive");
+  MOE_REQUIRE(d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
+              "d = %d and F = %d must be multiples of 128", d, F);
+  MOE_REQUIRE(offsets != nullptr, MOE_EINVAL, "NULL offsets");
+  MOE_REQUIRE(max_rows == 0 || (A && W1 && W3 && W2 && Yrows), MOE_EINVAL,
+              "NULL A, W1, W3, W2 or Yrows");
+  MOE_REQUIRE(max_rows == 0 || (W1_scale && W3_scale && W2_scale), MOE_EINVAL,
+              "NULL weight scales");
+  if ((rc = check_ws(ws, ws_bytes, ffn_ws_bytes(max_rows, G, d, F, MOE_BF16)))) return rc;
+  const WeightScales q{W1_scale, W3_scale, W2_scale, nullptr, nullptr, nullptr};
+  return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
+                                       nullptr, -1, MOE_BF16, d, F, max_rows, Yrows, ws,
+                                       (hipStream_t)stream, true, nullptr, &q),
+                    "moe_grouped_ffn_fp8");
+}
+
 // ----------------------------------------------------------------- combine
 int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w, int64_t T,
                 int k, int d, const float* shared, void* Y, int dtype, void* stream) {
@@ -262,6 +286,14 @@ int check_layer(const moe_layer* L, int64_t T) {
               "a selection bias is only defined for the sigmoid router");
   MOE_REQUIRE(!(L->capacity_factor > 0) || isfinite(L->capacity_factor), MOE_EINVAL,
               "capacity factor must be finite");
+  MOE_REQUIRE(L->wtype == MOE_W_DTYPE || L->wtype == MOE_W_FP8, MOE_EINVAL, "wtype %d unknown",
+              L->wtype);
+  if (L->wtype == MOE_W_FP8) {
+    MOE_REQUIRE(L->dtype == MOE_BF16, MOE_EUNSUPPORTED, "FP8 weights need a bf16 layer");
+    MOE_REQUIRE(L->W1_scale && L->W3_scale && L->W2_scale, MOE_EINVAL, "NULL weight scales");
+    MOE_REQUIRE(!L->n_shared || (L->Ws1_scale && L->Ws3_scale && L->Ws2_scale), MOE_EINVAL,
+                "NULL shared-expert weight scales");
+  }
   return MOE_OK;
 }
 }  // namespace
@@ -315,10 +347,13 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   // itself, unless the caller asked for the expert rows (then they are
   // summed into Yrows first).
   const float* part2 = nullptr;
+  const WeightScales q{L->W1_scale, L->W3_scale, L->W2_scale, L->Ws1_scale, L->Ws3_scale,
+                       L->Ws2_scale};
   if (e == hipSuccess)
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
-                           w + o.ffn, s, a.Yrows != nullptr, &part2);
+                           w + o.ffn, s, a.Yrows != nullptr, &part2,
+                           L->wtype == MOE_W_FP8 ? &q : nullptr);
   if (e == hipSuccess)
     e = launch_combine(yrows, part2, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
                        L->dtype, s);

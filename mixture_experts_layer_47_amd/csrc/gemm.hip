@@ -34,6 +34,7 @@
 //     wave owns matching gate and up columns, and SwiGLU runs on the fp32
 //     accumulators before one rounding of h to the storage type.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -243,18 +244,28 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
 // formed from the tile's first row.
 //   GLU : out = H (type T), h = silu(gate) * up rounded once
 //   else: split 0 writes fp32 to out, split ks > 0 to slab ks - 1 of out2
-template <typename T, int BN, int BNT, int WN, int FM, int FN, bool GLU>
+// With SC (FP8 weights) the accumulators are first multiplied by the
+// per-output-channel scales: gate by sc0[n], up by sc1[n], down by sc0[n].
+template <typename T, int BN, int BNT, int WN, int FM, int FN, bool GLU, bool SC = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __restrict__ out,
                                            float* __restrict__ out2, int ks, int max_rows, int N,
                                            int rbeg, int rows, int arow0, int n0, int wn,
-                                           int lane) {
+                                           int lane, const float* __restrict__ sc0 = nullptr,
+                                           const float* __restrict__ sc1 = nullptr) {
   constexpr int FNH = GLU ? FN / 2 : FN;
   constexpr int WCOLS = BNT / WN;
   const int lrow0 = arow0 + (lane >> 5) * 4;          // this lane's first row
   const int rem = rows - lrow0;                        // rows this lane may store
   const size_t row0 = (size_t)(rbeg + lrow0);
   if constexpr (GLU) {
-    T* H = (T*)out + row0 * N + n0 + wn * (BN / WN) + (lane & 31);
+    const int c0 = n0 + wn * (BN / WN) + (lane & 31);
+    float sg[FNH], su[FNH];
+#pragma unroll
+    for (int j = 0; j < FNH; ++j) {
+      sg[j] = SC ? sc0[c0 + j * 32] : 1.f;
+      su[j] = SC ? sc1[c0 + j * 32] : 1.f;
+    }
+    T* H = (T*)out + row0 * N + c0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -263,14 +274,19 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __
         if (off < rem) {
 #pragma unroll
           for (int j = 0; j < FNH; ++j) {
-            const float h = silu_f(acc[i][j][r]) * acc[i][j + FNH][r];
-            store_h<T>(H + (size_t)off * N + j * 32, h);
+            const float g = SC ? acc[i][j][r] * sg[j] : acc[i][j][r];
+            const float u = SC ? acc[i][j + FNH][r] * su[j] : acc[i][j + FNH][r];
+            store_h<T>(H + (size_t)off * N + j * 32, silu_f(g) * u);
           }
         }
       }
   } else {
+    const int c0 = n0 + wn * WCOLS + (lane & 31);
+    float sy[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sy[j] = SC ? sc0[c0 + j * 32] : 1.f;
     float* Yb = ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N;
-    float* Y = Yb + row0 * N + n0 + wn * WCOLS + (lane & 31);
+    float* Y = Yb + row0 * N + c0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -278,7 +294,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __
         const int off = i * 32 + (r >> 2) * 8 + (r & 3);
         if (off < rem) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) Y[(size_t)off * N + j * 32] = acc[i][j][r];
+          for (int j = 0; j < FN; ++j)
+            Y[(size_t)off * N + j * 32] = SC ? acc[i][j][r] * sy[j] : acc[i][j][r];
         }
       }
   }
@@ -390,15 +407,18 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 }
 
 // ------------------------------------------------------- LDS-DMA variant
-// bf16 tiles with BM, BNT multiples of 64.  A stage holds KB bytes of every
-// A and B row (KB = 64: 32 K-elements, KB = 128: 64); NBUF stages live in a
-// ring of distinct LDS arrays.  global_load_lds moves 16 B per lane from
-// global memory straight into LDS (lane L of one wave instruction fills
-// bytes [16 L, 16 L + 16) of a 1 KB block = 1024 / KB rows), so stages never
-// pass through registers.  LDS row r keeps chunk c (16 B) at slot
-// c ^ swz(r); the lane that fills a slot fetches the matching chunk, and
-// the 16-B fragment reads are bank-conflict free for 8- and 16-lane LDS
-// service.
+// bf16 activations, bf16 or FP8 (E4M3) weights; tiles with BM, BNT multiples
+// of 32.  A stage covers 64 K-elements (KB = 128) or 32 (KB = 64): KB bytes of
+// every A row and, for bf16 weights, of every B row (KB / 2 bytes for FP8).
+// NBUF stages live in a ring of distinct LDS arrays.  global_load_lds moves
+// 16 B per lane from global memory straight into LDS (lane L of one wave
+// instruction fills bytes [16 L, 16 L + 16) of a 1 KB block = 1024 / rowbytes
+// rows), so stages never pass through registers.  LDS row r keeps chunk c
+// (16 B) at slot c ^ swz(r); the lane that fills a slot fetches the matching
+// chunk, and the fragment reads are bank-conflict free for 8- and 16-lane
+// LDS service.  FP8 fragments (8 bytes per lane) are widened to bf16 in
+// registers (exact: every E4M3 value is a bf16 value); the per-output-channel
+// scales are applied to the fp32 accumulators in the epilogue.
 //
 // Iteration s (stage s in buffer s mod NBUF):
 //   wait until this wave's copies of stage s have landed (those of the
@@ -409,10 +429,11 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 //   per k16 substep: MFMA the previous substep's fragments | read this one's
 // Copies past the last stage re-fetch it (in bounds, never read), so every
 // wave always has the same number of copies in flight.
-template <int KB>
-__device__ __forceinline__ int swz_kb(int r) {
-  if constexpr (KB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
-  else return swz(r);
+template <int RB>
+__device__ __forceinline__ int swz_rb(int r) {       // RB = row bytes per stage
+  if constexpr (RB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  else if constexpr (RB == 128) return swz(r);
+  else return r & 15;                                // 256-B rows span all banks
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
@@ -423,32 +444,67 @@ __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Copies of one stage: instruction i of wave w fills A rows (w CA + i) RPI ..
-// + RPI and B rows BM + (w CB + i) RPI .. + RPI of the buffer.
-// pa[i], pb[i]: this lane's source of copy instruction i at stage 0.
-template <int BM, int CA, int CB, int KB>
-__device__ __forceinline__ void dma_stage(u32x4* buf, const uint16_t* const (&pa)[CA],
-                                          const uint16_t* const (&pb)[CB], int koff, int wave) {
-  constexpr int CPR = KB / 16, RPI = 64 / CPR;
+// Geometry of one stage.  A rows hold KB bytes (bf16), B rows KB or KB / 2.
+template <int BM, int BNT, int KB, bool Q8>
+struct StageGeo {
+  static constexpr int RBA = KB, RBB = Q8 ? KB / 2 : KB;        // row bytes
+  static constexpr int CPA = RBA / 16, CPB = RBB / 16;          // 16-B chunks per row
+  static constexpr int RPA = 64 / CPA, RPB = 64 / CPB;          // rows per copy instruction
+  static constexpr int CA = BM / (4 * RPA), CB = BNT / (4 * RPB);   // copies per wave
+  static constexpr int BOFF = BM * CPA;                          // first B slot
+  static constexpr int SZ = BM * CPA + BNT * CPB;                // 16-B slots per stage
+};
+
+// Copies of one stage: instruction i of wave w fills A rows (w CA + i) RPA ..
+// + RPA and B rows (w CB + i) RPB .. + RPB of the buffer.  pa[i], pb[i]: this
+// lane's source of copy i at stage 0; koff is the stage's first K element.
+template <int BM, int BNT, int KB, bool Q8, typename TB>
+__device__ __forceinline__ void dma_stage(u32x4* buf,
+                                          const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
+                                          const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                          int koff, int wave) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
 #pragma unroll
-  for (int i = 0; i < CA; ++i)
+  for (int i = 0; i < G::CA; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
-                                     (void*)(buf + ((wave * CA + i) * RPI) * CPR), 16, 0, 0);
+                                     (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA), 16,
+                                     0, 0);
 #pragma unroll
-  for (int i = 0; i < CB; ++i)
+  for (int i = 0; i < G::CB; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(pb[i] + koff),
-                                     (void*)(buf + (BM + (wave * CB + i) * RPI) * CPR), 16, 0, 0);
+                                     (void*)(buf + G::BOFF + ((wave * G::CB + i) * G::RPB) * G::CPB),
+                                     16, 0, 0);
 }
 
-template <int NA, int FM, int FN, int BN, bool GLU, int CPR>
-__device__ __forceinline__ void load_frags_kb(u32x4* f, const u32x4* pa, const u32x4* pb, int cs) {
+// Eight E4M3 bytes -> eight bf16 in MFMA operand order (byte i is element i),
+// two per v_cvt_scalef32_pk_bf16_fp8 with scale 1 (exact: every E4M3 value
+// is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ u32x4 widen_e4m3(uint2 v) {
+  return u32x4{e4m3x2_bf16x2<false>(v.x), e4m3x2_bf16x2<true>(v.x), e4m3x2_bf16x2<false>(v.y),
+               e4m3x2_bf16x2<true>(v.y)};
+}
+
+// Fragments of k16 substep q.  A (and bf16 B) reads are 16 B at slot cs; FP8
+// B reads are 8 B: half (lane / 32) of chunk q at slot csb.
+template <int NA, int FM, int FN, int BN, bool GLU, int CPA, int CPB, bool Q8>
+__device__ __forceinline__ void load_frags_dma(u32x4* f, const u32x4* pa, const u32x4* pb,
+                                               int cs, int csb, int half) {
   constexpr int FNH = GLU ? FN / 2 : FN;
 #pragma unroll
-  for (int i = 0; i < NA; ++i) f[i] = pa[i * 32 * CPR + cs];
+  for (int i = 0; i < NA; ++i) f[i] = pa[i * 32 * CPA + cs];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int rr = GLU ? ((j < FNH) ? j * 32 : BN + (j - FNH) * 32) : j * 32;
-    f[FM + j] = pb[rr * CPR + cs];
+    if constexpr (Q8) {
+      const uint2 v = *((const uint2*)(pb + rr * CPB + csb) + half);
+      f[FM + j] = widen_e4m3(v);
+    } else {
+      f[FM + j] = pb[rr * CPB + cs];
+    }
   }
 }
 
@@ -459,33 +515,51 @@ __device__ __forceinline__ u32x4* ring(int h, const Ring& r) {
   return h == 0 ? r.b0 : h == 1 ? r.b1 : h == 2 ? r.b2 : h == 3 ? r.b3 : h == 4 ? r.b4 : r.b5;
 }
 
+// Per-lane fragment addressing: A rows fa + 32 i, B rows fb + rr (both in
+// slots of their region), swizzled chunk per substep.
+struct FragAddr {
+  int fa, fb, half;
+  int cs[8], csb[8];
+};
+
 // MFMAs and fragment reads of one stage held in `cur`: per k16 substep, MFMA
 // the previous substep's fragments while reading this one's.
-template <int NV, int BN, int CA, int CB, int FM, int FN, bool GLU, int KB>
+template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, bool Q8>
 __device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cur,
-                                          u32x4 (&f0)[FM + FN], u32x4 (&f1)[FM + FN], int fa,
-                                          int fb, const int (&cs)[4], bool with_copies) {
-  constexpr int CPR = KB / 16;
-  constexpr int NSUB = KB / 32;
+                                          u32x4 (&f0)[FM + FN], u32x4 (&f1)[FM + FN],
+                                          const FragAddr& fr, bool with_copies) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
+  constexpr int NSUB = KB / 32;              // k16 substeps per stage
+  const u32x4* pa = cur + fr.fa;
+  const u32x4* pb = cur + G::BOFF + fr.fb;
 #pragma unroll
   for (int q = 0; q < NSUB; q += 2) {
-    load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f0, cur + fa, cur + fb, cs[q]);
+    load_frags_dma<NV, FM, FN, BN, GLU, G::CPA, G::CPB, Q8>(f0, pa, pb, fr.cs[q], fr.csb[q],
+                                                             fr.half);
     mma_substep<uint16_t, NV, FM, FN>(acc, f1);
-    load_frags_kb<NV, FM, FN, BN, GLU, CPR>(f1, cur + fa, cur + fb, cs[q + 1]);
+    load_frags_dma<NV, FM, FN, BN, GLU, G::CPA, G::CPB, Q8>(f1, pa, pb, fr.cs[q + 1],
+                                                             fr.csb[q + 1], fr.half);
     mma_substep<uint16_t, NV, FM, FN>(acc, f0);
   }
   constexpr int NM = NV * FN;
   constexpr int ND = NV + FN;
-  constexpr int NG = CA + CB;
+  constexpr int NG = G::CA + G::CB;
   if (with_copies) {
     if constexpr (NSUB == 2) {
       sched_substep<NM, ND, NG, 0>();
       sched_substep<NM, ND, 0, 0>();
-    } else {
+    } else if constexpr (NSUB == 4) {
       sched_substep<NM, ND, NG / 2, 0>();
       sched_substep<NM, ND, NG - NG / 2, 0>();
       sched_substep<NM, ND, 0, 0>();
       sched_substep<NM, ND, 0, 0>();
+    } else {                                 // 8 substeps: copies over the first four
+      sched_substep<NM, ND, NG / 4, 0>();
+      sched_substep<NM, ND, NG / 4, 0>();
+      sched_substep<NM, ND, NG / 4, 0>();
+      sched_substep<NM, ND, NG - 3 * (NG / 4), 0>();
+#pragma unroll
+      for (int q = 4; q < NSUB; ++q) sched_substep<NM, ND, 0, 0>();
     }
   } else {
 #pragma unroll
@@ -493,20 +567,22 @@ __device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cu
   }
 }
 
-template <int NV, int BM, int BN, int CA, int CB, int FM, int FN, bool GLU, int KB, int NBUF>
+template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBUF, bool Q8,
+          typename TB>
 __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring& rb,
-                                              const uint16_t* const (&pa)[CA],
-                                              const uint16_t* const (&pb)[CB], int nk, int fa,
-                                              int fb, const int (&cs)[4], int wave) {
+                                              const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
+                                              const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                              int nk, const FragAddr& fr, int wave) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
   constexpr int NF = FM + FN;
   constexpr int BK = KB / 2;                 // K-elements per stage
   // The last buffer first receives a throw-away copy (stage 0 again), so the
   // copies in flight when the loop is entered target the same buffers, in
   // the same order, as at the end of every loop iteration.
-  dma_stage<BM, CA, CB, KB>(ring(NBUF - 1, rb), pa, pb, 0, wave);
+  dma_stage<BM, BNT, KB, Q8, TB>(ring(NBUF - 1, rb), pa, pb, 0, wave);
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
-    dma_stage<BM, CA, CB, KB>(ring(p, rb), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
+    dma_stage<BM, BNT, KB, Q8, TB>(ring(p, rb), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
   u32x4 f0[NF], f1[NF];
 #pragma unroll
   for (int x = 0; x < NF; ++x) f1[x] = u32x4{0u, 0u, 0u, 0u};
@@ -515,13 +591,13 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
 #pragma unroll
     for (int h = 0; h < NBUF; ++h) {
       const int s = s0 + h;
-      wait_vm_lgkm<(NBUF - 2) * (CA + CB)>();
+      wait_vm_lgkm<(NBUF - 2) * (G::CA + G::CB)>();
       __builtin_amdgcn_s_barrier();
       const int t = s + NBUF - 1;
-      dma_stage<BM, CA, CB, KB>(ring((h + NBUF - 1) % NBUF, rb), pa, pb,
-                                (t < nk ? t : nk - 1) * BK, wave);
+      dma_stage<BM, BNT, KB, Q8, TB>(ring((h + NBUF - 1) % NBUF, rb), pa, pb,
+                                     (t < nk ? t : nk - 1) * BK, wave);
       if constexpr (NV > 0)
-        stage_mma<NV, BN, CA, CB, FM, FN, GLU, KB>(acc, ring(h, rb), f0, f1, fa, fb, cs, true);
+        stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(h, rb), f0, f1, fr, true);
     }
   }
   // Tail (nk mod NBUF stages): their copies were all started inside the loop
@@ -534,32 +610,39 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
 #pragma unroll
       for (int c = 0; c < NBUF; ++c)
         if (h == c)
-          stage_mma<NV, BN, CA, CB, FM, FN, GLU, KB>(acc, ring(c, rb), f0, f1, fa, fb, cs, false);
+          stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(c, rb), f0, f1, fr, false);
     }
   }
   if constexpr (NV > 0) mma_substep<uint16_t, NV, FM, FN>(acc, f1);
   wait_vm_lgkm<0>();   // no copy may still be landing when the block ends
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF>
+// TB = uint16_t (bf16 weights) or uint8_t (E4M3 weights, Q8, with scales
+// sc0/sc1 [G][N] and sc0l/sc1l [N] for group g_last).
+template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8>
 __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
-    const int32_t* __restrict__ nwork, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B0_last,
-    const uint16_t* __restrict__ B1_last, int g_last, int K, int N, int max_rows, int ksplit,
-    int round, void* __restrict__ out, float* __restrict__ out2) {
+    const int32_t* __restrict__ nwork, const void* __restrict__ B0v,
+    const void* __restrict__ B1v, const void* __restrict__ B0lv,
+    const void* __restrict__ B1lv, int g_last, int K, int N, int max_rows, int ksplit,
+    int round, void* __restrict__ out, float* __restrict__ out2,
+    const float* __restrict__ sc0, const float* __restrict__ sc1,
+    const float* __restrict__ sc0l, const float* __restrict__ sc1l) {
   using T = uint16_t;
+  using TB = typename std::conditional<Q8, uint8_t, uint16_t>::type;
   constexpr int BNT = GLU ? 2 * BN : BN;
-  constexpr int CPR = KB / 16, RPI = 64 / CPR;
-  constexpr int CA = BM / (4 * RPI), CB = BNT / (4 * RPI);   // copies per wave per stage
+  using G = StageGeo<BM, BNT, KB, Q8>;
   constexpr int WROWS = BM / WM, WCOLS = BNT / WN;
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
-  constexpr int SZ = (BM + BNT) * CPR;                       // 16-B slots per stage
-  static_assert(WM * WN == 4 && (KB == 64 || KB == 128), "four waves, 64- or 128-B rows");
+  static_assert(WM * WN == 4 && (KB == 64 || KB == 128 || (Q8 && KB == 256)) && (!Q8 || KB >= 128),
+                "four waves; A rows of 64 or 128 B (256 B with FP8 weights, whose rows are half)");
   static_assert(NBUF >= 2 && NBUF <= 6, "stage ring of 2..6 buffers");
-  static_assert(BM % (4 * RPI) == 0 && BNT % (4 * RPI) == 0 && FM >= 1 && FN >= 1 &&
-                (!GLU || FN % 2 == 0), "tile shape");
+  static_assert(G::CA >= 1 && G::CB >= 1 && BM % (4 * G::RPA) == 0 && BNT % (4 * G::RPB) == 0 &&
+                FM >= 1 && FN >= 1 && (!GLU || FN % 2 == 0), "tile shape");
+  // GLU: a copy instruction's rows never straddle the W1 / W3 halves
+  static_assert(!GLU || BN % G::RPB == 0, "gate/up halves split on copy rows");
+  constexpr int SZ = G::SZ;
   __shared__ u32x4 L0[SZ], L1[SZ], L2[NBUF > 2 ? SZ : 1], L3[NBUF > 3 ? SZ : 1],
       L4[NBUF > 4 ? SZ : 1], L5[NBUF > 5 ? SZ : 1];
   const Ring rb{L0, L1, L2, L3, L4, L5};
@@ -568,11 +651,15 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * WROWS;
-  const int fa = (arow0 + (lane & 31)) * CPR;
-  const int fb = (BM + (GLU ? wn * (BN / WN) : wn * WCOLS) + (lane & 31)) * CPR;
-  int cs[4];
+  FragAddr fr;
+  fr.fa = (arow0 + (lane & 31)) * G::CPA;
+  fr.fb = ((GLU ? wn * (BN / WN) : wn * WCOLS) + (lane & 31)) * G::CPB;
+  fr.half = lane >> 5;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) cs[q] = ((2 * q + (lane >> 5)) % CPR) ^ swz_kb<KB>(lane & 31);
+  for (int q = 0; q < 8; ++q) {
+    fr.cs[q] = ((2 * q + (lane >> 5)) % G::CPA) ^ swz_rb<G::RBA>(lane & 31);
+    fr.csb[q] = (q % G::CPB) ^ swz_rb<G::RBB>(lane & 31);
+  }
   const int cx = round >> 3;
   const int xi = blockIdx.x >> 3;
   const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
@@ -587,26 +674,28 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   const int gbeg = min(max(offsets[g], 0), max_rows);
   const int rbeg = gbeg + wi.y;
   const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
-  const T* w0 = ((g == g_last) ? B0_last : B0 + (size_t)g * N * K) + kbeg;
-  const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) + kbeg : nullptr;
+  const TB* B0 = (const TB*)B0v;
+  const TB* B1 = (const TB*)B1v;
+  const TB* w0 = ((g == g_last) ? (const TB*)B0lv : B0 + (size_t)g * N * K) + kbeg;
+  const TB* w1 = GLU ? ((g == g_last) ? (const TB*)B1lv : B1 + (size_t)g * N * K) + kbeg : nullptr;
 
-  // This lane's source of each copy: row (w C + i) RPI + lane / CPR of the
-  // tile, chunk (lane % CPR) ^ swz(row).  Rows past the tile's end re-read
-  // its first row: their outputs are never stored.
-  const int slot = lane % CPR;
-  const T* pa[CA];
+  // This lane's source of each copy: row (w C + i) RP + lane / CP of the
+  // tile, chunk (lane % CP) ^ swz(row).  Rows past the tile's end re-read its
+  // first row: their outputs are never stored.
+  const T* pa[G::CA];
 #pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int r = (wave * CA + i) * RPI + lane / CPR;
+  for (int i = 0; i < G::CA; ++i) {
+    const int r = (wave * G::CA + i) * G::RPA + lane / G::CPA;
     int src = rbeg + (r < rows ? r : 0);
     if (row_token) src = row_token[src];
-    pa[i] = A + (size_t)src * K + kbeg + ((slot ^ swz_kb<KB>(r & 31)) * 8);
+    pa[i] = A + (size_t)src * K + kbeg + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
   }
-  const T* pb[CB];
+  constexpr int EPC_B = 16 / sizeof(TB);             // B elements per 16-B chunk
+  const TB* pb[G::CB];
 #pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int r = (wave * CB + i) * RPI + lane / CPR;
-    const int c = (slot ^ swz_kb<KB>(r & 31)) * 8;
+  for (int i = 0; i < G::CB; ++i) {
+    const int r = (wave * G::CB + i) * G::RPB + lane / G::CPB;
+    const int c = ((lane % G::CPB) ^ swz_rb<G::RBB>(r & 31)) * EPC_B;
     if constexpr (GLU)
       pb[i] = (r < BN ? w0 + (size_t)(n0 + r) * K : w1 + (size_t)(n0 + r - BN) * K) + c;
     else
@@ -622,8 +711,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
-#define MOE_DMA_LOOP(NV_)                                                                   \
-  main_loop_dma<NV_, BM, BN, CA, CB, FM, FN, GLU, KB, NBUF>(acc, rb, pa, pb, nk, fa, fb, cs, wave)
+#define MOE_DMA_LOOP(NV_)                                                                     \
+  main_loop_dma<NV_, BM, BN, BNT, FM, FN, GLU, KB, NBUF, Q8, TB>(acc, rb, pa, pb, nk, fr, wave)
   if (nv >= FM) {
     MOE_DMA_LOOP(FM);
   } else if (nv == 0) {
@@ -636,8 +725,14 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     if constexpr (FM > 5) { if (nv == 5) MOE_DMA_LOOP(5); }
   }
 #undef MOE_DMA_LOOP
-  store_tile<T, BN, BNT, WN, FM, FN, GLU>(acc, out, out2, ks, max_rows, N, rbeg, rows, arow0, n0,
-                                          wn, lane);
+  const float* s0p = nullptr;
+  const float* s1p = nullptr;
+  if constexpr (Q8) {
+    s0p = (g == g_last) ? sc0l : sc0 + (size_t)g * N;
+    s1p = GLU ? ((g == g_last) ? sc1l : sc1 + (size_t)g * N) : nullptr;
+  }
+  store_tile<T, BN, BNT, WN, FM, FN, GLU, Q8>(acc, out, out2, ks, max_rows, N, rbeg, rows, arow0,
+                                              n0, wn, lane, s0p, s1p);
 }
 
 // Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
@@ -776,6 +871,7 @@ struct GemmArgs {
   int32_t* nwork;
   int ksplit;
   float* out2;
+  const float *sc0, *sc1, *sc0l, *sc1l;   // FP8 weights: per-output-channel scales
 };
 
 static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s) {
@@ -796,16 +892,16 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2>
+template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
-                     (const T*)a.B0, (const T*)a.B1, (const T*)a.B0l, (const T*)a.B1l, a.g_last,
-                     a.K, a.N, a.max_rows, a.ksplit, round, a.out, a.out2);
+                     a.B0, a.B1, a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
+                     a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
 }
 
 // Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
@@ -880,7 +976,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s, bool reduce, const float** partial2) {
+                              hipStream_t s, bool reduce, const float** partial2,
+                              const WeightScales* qs) {
   if (partial2) *partial2 = nullptr;
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
@@ -899,10 +996,37 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
               1,  nullptr};
   GemmArgs dn{H,  nullptr, offsets, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
               nwork + 1, ks, slabs};
+  if (qs) {
+    up.sc0 = qs->s1; up.sc1 = qs->s3; up.sc0l = qs->s1l; up.sc1l = qs->s3l;
+    dn.sc0 = qs->s2; dn.sc0l = qs->s2l;
+  }
   run_work_list(up, p.BM, up_bn(p.cfg), true, s);
   run_work_list(dn, p.BM, down_bn(p.cfg, d), false, s);
   timing_mark("tile_map", s);
-  if (dtype == MOE_BF16) {
+  if (qs) {
+    // FP8 weights: 256-row tiles keep 64-K stages (32 KB A + 16 KB B rows,
+    // three buffers); the others use 128-K stages (256-B A rows, 128-B weight
+    // rows: whole cache lines per copy) in two buffers of 64 / 72 KB.
+    switch (p.cfg) {
+      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 3, true>(up, s); break;
+      case 1: run_gemm_dma<128, 128, 2, 2, true, 256, 2, true>(up, s); break;
+      default: run_gemm_dma<32, 256, 1, 4, true, 256, 2, true>(up, s); break;
+    }
+    timing_mark("ffn_up", s);
+    const bool b256 = down_bn(p.cfg, d) == 256;
+    switch (p.cfg) {
+      case 0:
+        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 3, true>(dn, s);
+        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 3, true>(dn, s);
+        break;
+      case 1:
+        if (b256) run_gemm_dma<128, 256, 2, 2, false, 256, 2, true>(dn, s);
+        else run_gemm_dma<128, 128, 2, 2, false, 256, 2, true>(dn, s);
+        break;
+      default: run_gemm_dma<32, 256, 1, 4, false, 256, 2, true>(dn, s); break;
+    }
+    timing_mark("ffn_down", s);
+  } else if (dtype == MOE_BF16) {
     using T = uint16_t;
     switch (p.cfg) {
       case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true>(up, s); break;

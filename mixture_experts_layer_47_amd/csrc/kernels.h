@@ -38,14 +38,21 @@ int router_gemm_tiles(int64_t T, int E);
 size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split);
 hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, int E, int split,
                               float* part, void* ws, hipStream_t s);
+// Per-output-channel scales of FP8 (E4M3) weights: s1, s3 [G][F], s2 [G][d]
+// for the routed groups, s1l, s3l [F], s2l [d] for group g_last.
+struct WeightScales {
+  const float *s1, *s3, *s2, *s1l, *s3l, *s2l;
+};
 // The down projection may be split along K (ffn_down_split() > 1): then the
 // partial sums are summed into Yrows if `reduce`, else *partial2 receives the
 // second partial slab ([max_rows][d], to be added to Yrows by the caller).
+// q != NULL: W1/W3/W2 (and the g_last matrices) hold E4M3 codes, A is bf16.
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s, bool reduce, const float** partial2);
+                              hipStream_t s, bool reduce, const float** partial2,
+                              const WeightScales* q = nullptr);
 
 // combine.hip
 // Yrows2 (optional): second K-split partial of the rows, added to Yrows.

@@ -18,6 +18,12 @@ W_g ~ N(0, 1/sqrt(d)) unless the workload fixes another std; bias ~ N(0, std);
 all drawn in fp32, then rounded to bf16 (round-to-nearest-even) for bf16
 workloads.  The skewed-load workload adds o_e = -s * ln(r_e) with r a seeded
 random permutation of 1..E, i.e. expert popularity proportional to r^-s.
+
+FP8 workloads (wdtype "fp8") draw the same fp32 expert weights and store them
+as FP8 E4M3 codes with one fp32 scale per output channel (storage row):
+scale = max|row| / 448, code = E4M3(row / scale) rounded to nearest even
+(torch's float8_e4m3fn cast); "scales" holds (W1_scale [E,F], W3_scale [E,F],
+W2_scale [E,d]) and "shared_scales" the shared expert's three vectors.
 """
 from __future__ import annotations
 
@@ -43,6 +49,7 @@ class Workload:
     wg_std: float | None = None    # None -> 1/sqrt(d)
     bias_std: float | None = None  # sigmoid selection bias std, None = no bias
     zipf_s: float | None = None    # per-expert logit offset exponent
+    wdtype: str = "same"           # "same" | "fp8" (E4M3 expert weights, bf16 layer)
     seed: int = 0                  # seed of the weights
     x_seed: int | None = None      # seed of X (defaults to ``seed``)
     note: str = field(default="", compare=False)
@@ -77,6 +84,10 @@ WORKLOADS = {
 }
 WORKLOADS["switch_capacity_cf125"] = WORKLOADS["switch_capacity"].with_(
     name="switch_capacity_cf125", cf=1.25, note="Switch-style top-1, CF 1.25")
+# The same layers with FP8 E4M3 expert weights (per-output-channel scales).
+for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
+    WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", wdtype="fp8",
+                                                 note=WORKLOADS[_n].note + ", FP8 weights")
 
 # Reduced versions: same routing rule and dtype, sizes the CPU oracle finishes
 # in seconds, with several tiles per expert and ragged tails.
@@ -93,6 +104,8 @@ SMALL = {
     "switch_capacity_cf125": WORKLOADS["switch_capacity_cf125"].with_(
         name="switch_capacity_cf125_small", T=700, d=256, E=16, F=512),
 }
+for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
+    SMALL[_n + "_fp8"] = SMALL[_n].with_(name=SMALL[_n].name + "_fp8", wdtype="fp8")
 
 
 def _seed(*parts: int) -> int:
@@ -114,27 +127,56 @@ def _normal(shape, std, seed_parts, device, dtype):
 _X, _WG, _W1, _W3, _W2, _S1, _S3, _S2, _BIAS, _PERM = range(10)
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3_rows(t: torch.Tensor):
+    """fp32 [..., N, K] -> (uint8 E4M3 codes [..., N, K], fp32 scales [..., N])."""
+    amax = t.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    codes = (t / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale.to(torch.float32)
+
+
 def make_inputs(w: Workload, device="cpu") -> dict:
     """Draw every input of workload ``w`` on ``device`` (storage layout)."""
     dt = w.torch_dtype
     dev = torch.device(device)
+    fp8 = w.wdtype == "fp8"
+    if fp8 and w.dtype != "bf16":
+        raise ValueError("FP8 expert weights need a bf16 layer")
     xs = w.seed if w.x_seed is None else w.x_seed
     out = {"workload": w}
     out["X"] = _normal((w.T, w.d), 1.0, (xs, _X), dev, dt)
     wg_std = w.wg_std if w.wg_std is not None else 1.0 / np.sqrt(w.d)
     out["Wg"] = _normal((w.E, w.d), wg_std, (w.seed, _WG), dev, dt)
     s_in, s_out = 1.0 / np.sqrt(w.d), 1.0 / np.sqrt(w.F)
+    scales = []
     for name, tid, shp, std in (("W1", _W1, (w.F, w.d), s_in),
                                 ("W3", _W3, (w.F, w.d), s_in),
                                 ("W2", _W2, (w.d, w.F), s_out)):
-        t = torch.empty((w.E,) + shp, device=dev, dtype=dt)
+        t = torch.empty((w.E,) + shp, device=dev, dtype=torch.uint8 if fp8 else dt)
+        sc = torch.empty((w.E, shp[0]), device=dev, dtype=torch.float32) if fp8 else None
         for e in range(w.E):            # one expert at a time bounds the fp32 temp
-            t[e] = _normal(shp, std, (w.seed, tid, e), dev, dt)
+            if fp8:
+                t[e], sc[e] = quantize_e4m3_rows(
+                    _normal(shp, std, (w.seed, tid, e), dev, torch.float32))
+            else:
+                t[e] = _normal(shp, std, (w.seed, tid, e), dev, dt)
         out[name] = t
+        scales.append(sc)
+    out["scales"] = tuple(scales) if fp8 else None
+    out["shared_scales"] = None
     if w.n_shared:
-        out["shared"] = (_normal((w.F, w.d), s_in, (w.seed, _S1), dev, dt),
-                         _normal((w.F, w.d), s_in, (w.seed, _S3), dev, dt),
-                         _normal((w.d, w.F), s_out, (w.seed, _S2), dev, dt))
+        shp3 = (((w.F, w.d), s_in, _S1), ((w.F, w.d), s_in, _S3), ((w.d, w.F), s_out, _S2))
+        if fp8:
+            q = [quantize_e4m3_rows(_normal(shp, std, (w.seed, tid), dev, torch.float32))
+                 for shp, std, tid in shp3]
+            out["shared"] = tuple(c for c, _ in q)
+            out["shared_scales"] = tuple(sc for _, sc in q)
+        else:
+            out["shared"] = tuple(_normal(shp, std, (w.seed, tid), dev, dt)
+                                  for shp, std, tid in shp3)
     else:
         out["shared"] = None
     out["bias"] = (None if w.bias_std is None else
@@ -150,7 +192,11 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     return out
 
 
+def weight_elem_bytes(w: Workload) -> int:
+    """Bytes per stored expert-weight element."""
+    return 1 if w.wdtype == "fp8" else (2 if w.dtype == "bf16" else 4)
+
+
 def weight_bytes(w: Workload) -> int:
-    """Bytes of all resident expert weights (routed + shared)."""
-    el = 2 if w.dtype == "bf16" else 4
-    return (w.E + w.n_shared) * 3 * w.d * w.F * el
+    """Bytes of all resident expert weights (routed + shared), scales excluded."""
+    return (w.E + w.n_shared) * 3 * w.d * w.F * weight_elem_bytes(w)

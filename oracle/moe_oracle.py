@@ -51,10 +51,15 @@ R9  bf16 mode: the activation h is rounded to bf16 (round-to-nearest-even)
     intermediates stay exact.
 R10 Shared expert: same width F, weight 1, added to every token's output.
 R11 Optional per-expert logit offset o_e is added to the logits before scoring.
+R12 FP8 expert weights (the format the DeepSeek-V3 weights are stored in,
+    [Book 14.2.5]): OCP FP8 E4M3 codes with one fp32 scale per output channel,
+    W = value(code) * scale.  The format itself is not spelled out on the
+    pages; its public definition is restated in decode_e4m3.
 
 Parity status: every function here is pinned by the CPU tests (worked examples
 printed on the pages, closed forms, brute force and cross-tier agreement).  The
-bf16 rounding of h (R9) is a reading, pinned only by its own RNE unit test.
+bf16 rounding of h (R9) is a reading, pinned only by its own RNE unit test; the
+E4M3 decode (R12) is pinned by closed-form codes and by a library decoder.
 """
 from __future__ import annotations
 
@@ -67,7 +72,7 @@ __all__ = [
     "capacity", "router_logits", "scores", "select_topk", "gates", "route",
     "dispatch", "silu", "round_bf16", "expert_ffn", "combine", "forward",
     "forward_token_loop", "forward_dense_masked", "balance_value",
-    "balance_stat", "expert_weight_shapes",
+    "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows",
 ]
 
 
@@ -217,6 +222,26 @@ def round_bf16(x):
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)              # x = m * 2**e, 0.5 <= |m| < 1
     return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def decode_e4m3(codes):
+    """Values of FP8 E4M3 codes (R12): bit 7 sign, bits 6-3 exponent with bias
+    7, bits 2-0 mantissa.  Exponent field 0 is subnormal, (m/8) * 2^-6; fields
+    1..15 are normal, (1 + m/8) * 2^(e-7), except S.1111.111, which is NaN.
+    There are no infinities; the largest finite magnitude is 448."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def dequantize_rows(codes, scale):
+    """W[..., n, :] = value(codes[..., n, :]) * scale[..., n] (R12): one scale
+    per output channel, i.e. per row of the reduction-contiguous storage."""
+    return decode_e4m3(codes) * np.asarray(scale, dtype=np.float64)[..., None]
 
 
 def expert_weight_shapes(d: int, F: int):

@@ -19,27 +19,40 @@ def np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def weights64(t, scale=None):
+    """Storage-layout weights as float64; E4M3 codes (uint8) are decoded by
+    the oracle and multiplied by their per-row scales."""
+    if t.dtype == torch.uint8:
+        return O.dequantize_rows(t.cpu().numpy(), scale.detach().cpu().numpy())
+    return np64(t)
+
+
 def logical(inp):
     """Oracle-side view of a workload's tensors (pages' logical shapes)."""
+    sc = inp.get("scales") or (None, None, None)
     out = {
         "X": np64(inp["X"]),
         "Wg": np64(inp["Wg"]).T,
-        "W1": np64(inp["W1"]).transpose(0, 2, 1),
-        "W3": np64(inp["W3"]).transpose(0, 2, 1),
-        "W2": np64(inp["W2"]).transpose(0, 2, 1),
+        "W1": weights64(inp["W1"], sc[0]).transpose(0, 2, 1),
+        "W3": weights64(inp["W3"], sc[1]).transpose(0, 2, 1),
+        "W2": weights64(inp["W2"], sc[2]).transpose(0, 2, 1),
         "bias": None if inp["bias"] is None else np64(inp["bias"]),
         "offset": None if inp["offset"] is None else np64(inp["offset"]),
         "shared": None,
     }
     if inp["shared"] is not None:
         s1, s3, s2 = inp["shared"]
-        out["shared"] = (np64(s1).T, np64(s3).T, np64(s2).T)
+        ss = inp.get("shared_scales") or (None, None, None)
+        out["shared"] = (weights64(s1, ss[0]).T, weights64(s3, ss[1]).T, weights64(s2, ss[2]).T)
     return out
 
 
 def expert_logical(inp, e):
     """One expert's logical matrices (W1 [d,F], W3 [d,F], W2 [F,d])."""
-    return (np64(inp["W1"][e]).T, np64(inp["W3"][e]).T, np64(inp["W2"][e]).T)
+    sc = inp.get("scales") or (None, None, None)
+    pick = (lambda i: None) if sc[0] is None else (lambda i: sc[i][e])
+    return (weights64(inp["W1"][e], pick(0)).T, weights64(inp["W3"][e], pick(1)).T,
+            weights64(inp["W2"][e], pick(2)).T)
 
 
 def rel_err(got, ref):

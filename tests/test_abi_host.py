@@ -19,7 +19,7 @@ ROOT = Path(__file__).resolve().parent.parent
 def _header_functions():
     text = (ROOT / "include" / "moe.h").read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")

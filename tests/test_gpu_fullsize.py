@@ -80,7 +80,8 @@ def test_fullsize_workload(name):
 
     # --- S: shared expert rows of sampled tokens
     if inp["shared"] is not None:
-        s1, s3, s2 = (H.np64(t).T for t in inp["shared"])
+        ss = inp.get("shared_scales") or (None, None, None)
+        s1, s3, s2 = (H.weights64(t, sc).T for t, sc in zip(inp["shared"], ss))
         ref = O.expert_ffn(xs, s1, s3, s2, bf16_h=bf16)
         got = H.np64(aux["Yrows"][torch.as_tensor(R + ts, device=DEV)])
         H.check_rows(got, ref, bf16, f"{name} shared rows")

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import mixture_experts_layer_47_amd as moe
-from mixture_experts_layer_47_amd.workloads import SMALL, Workload, make_inputs
+from mixture_experts_layer_47_amd.workloads import SMALL, Workload, make_inputs, quantize_e4m3_rows
 from oracle import moe_oracle as O
 from tests import parity_helpers as H
 
@@ -214,35 +214,46 @@ FFN_SHAPES = {
 }
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
 @pytest.mark.parametrize("use_row_token", [False, True])
 @pytest.mark.parametrize("shape", list(FFN_SHAPES))
 def test_grouped_ffn_entry_point(dtype, use_row_token, shape):
+    """bf16 / fp32 layers, and bf16 activations with E4M3 weights ("fp8")."""
     _announce(f"moe_grouped_ffn {shape} {dtype} row_token={use_row_token}")
     d, F, counts, slack = FFN_SHAPES[shape]
     G = len(counts)
     g = torch.Generator().manual_seed(5)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     T = 400
     X = torch.randn((T, d), generator=g).to(tdt)
-    W1 = (torch.randn((G, F, d), generator=g) / d ** 0.5).to(tdt)
-    W3 = (torch.randn((G, F, d), generator=g) / d ** 0.5).to(tdt)
-    W2 = (torch.randn((G, d, F), generator=g) / F ** 0.5).to(tdt)
+    Ws = [torch.randn((G, F, d), generator=g) / d ** 0.5,
+          torch.randn((G, F, d), generator=g) / d ** 0.5,
+          torch.randn((G, d, F), generator=g) / F ** 0.5]
+    if dtype == "fp8":
+        q = [quantize_e4m3_rows(w) for w in Ws]
+        dev_w = [c.to(DEV) for c, _ in q]
+        scales = tuple(sc.to(DEV) for _, sc in q)
+        ref_w = [O.dequantize_rows(c.numpy(), sc.numpy()) for c, sc in q]
+    else:
+        Ws = [w.to(tdt) for w in Ws]
+        dev_w = [w.to(DEV) for w in Ws]
+        scales = None
+        ref_w = [w.double().numpy() for w in Ws]
     R = sum(counts)
     offs = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32)
     tok = torch.randint(0, T, (R,), generator=g, dtype=torch.int32)
     A = X if use_row_token else X[tok.long()]
-    Y = moe.grouped_ffn(A.to(DEV), offs.to(DEV), W1.to(DEV), W3.to(DEV), W2.to(DEV), R + slack,
-                        row_token=tok.to(DEV) if use_row_token else None)
+    Y = moe.grouped_ffn(A.to(DEV), offs.to(DEV), *dev_w, R + slack,
+                        row_token=tok.to(DEV) if use_row_token else None, scales=scales)
     torch.cuda.synchronize()
     Xr = X[tok.long()].double().numpy()
+    bf16 = dtype != "f32"
     for e in range(G):
         a, b = int(offs[e]), int(offs[e + 1])
         if b == a:
             continue
-        ref = O.expert_ffn(Xr[a:b], W1[e].double().numpy().T, W3[e].double().numpy().T,
-                           W2[e].double().numpy().T, bf16_h=(dtype == "bf16"))
-        H.check_rows(H.np64(Y[a:b]), ref, dtype == "bf16")
+        ref = O.expert_ffn(Xr[a:b], ref_w[0][e].T, ref_w[1][e].T, ref_w[2][e].T, bf16_h=bf16)
+        H.check_rows(H.np64(Y[a:b]), ref, bf16)
 
 
 def test_forward_ksplit_paths_agree():

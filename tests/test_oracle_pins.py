@@ -398,3 +398,39 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_drop_six_token_example()
     monkeypatch.setattr(O, "dispatch", good_disp)
+
+
+# ------------------------------------------------------------- FP8 weights --
+def test_e4m3_closed_forms():
+    v = O.decode_e4m3
+    assert v(0x00) == 0.0 and v(0x80) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert v(0x01) == 2.0 ** -9                    # smallest subnormal
+    assert v(0x07) == 7 * 2.0 ** -9                # largest subnormal
+    assert v(0x08) == 2.0 ** -6                    # smallest normal
+    assert v(0x38) == 1.0 and v(0x40) == 2.0 and v(0x3C) == 1.5
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0  # largest finite
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+
+
+def test_e4m3_matches_library_decoder():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # positive finite codes are strictly increasing
+    assert (np.diff(got[:0x7F]) > 0).all()
+
+
+def test_dequantize_rows_scales_output_channels():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 256, size=(3, 5, 7)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10           # no NaN codes
+    scale = rng.uniform(0.5, 2.0, size=(3, 5))
+    W = O.dequantize_rows(codes, scale)
+    assert W.shape == (3, 5, 7)
+    for e in range(3):
+        for n in range(5):
+            assert np.array_equal(W[e, n], O.decode_e4m3(codes[e, n]) * scale[e, n])
