@@ -398,6 +398,12 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_drop_six_token_example()
     monkeypatch.setattr(O, "dispatch", good_disp)
+    # 7. E4M3 exponent bias off by one
+    good_dec = O.decode_e4m3
+    monkeypatch.setattr(O, "decode_e4m3", lambda c: good_dec(c) * 2.0)
+    with pytest.raises(AssertionError):
+        test_e4m3_closed_forms()
+    monkeypatch.setattr(O, "decode_e4m3", good_dec)
 
 
 # ------------------------------------------------------------- FP8 weights --
