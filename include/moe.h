@@ -78,6 +78,16 @@ int64_t moe_capacity(double cf, int64_t N, int k, int E);
  *                    MOE_SIGMOID: s = sigmoid(l) per cell; the key is s + b,
  *                    evaluated in fp64; the gate uses the raw s.
  *   renorm           1: gates g_e / sum_{chosen} g; 0: the raw p or s.
+ *   n_group, topk_group  group-limited routing (LLM Internals 14.2.3,
+ *                    node-limited routing with groups of experts standing in
+ *                    for nodes): n_group <= 1 disables it.  Otherwise E is
+ *                    split into n_group groups of E / n_group consecutive
+ *                    experts; a group's score is the sum of its
+ *                    max(1, k / topk_group) highest affinities (p, or s
+ *                    without the bias); only the topk_group best groups
+ *                    (lower id on ties) are eligible for the top-k.  Needs
+ *                    E % n_group == 0, n_group <= 64, 1 <= topk_group <=
+ *                    n_group and k <= topk_group * E / n_group.
  * Outputs (device):
  *   logits[T][E]     fp32 logits (with the offset) or NULL
  *   topk_ids[T][k]   int32, key descending, ties to the lower expert id
@@ -87,9 +97,9 @@ int64_t moe_capacity(double cf, int64_t N, int k, int E);
 size_t moe_route_workspace_size(int64_t T, int d, int E);
 int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
               int E, const float* bias, const float* logit_offset, int score,
-              int k, int renorm, float* logits, int32_t* topk_ids,
-              float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
-              void* stream);
+              int k, int renorm, int n_group, int topk_group, float* logits,
+              int32_t* topk_ids, float* topk_w, float* prob_sum, void* ws,
+              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------- dispatch --
  * Dispatch permutation with an optional capacity drop (LLM Internals 14.2.1
@@ -195,6 +205,8 @@ typedef struct moe_layer {
   const float* Ws1_scale;  /* [F]  (shared expert)                           */
   const float* Ws3_scale;  /* [F]                                            */
   const float* Ws2_scale;  /* [d]                                            */
+  int n_group;             /* group-limited routing as in moe_route; <= 1 off */
+  int topk_group;
 } moe_layer;
 
 /* Optional device outputs of moe_forward; any member may be NULL. */

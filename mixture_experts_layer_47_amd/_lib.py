@@ -48,7 +48,8 @@ class MoeLayerC(ctypes.Structure):
                 ("wtype", ctypes.c_int),
                 ("W1_scale", ctypes.c_void_p), ("W3_scale", ctypes.c_void_p),
                 ("W2_scale", ctypes.c_void_p), ("Ws1_scale", ctypes.c_void_p),
-                ("Ws3_scale", ctypes.c_void_p), ("Ws2_scale", ctypes.c_void_p)]
+                ("Ws3_scale", ctypes.c_void_p), ("Ws2_scale", ctypes.c_void_p),
+                ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int)]
 
 
 class MoeAuxC(ctypes.Structure):
@@ -66,7 +67,7 @@ def _declare(L):
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_capacity": (I64, [D, I64, I, I]),
         "moe_route_workspace_size": (SZ, [I64, I, I]),
-        "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_dispatch_workspace_size": (SZ, [I64, I, I]),
         "moe_dispatch": (I, [P, I64, I, I, I64, P, P, P, P, P, P, I, I, P, P, SZ, P]),
         "moe_grouped_ffn_workspace_size": (SZ, [I64, I, I, I, I]),
@@ -144,7 +145,7 @@ def capacity(cf: float, N: int, k: int, E: int) -> int:
 
 
 def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
-          want_logits=True, want_prob_sum=True):
+          want_logits=True, want_prob_sum=True, n_group=1, topk_group=1):
     T, d = X.shape
     E = Wg.shape[0]
     dev = X.device
@@ -156,7 +157,8 @@ def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
     ws_n = L.moe_route_workspace_size(T, d, E)
     ws = _workspace(ws_n, dev)
     _check(L.moe_route(_ptr(X), _dtype_code(X), T, d, _ptr(Wg), E, _ptr(bias), _ptr(offset),
-                       _score_code(score), int(k), int(bool(renorm)), _ptr(lg), _ptr(ids),
+                       _score_code(score), int(k), int(bool(renorm)), int(n_group),
+                       int(topk_group), _ptr(lg), _ptr(ids),
                        _ptr(w), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)))
     return {"ids": ids, "w": w, "logits": lg, "prob_sum": ps}
 
@@ -236,6 +238,8 @@ class MoeLayer:
     capacity_factor: float = 0.0
     scales: Optional[tuple] = None         # E4M3 weights: (W1_scale, W3_scale, W2_scale)
     shared_scales: Optional[tuple] = None  # and the shared expert's three scale vectors
+    n_group: int = 1                       # group-limited routing (1 = off)
+    topk_group: int = 1
 
     def cstruct(self) -> MoeLayerC:
         E, F, d = self.W1.shape
@@ -249,7 +253,7 @@ class MoeLayer:
             self.Wg.data_ptr(), _addr(self.bias), _addr(self.offset), self.W1.data_ptr(),
             self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]),
             MOE_W_FP8 if fp8 else MOE_W_DTYPE, _addr(q[0]), _addr(q[1]), _addr(q[2]),
-            _addr(qs[0]), _addr(qs[1]), _addr(qs[2]))
+            _addr(qs[0]), _addr(qs[1]), _addr(qs[2]), int(self.n_group), int(self.topk_group))
         return self._keep
 
 
@@ -263,7 +267,8 @@ def layer_from_inputs(inp: dict) -> MoeLayer:
     return MoeLayer(Wg=inp["Wg"], W1=inp["W1"], W3=inp["W3"], W2=inp["W2"], k=w.k,
                     score=w.score, renorm=w.renorm, bias=inp["bias"], offset=inp["offset"],
                     shared=inp["shared"], capacity_factor=w.cf or 0.0,
-                    scales=inp.get("scales"), shared_scales=inp.get("shared_scales"))
+                    scales=inp.get("scales"), shared_scales=inp.get("shared_scales"),
+                    n_group=w.n_group, topk_group=w.topk_group)
 
 
 class Forward:

@@ -55,6 +55,17 @@ int check_router_dims(int64_t T, int d, int E, int k) {
   return MOE_OK;
 }
 
+int check_groups(int E, int k, int n_group, int topk_group) {
+  if (n_group <= 1) return MOE_OK;
+  MOE_REQUIRE(n_group <= 64 && E % n_group == 0, MOE_EINVAL,
+              "n_group = %d must divide E = %d and be <= 64", n_group, E);
+  MOE_REQUIRE(topk_group >= 1 && topk_group <= n_group, MOE_EINVAL,
+              "topk_group = %d must be in [1, n_group = %d]", topk_group, n_group);
+  MOE_REQUIRE(k <= topk_group * (E / n_group), MOE_EINVAL,
+              "k = %d exceeds the %d experts of the chosen groups", k, topk_group * (E / n_group));
+  return MOE_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   MOE_REQUIRE(have >= need, MOE_EWORKSPACE, "workspace of %zu bytes < required %zu", have, need);
   MOE_REQUIRE(need == 0 || ws != nullptr, MOE_EINVAL, "workspace pointer is NULL");
@@ -114,18 +125,20 @@ size_t moe_route_workspace_size(int64_t T, int d, int E) {
 
 int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
               const float* bias, const float* logit_offset, int score, int k, int renorm,
-              float* logits, int32_t* topk_ids, float* topk_w, float* prob_sum, void* ws,
-              size_t ws_bytes, void* stream) {
+              int n_group, int topk_group, float* logits, int32_t* topk_ids, float* topk_w,
+              float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_dtype(dtype))) return rc;
   if ((rc = check_router_dims(T, d, E, k))) return rc;
+  if ((rc = check_groups(E, k, n_group, topk_group))) return rc;
   MOE_REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_EINVAL, "score %d unknown", score);
   MOE_REQUIRE(T == 0 || (X && Wg && topk_ids && topk_w), MOE_EINVAL, "NULL X, Wg, topk_ids or topk_w");
   MOE_REQUIRE(score == MOE_SIGMOID || bias == nullptr, MOE_EINVAL,
               "a selection bias is only defined for the sigmoid router");
   if ((rc = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E)))) return rc;
   return hip_status(launch_route(X, dtype, T, d, Wg, E, bias, logit_offset, score, k, renorm,
-                                 logits, topk_ids, topk_w, prob_sum, ws, (hipStream_t)stream),
+                                 n_group, topk_group, logits, topk_ids, topk_w, prob_sum, ws,
+                                 (hipStream_t)stream),
                     "moe_route");
 }
 
@@ -288,6 +301,7 @@ int check_layer(const moe_layer* L, int64_t T) {
               "capacity factor must be finite");
   MOE_REQUIRE(L->wtype == MOE_W_DTYPE || L->wtype == MOE_W_FP8, MOE_EINVAL, "wtype %d unknown",
               L->wtype);
+  if ((rc = check_groups(L->E, L->k, L->n_group, L->topk_group))) return rc;
   if (L->wtype == MOE_W_FP8) {
     MOE_REQUIRE(L->dtype == MOE_BF16, MOE_EUNSUPPORTED, "FP8 weights need a bf16 layer");
     MOE_REQUIRE(L->W1_scale && L->W3_scale && L->W2_scale, MOE_EINVAL, "NULL weight scales");
@@ -337,7 +351,8 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
 
   timing_mark("begin", s, 1);
   hipError_t e = launch_route(X, L->dtype, T, L->d, L->Wg, L->E, L->bias, L->logit_offset,
-                              L->score, L->k, L->renorm, a.logits, ids, gw, psum, w + o.route, s);
+                              L->score, L->k, L->renorm, L->n_group, L->topk_group, a.logits, ids,
+                              gw, psum, w + o.route, s);
   timing_mark("route", s);
   if (e == hipSuccess)
     e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,

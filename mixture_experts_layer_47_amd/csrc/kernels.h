@@ -11,10 +11,11 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // router.hip
 int router_split(int64_t T, int d, int E, int dtype);
 size_t route_ws_bytes(int64_t T, int d, int E);
+// n_group > 1: group-limited routing (topk_group groups of E / n_group).
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
                         const float* bias, const float* offset, int score, int k, int renorm,
-                        float* logits, int32_t* ids, float* w, float* prob_sum, void* ws,
-                        hipStream_t s);
+                        int n_group, int topk_group, float* logits, int32_t* ids, float* w,
+                        float* prob_sum, void* ws, hipStream_t s);
 hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E,
                           double* out, hipStream_t s);
 

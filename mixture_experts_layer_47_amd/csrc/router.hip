@@ -69,12 +69,70 @@ __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);   // key descending, lower id wins ties
 }
 
+// Wave arg-max of (key, id) over this lane's candidates (already reduced to
+// one per lane): the best key, lower id on ties.
+__device__ __forceinline__ void wave_best(double& bk, int& bi) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ok_ = __shfl_xor(bk, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ok_, oi, bk, bi)) { bk = ok_; bi = oi; }
+  }
+}
+
+// Group-limited routing (LLM Internals 14.2.3, node-limited routing: groups
+// of E / n_group consecutive experts stand in for nodes).  A group's score is
+// the sum of its gk = k / topk_group (>= 1) highest affinities, largest
+// first; the topk_group best groups (lower id on ties) stay eligible, every
+// other expert's key becomes -inf.  aff: the softmax numerator exp(l - max)
+// (same order as the probability) or the sigmoid s, in fp64.
+template <int NE>
+__device__ __forceinline__ void limit_groups(double (&key)[NE], const double (&aff)[NE], int E,
+                                             int k, int n_group, int topk_group, int lane) {
+  const int gs = E / n_group;
+  int gk = k / topk_group;
+  gk = gk < 1 ? 1 : (gk > gs ? gs : gk);
+  double gscore = -INFINITY;                 // lane g holds group g's score
+  for (int g = 0; g < n_group; ++g) {
+    uint32_t taken = 0;
+    double acc = 0.0;
+    for (int r = 0; r < gk; ++r) {
+      double bk = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && e / gs == g && !((taken >> i) & 1u) && better(aff[i], e, bk, bi)) {
+          bk = aff[i];
+          bi = e;
+        }
+      }
+      wave_best(bk, bi);
+      if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
+      acc += bk;
+    }
+    if (lane == g) gscore = acc;
+  }
+  uint64_t chosen = 0;
+  for (int r = 0; r < topk_group; ++r) {
+    const bool cand = lane < n_group && !((chosen >> lane) & 1ull);
+    double bk = cand ? gscore : -INFINITY;
+    int bi = cand ? lane : 0x7fffffff;
+    wave_best(bk, bi);
+    chosen |= 1ull << bi;
+  }
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E && !((chosen >> (e / gs)) & 1ull)) key[i] = -INFINITY;
+  }
+}
+
 template <int NE>
 __global__ __launch_bounds__(256) void k_router_select(
     const float* __restrict__ part, int nsplit, int T_, int E,
     const float* __restrict__ offset, const float* __restrict__ bias, int score,
-    int k, int renorm, float* __restrict__ logits, int32_t* __restrict__ ids,
-    float* __restrict__ wts, float* __restrict__ ps_part) {
+    int k, int renorm, int n_group, int topk_group, float* __restrict__ logits,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part) {
   __shared__ float sp[4][NE * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -93,11 +151,15 @@ __global__ __launch_bounds__(256) void k_router_select(
     }
     l[i] = v;
   }
+  double aff[NE];                        // group scores' affinities (fp64)
   if (score == MOE_SOFTMAX) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NE; ++i) m = fmaxf(m, l[i]);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      aff[i] = (n_group > 1 && tok_ok && lane + 64 * i < E) ? exp((double)l[i] - (double)m) : 0.0;
     float zs = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
@@ -120,10 +182,12 @@ __global__ __launch_bounds__(256) void k_router_select(
       const bool ok = (e < E && tok_ok);
       const double s = ok ? 1.0 / (1.0 + exp(-(double)l[i])) : 0.0;
       s64[i] = s;
+      aff[i] = s;
       p[i] = (float)s;
       key[i] = ok ? s + (bias ? (double)bias[e] : 0.0) : -INFINITY;
     }
   }
+  if (n_group > 1) limit_groups<NE>(key, aff, E, k, n_group, topk_group, lane);
   // Iterative wave arg-max, k rounds; lane j keeps the j-th winner.
   uint32_t taken = 0;
   int my_id = 0;
@@ -136,11 +200,7 @@ __global__ __launch_bounds__(256) void k_router_select(
       const int e = lane + 64 * i;
       if (e < E && !((taken >> i) & 1u) && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ok_ = __shfl_xor(bk, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ok_, oi, bk, bi)) { bk = ok_; bi = oi; }
-    }
+    wave_best(bk, bi);
     // owner lane marks the winner; every lane fetches its score
     const int oi = bi >> 6, ol = bi & 63;
     double mine = 0.0;
@@ -230,8 +290,8 @@ size_t route_ws_bytes(int64_t T, int d, int E) {
 
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
                         int E, const float* bias, const float* offset, int score,
-                        int k, int renorm, float* logits, int32_t* ids, float* w,
-                        float* prob_sum, void* ws, hipStream_t s) {
+                        int k, int renorm, int n_group, int topk_group, float* logits,
+                        int32_t* ids, float* w, float* prob_sum, void* ws, hipStream_t s) {
   if (T == 0) {
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
@@ -262,7 +322,8 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
   const int ne = MOE_CEIL_DIV(E, 64);
 #define MOE_SEL(NE_)                                                                 \
   hipLaunchKernelGGL(k_router_select<NE_>, dim3(nblk), dim3(256), 0, s, part, split, \
-                     (int)T, E, offset, bias, score, k, renorm, logits, ids, w, psp)
+                     (int)T, E, offset, bias, score, k, renorm, n_group, topk_group, logits, \
+                     ids, w, psp)
   switch (ne) {
     case 1: MOE_SEL(1); break;
     case 2: MOE_SEL(2); break;

@@ -50,6 +50,8 @@ class Workload:
     bias_std: float | None = None  # sigmoid selection bias std, None = no bias
     zipf_s: float | None = None    # per-expert logit offset exponent
     wdtype: str = "same"           # "same" | "fp8" (E4M3 expert weights, bf16 layer)
+    n_group: int = 1               # group-limited routing: groups of E / n_group experts
+    topk_group: int = 1            # groups a token may use
     seed: int = 0                  # seed of the weights
     x_seed: int | None = None      # seed of X (defaults to ``seed``)
     note: str = field(default="", compare=False)
@@ -84,6 +86,10 @@ WORKLOADS = {
 }
 WORKLOADS["switch_capacity_cf125"] = WORKLOADS["switch_capacity"].with_(
     name="switch_capacity_cf125", cf=1.25, note="Switch-style top-1, CF 1.25")
+# DeepSeek-V3 routing with its group limit: 8 groups of 32 experts, 4 per token.
+WORKLOADS["dsv3_prefill_grouped"] = WORKLOADS["dsv3_prefill"].with_(
+    name="dsv3_prefill_grouped", n_group=8, topk_group=4,
+    note="DeepSeek-V3-shaped prefill, group-limited routing (8 groups, 4 used)")
 # The same layers with FP8 E4M3 expert weights (per-output-channel scales).
 for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
     WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", wdtype="fp8",
@@ -106,6 +112,10 @@ SMALL = {
 }
 for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
     SMALL[_n + "_fp8"] = SMALL[_n].with_(name=SMALL[_n].name + "_fp8", wdtype="fp8")
+SMALL["dsv3_prefill_grouped"] = SMALL["dsv3_prefill"].with_(
+    name="dsv3_prefill_grouped_small", n_group=8, topk_group=4)
+SMALL["mixtral_grouped"] = SMALL["mixtral_prefill"].with_(
+    name="mixtral_grouped_small", E=16, k=4, n_group=4, topk_group=2)
 
 
 def _seed(*parts: int) -> int:

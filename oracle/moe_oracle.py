@@ -51,6 +51,13 @@ R9  bf16 mode: the activation h is rounded to bf16 (round-to-nearest-even)
     intermediates stay exact.
 R10 Shared expert: same width F, weight 1, added to every token's output.
 R11 Optional per-expert logit offset o_e is added to the logits before scoring.
+R13 Group-limited routing (node-limited routing of [Book 14.2.3], M = 4 for
+    DeepSeek-V3; on one GPU the E experts are split into n_group equal,
+    contiguous groups standing in for nodes): a group's score is the sum of
+    its k // topk_group highest affinities (at least 1) - the full-row softmax
+    probability or the raw sigmoid s, without the bias - summed largest first;
+    the topk_group best groups (ties to the lower group id) stay eligible and
+    top-k then runs over their experts only.
 R12 FP8 expert weights (the format the DeepSeek-V3 weights are stored in,
     [Book 14.2.5]): OCP FP8 E4M3 codes with one fp32 scale per output channel,
     W = value(code) * scale.  The format itself is not spelled out on the
@@ -72,7 +79,7 @@ __all__ = [
     "capacity", "router_logits", "scores", "select_topk", "gates", "route",
     "dispatch", "silu", "round_bf16", "expert_ffn", "combine", "forward",
     "forward_token_loop", "forward_dense_masked", "balance_value",
-    "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows",
+    "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows", "group_mask",
 ]
 
 
@@ -116,12 +123,37 @@ def scores(logits, score_func: str):
     raise ValueError(score_func)
 
 
-def select_topk(logits, k: int, score_func: str, bias=None):
+def group_mask(logits, k: int, score_func: str, n_group: int, topk_group: int):
+    """Eligible experts under group-limited routing (R13), bool [T,E]."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    if n_group < 1 or E % n_group or not 1 <= topk_group <= n_group:
+        raise ValueError("need E % n_group == 0 and 1 <= topk_group <= n_group")
+    gs = E // n_group
+    gk = min(max(1, k // topk_group), gs)
+    aff = scores(lg, score_func)
+    ok = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        gscore = np.empty(n_group)
+        for g in range(n_group):
+            top = np.sort(aff[t, g * gs:(g + 1) * gs])[::-1][:gk]
+            acc = 0.0
+            for v in top:                 # largest first
+                acc += v
+            gscore[g] = acc
+        for g in np.argsort(-gscore, kind="stable")[:topk_group]:
+            ok[t, g * gs:(g + 1) * gs] = True
+    return ok
+
+
+def select_topk(logits, k: int, score_func: str, bias=None, n_group: int = 1,
+                topk_group: int = 1):
     """Top-k hard selection [Book 14.2.1] step 3, [KMap router] step 3.
 
     Key: the logit for a softmax router (R4); s + b for a sigmoid router with a
-    selection-only bias (eq. 16, [Book 14.2.3]).  Returns ids [T,k] ordered by
-    key descending, ties to the lower id (R3), and the keys themselves.
+    selection-only bias (eq. 16, [Book 14.2.3]).  With n_group > 1 only the
+    experts of the chosen groups are eligible (R13).  Returns ids [T,k] ordered
+    by key descending, ties to the lower id (R3), and the keys themselves.
     """
     lg = np.asarray(logits, dtype=np.float64)
     T, E = lg.shape
@@ -133,6 +165,10 @@ def select_topk(logits, k: int, score_func: str, bias=None):
         key = scores(lg, "sigmoid")
         if bias is not None:
             key = key + np.asarray(bias, dtype=np.float64)[None, :]
+    if n_group > 1:
+        if k > topk_group * (E // n_group):
+            raise ValueError("the chosen groups hold fewer than k experts")
+        key = np.where(group_mask(lg, k, score_func, n_group, topk_group), key, -np.inf)
     ids = np.empty((T, k), dtype=np.int64)
     for t in range(T):
         # a stable sort of -key keeps equal keys in ascending id order
@@ -155,9 +191,9 @@ def gates(logits, ids, score_func: str, renorm: bool):
     return g
 
 
-def route(logits, k, score_func, renorm, bias=None):
+def route(logits, k, score_func, renorm, bias=None, n_group=1, topk_group=1):
     """Steps 2-3 on given logits: ids [T,k], gates [T,k], full scores [T,E]."""
-    ids, _ = select_topk(logits, k, score_func, bias)
+    ids, _ = select_topk(logits, k, score_func, bias, n_group, topk_group)
     g = gates(logits, ids, score_func, renorm)
     return ids, g, scores(logits, score_func)
 
@@ -264,7 +300,7 @@ def expert_ffn(x, W1, W3, W2, bf16_h: bool = False):
 # ----------------------------------------------------------------- forward --
 def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
             bias=None, offset=None, cap=None, shared=None, bf16_h=False,
-            logits=None):
+            logits=None, n_group=1, topk_group=1):
     """Tier 1: the six steps of [Book 14.2.1] with per-expert matmuls.
 
     X[T,d]; Wg[d,E]; W1,W3[E,d,F]; W2[E,F,d]; shared = (W1s[d,F], W3s[d,F],
@@ -277,7 +313,7 @@ def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
     E = np.asarray(Wg).shape[1]
     own = router_logits(X, Wg, offset)
     lg = own if logits is None else np.asarray(logits, dtype=np.float64)
-    ids, g, p = route(lg, k, score_func, renorm, bias)
+    ids, g, p = route(lg, k, score_func, renorm, bias, n_group, topk_group)
     disp = dispatch(ids, E, cap)
     rows = np.zeros((disp["n_kept"], d))
     for e in range(E):

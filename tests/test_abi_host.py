@@ -74,14 +74,19 @@ def test_down_projection_split_decision(L):
 
 def _route(L, **over):
     a = dict(X=1, dtype=1, T=16, d=256, Wg=1, E=8, bias=None, off=None, score=0, k=2, renorm=1,
-             logits=None, ids=1, w=1, ps=None, ws=256, ws_bytes=1 << 30, stream=None)
+             ng=1, tg=1, logits=None, ids=1, w=1, ps=None, ws=256, ws_bytes=1 << 30, stream=None)
     a.update(over)
     return L.moe_route(a["X"], a["dtype"], a["T"], a["d"], a["Wg"], a["E"], a["bias"], a["off"],
-                       a["score"], a["k"], a["renorm"], a["logits"], a["ids"], a["w"], a["ps"],
-                       a["ws"], a["ws_bytes"], a["stream"])
+                       a["score"], a["k"], a["renorm"], a["ng"], a["tg"], a["logits"], a["ids"],
+                       a["w"], a["ps"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_route_validation(L):
+    # group-limited routing: groups must divide E and hold at least k experts
+    assert _route(L, ng=3) == -1                # 3 does not divide 8
+    assert _route(L, ng=4, tg=5) == -1          # topk_group > n_group
+    assert _route(L, ng=4, tg=0) == -1
+    assert _route(L, ng=8, tg=1, k=2) == -1     # one group of 1 expert < k
     assert _route(L, k=0) == -1
     assert _route(L, k=9) == -1                 # k > E
     assert _route(L, E=0) == -1

@@ -48,8 +48,8 @@ def test_fullsize_workload(name):
 
     # --- R2: routing on every token (oracle top-k on the device's fp32 logits)
     bias = None if inp["bias"] is None else H.np64(inp["bias"])
-    ids_ref, g_ref, p_ref = O.route(lg, w.k, w.score, w.renorm, bias)
-    _, keys = O.select_topk(lg, w.k, w.score, bias)
+    ids_ref, g_ref, p_ref = O.route(lg, w.k, w.score, w.renorm, bias, w.n_group, w.topk_group)
+    _, keys = O.select_topk(lg, w.k, w.score, bias, w.n_group, w.topk_group)
     ids = H.np64(aux["topk_ids"]).astype(np.int64)
     ties = H.check_ids(ids, ids_ref, keys if w.score == "sigmoid" else None)
     print(f"[info] {name}: near-tie tokens {ties}", flush=True)

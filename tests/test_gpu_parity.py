@@ -26,7 +26,8 @@ def _oracle_forward(inp, lg_gpu):
     cap = O.capacity(w.cf, w.T, w.k, w.E) if w.cf else None
     return O.forward(L["X"], L["Wg"], L["W1"], L["W3"], L["W2"], k=w.k, score_func=w.score,
                      renorm=w.renorm, bias=L["bias"], offset=L["offset"], cap=cap,
-                     shared=L["shared"], bf16_h=(w.dtype == "bf16"), logits=lg_gpu), cap
+                     shared=L["shared"], bf16_h=(w.dtype == "bf16"), logits=lg_gpu,
+                     n_group=w.n_group, topk_group=w.topk_group), cap
 
 
 def _full_check(inp):
@@ -40,7 +41,7 @@ def _full_check(inp):
     # R1: logits against the oracle's own fp64 logits
     H.check_logits(lg, ref["logits"])
     # R2: ids exact (oracle top-k on the device's fp32 logits), gates within tolerance
-    _, keys = O.select_topk(lg, w.k, w.score, H.logical(inp)["bias"])
+    _, keys = O.select_topk(lg, w.k, w.score, H.logical(inp)["bias"], w.n_group, w.topk_group)
     ties = H.check_ids(H.np64(aux["topk_ids"]).astype(np.int64), ref["ids"],
                        keys if w.score == "sigmoid" else None)
     assert ties == 0, "near-tie reordering in a small workload"
@@ -160,17 +161,21 @@ def test_deterministic_bitwise():
 
 
 # ---------------------------------------------------------- entry points --
-def test_route_entry_point():
-    w = SMALL["dsv3_prefill"].with_(T=333)
-    _announce("moe_route")
+@pytest.mark.parametrize("score,ng,tg", [("sigmoid", 1, 1), ("sigmoid", 8, 4), ("sigmoid", 4, 1),
+                                         ("softmax", 8, 2), ("softmax", 32, 32)])
+def test_route_entry_point(score, ng, tg):
+    w = SMALL["dsv3_prefill"].with_(T=333, score=score,
+                                    bias_std=0.01 if score == "sigmoid" else None)
+    _announce(f"moe_route {score} n_group={ng} topk_group={tg}")
     inp = make_inputs(w, DEV)
-    r = moe.route(inp["X"], inp["Wg"], w.k, w.score, w.renorm, bias=inp["bias"])
+    r = moe.route(inp["X"], inp["Wg"], w.k, w.score, w.renorm, bias=inp["bias"], n_group=ng,
+                  topk_group=tg)
     torch.cuda.synchronize()
     L = H.logical(inp)
     lg = H.np64(r["logits"])
     H.check_logits(lg, O.router_logits(L["X"], L["Wg"]))
-    ids, g, p = O.route(lg, w.k, w.score, w.renorm, L["bias"])
-    _, keys = O.select_topk(lg, w.k, w.score, L["bias"])
+    ids, g, p = O.route(lg, w.k, w.score, w.renorm, L["bias"], ng, tg)
+    _, keys = O.select_topk(lg, w.k, w.score, L["bias"], ng, tg)
     H.check_ids(H.np64(r["ids"]).astype(np.int64), ids, keys)
     H.check_gates(H.np64(r["w"]), g)
     assert np.allclose(H.np64(r["prob_sum"]), p.sum(axis=0), rtol=1e-5, atol=1e-5)

@@ -404,6 +404,12 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_e4m3_closed_forms()
     monkeypatch.setattr(O, "decode_e4m3", good_dec)
+    # 8. group score from the single best affinity instead of the top k/M
+    good_gm = O.group_mask
+    monkeypatch.setattr(O, "group_mask", lambda lg, k, sf, ng, tg: good_gm(lg, tg, sf, ng, tg))
+    with pytest.raises(AssertionError):
+        test_group_limited_hand_example()
+    monkeypatch.setattr(O, "group_mask", good_gm)
 
 
 # ------------------------------------------------------------- FP8 weights --
@@ -440,3 +446,59 @@ def test_dequantize_rows_scales_output_channels():
     for e in range(3):
         for n in range(5):
             assert np.array_equal(W[e, n], O.decode_e4m3(codes[e, n]) * scale[e, n])
+
+
+# ------------------------------------------------------ group-limited routing --
+def test_group_limited_hand_example():
+    # 8 experts in 4 groups of 2; top-2 with one group allowed: the group with
+    # the larger sum of its top-2 (= both) affinities wins, even though the
+    # single best expert (id 6) sits in another group
+    s = np.array([[0.50, 0.45, 0.10, 0.10, 0.20, 0.20, 0.90, 0.01]])
+    lg = np.log(s / (1.0 - s))                       # sigmoid(lg) = s
+    ids, _ = O.select_topk(lg, 2, "sigmoid", n_group=4, topk_group=1)
+    assert ids.tolist() == [[0, 1]]                  # 0.95 beats 0.91
+    ids, _ = O.select_topk(lg, 2, "sigmoid", n_group=4, topk_group=2)
+    assert ids.tolist() == [[6, 0]]                  # groups {0,3}: best two keys
+    # one allowed group of size 2 with k = 1: the group's score is its max
+    ids, _ = O.select_topk(lg, 1, "sigmoid", n_group=4, topk_group=1)
+    assert ids.tolist() == [[6]]
+    # the bias moves selection inside the chosen groups but not the group scores
+    b = np.zeros(8); b[2] = 5.0
+    ids, _ = O.select_topk(lg, 1, "sigmoid", bias=b, n_group=4, topk_group=1)
+    assert ids.tolist() == [[6]]                     # expert 2's bias cannot pull group 1 in
+    b = np.zeros(8); b[1] = 1.0; b[7] = 5.0
+    ids, _ = O.select_topk(lg, 1, "sigmoid", bias=b, n_group=4, topk_group=1)
+    assert ids.tolist() == [[7]]                     # inside the chosen group 3
+    ids, _ = O.select_topk(lg, 2, "sigmoid", bias=b, n_group=4, topk_group=2)
+    assert ids.tolist() == [[7, 1]]                  # groups {3, 0} by their top-1
+
+
+def test_group_limited_special_cases():
+    rng = np.random.default_rng(12)
+    lg = rng.normal(size=(40, 16)) * 2
+    for sf in ("softmax", "sigmoid"):
+        plain = O.select_topk(lg, 4, sf)[0]
+        assert np.array_equal(O.select_topk(lg, 4, sf, n_group=1, topk_group=1)[0], plain)
+        assert np.array_equal(O.select_topk(lg, 4, sf, n_group=4, topk_group=4)[0], plain)
+        assert np.array_equal(O.select_topk(lg, 4, sf, n_group=16, topk_group=16)[0], plain)
+
+
+def test_group_limited_brute_force():
+    # every chosen expert lies in a chosen group, the chosen groups are the
+    # best by the summed top-(k/M) affinities, and inside them the ids are the
+    # plain top-k of the masked keys
+    rng = np.random.default_rng(13)
+    E, G, M, k = 12, 4, 2, 4
+    lg = rng.normal(size=(60, E))
+    for sf in ("softmax", "sigmoid"):
+        ids, key = O.select_topk(lg, k, sf, n_group=G, topk_group=M)
+        aff = O.scores(lg, sf)
+        gs = E // G
+        for t in range(lg.shape[0]):
+            gsc = [sorted(aff[t, g * gs:(g + 1) * gs])[::-1][0] + sorted(aff[t, g * gs:(g + 1) * gs])[::-1][1]
+                   for g in range(G)]
+            best = sorted(range(G), key=lambda g: (-gsc[g], g))[:M]
+            allowed = [e for g in best for e in range(g * gs, (g + 1) * gs)]
+            kk = lg[t] if sf == "softmax" else aff[t]
+            exp = sorted(allowed, key=lambda e: (-kk[e], e))[:k]
+            assert ids[t].tolist() == exp
