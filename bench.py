@@ -171,6 +171,8 @@ def main():
     kept = probe.aux["offsets"].diff().cpu().numpy()
     n_kept = int(probe.aux["n_kept"].item())
     balance = float(probe.aux["balance"].item())
+    health = dict(zip(("token_entropy", "load_entropy", "load_cv", "drop_rate"),
+                      (float(v) for v in probe.aux["health"].cpu().tolist())))
     del probe
     torch.cuda.empty_cache()
     fwd = moe.Forward(layer, inp["X"], aux=False)
@@ -242,7 +244,8 @@ def main():
         "layer": {"flops": layer_flops, "bytes": layer_bytes,
                   "mfma_frac": layer_flops / (ms_step * 1e-3) / (peak_flops * 1e12),
                   "hbm_frac": layer_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-                  "kept_rows": n_kept, "balance_stat": balance, "phases_ms": phase_ms},
+                  "kept_rows": n_kept, "balance_stat": balance, "router_health": health,
+                  "phases_ms": phase_ms},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_target_s)

@@ -222,6 +222,13 @@ typedef struct moe_aux {
   int32_t* n_kept;         /* [1]     */
   float* Yrows;            /* [T*k + n_shared*T][d] expert output rows       */
   double* balance;         /* [1]     */
+  double* health;          /* [4] router health (LLM Internals 14.2.3's three
+                              signals, AI Knowledge Map's load CV): mean
+                              per-token routing entropy of the full-row
+                              distribution (sigmoid scores normalised to sum
+                              1), entropy of the pre-drop load fractions
+                              counts/(T*k), std/mean of the per-expert
+                              counts, drop rate 1 - R/(T*k)               */
 } moe_aux;
 
 size_t moe_forward_workspace_size(const moe_layer* L, int64_t T);

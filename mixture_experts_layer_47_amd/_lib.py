@@ -55,7 +55,7 @@ class MoeLayerC(ctypes.Structure):
 class MoeAuxC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("logits", "topk_ids", "topk_w", "prob_sum", "counts", "offsets",
-                 "sorted_slot", "slot_row", "n_kept", "Yrows", "balance")]
+                 "sorted_slot", "slot_row", "n_kept", "Yrows", "balance", "health")]
 
 
 _LIB = None
@@ -300,6 +300,8 @@ class Forward:
                 "n_kept": torch.empty(1, **i32),
                 "Yrows": torch.empty((max(rows, 1), d), dtype=torch.float32, device=dev),
                 "balance": torch.empty(1, dtype=torch.float64, device=dev),
+                # token entropy, load entropy, load CV, drop rate
+                "health": torch.empty(4, dtype=torch.float64, device=dev),
             }
             for n, t in self.aux.items():
                 setattr(self.caux, n, t.data_ptr())

@@ -253,7 +253,7 @@ int moe_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, 
 // ----------------------------------------------------------------- forward
 namespace {
 struct FwdLayout {
-  size_t route, ids, w, psum, counts, offsets, nkept, sorted, slotrow, rowtok, hist, yrows, ffn,
+  size_t route, ids, w, psum, counts, offsets, nkept, sorted, slotrow, rowtok, hist, ent, yrows, ffn,
       total;
 };
 
@@ -279,6 +279,7 @@ FwdLayout fwd_layout(const moe_layer* L, int64_t T) {
   o.slotrow = take((size_t)Tk * 4);
   o.rowtok = take((size_t)rows * 4);
   o.hist = take(dispatch_ws_bytes(T, L->k, L->E));
+  o.ent = take((size_t)MOE_CEIL_DIV(T, 4) * 4);
   o.yrows = take((size_t)rows * L->d * 4);
   o.ffn = take(ffn_ws_bytes(rows, G, L->d, L->F, L->dtype));
   o.total = at;
@@ -350,9 +351,10 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   const int64_t Tk = T * (int64_t)L->k;
 
   timing_mark("begin", s, 1);
+  float* ent = a.health ? (float*)(w + o.ent) : nullptr;
   hipError_t e = launch_route(X, L->dtype, T, L->d, L->Wg, L->E, L->bias, L->logit_offset,
                               L->score, L->k, L->renorm, L->n_group, L->topk_group, a.logits, ids,
-                              gw, psum, w + o.route, s);
+                              gw, psum, w + o.route, s, ent);
   timing_mark("route", s);
   if (e == hipSuccess)
     e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,
@@ -376,6 +378,8 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   if (e == hipSuccess && a.offsets)
     e = hipMemcpyAsync(a.offsets, offsets, (size_t)(L->E + 1) * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess && a.balance) e = launch_balance(counts, psum, T, L->k, L->E, a.balance, s);
+  if (e == hipSuccess && a.health)
+    e = launch_router_health(counts, nkept, ent, T, L->k, L->E, a.health, s);
   timing_mark("aux", s);
   return hip_status(e, "moe_forward");
 }

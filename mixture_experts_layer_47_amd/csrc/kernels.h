@@ -15,7 +15,12 @@ size_t route_ws_bytes(int64_t T, int d, int E);
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
                         const float* bias, const float* offset, int score, int k, int renorm,
                         int n_group, int topk_group, float* logits, int32_t* ids, float* w,
-                        float* prob_sum, void* ws, hipStream_t s);
+                        float* prob_sum, void* ws, hipStream_t s, float* ent_part = nullptr);
+// {token entropy, load entropy, load CV, drop rate}; ent_part holds one
+// partial per block of four tokens (written by launch_route).
+hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
+                                const float* ent_part, int64_t T, int k, int E, double* out,
+                                hipStream_t s);
 hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E,
                           double* out, hipStream_t s);
 

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void k_router_select(
     const float* __restrict__ part, int nsplit, int T_, int E,
     const float* __restrict__ offset, const float* __restrict__ bias, int score,
     int k, int renorm, int n_group, int topk_group, float* __restrict__ logits,
-    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part) {
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part,
+    float* __restrict__ ent_part) {
   __shared__ float sp[4][NE * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -215,6 +216,26 @@ __global__ __launch_bounds__(256) void k_router_select(
     ids[(size_t)t * k + lane] = my_id;
     wts[(size_t)t * k + lane] = (float)(renorm ? my_val / tot : my_val);
   }
+  if (ent_part) {  // per-block partial of the tokens' routing entropies
+    // q = p, or s / sum(s) for a sigmoid router; -sum q ln q in fp32
+    float zs = 0.f;
+    if (score != MOE_SOFTMAX) {
+#pragma unroll
+      for (int i = 0; i < NE; ++i) zs += p[i];
+      for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
+    }
+    float h = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const float q = score == MOE_SOFTMAX ? p[i] : (zs > 0.f ? p[i] / zs : 0.f);
+      if (q > 0.f) h -= q * logf(q);
+    }
+    for (int o = 32; o > 0; o >>= 1) h += __shfl_xor(h, o);
+    __shared__ float eh[4];
+    if (lane == 0) eh[wave] = tok_ok ? h : 0.f;
+    __syncthreads();
+    if (threadIdx.x == 0) ent_part[blockIdx.x] = ((eh[0] + eh[1]) + eh[2]) + eh[3];
+  }
   if (ps_part) {   // per-block partial of sum_t p[t][e], fixed summation order
 #pragma unroll
     for (int i = 0; i < NE; ++i) sp[wave][lane + 64 * i] = tok_ok ? p[i] : 0.f;
@@ -262,6 +283,45 @@ __global__ __launch_bounds__(256) void k_balance(const int32_t* __restrict__ cou
   }
 }
 
+// Router health: out = {mean token entropy, load entropy, load CV, drop rate}
+// (LLM Internals 14.2.3's routing entropy / per-expert distribution / drop
+// rate, AI Knowledge Map's expert-load CV).  One block, fixed-order sums.
+__global__ __launch_bounds__(256) void k_router_health(const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ n_kept,
+                                                       const float* __restrict__ ent_part,
+                                                       int nblk, int64_t T_, int k, int E,
+                                                       double* __restrict__ out) {
+  __shared__ double r0[256], r1[256], r2[256];
+  const double tk = (double)T_ * (double)k;
+  const double mean = tk / (double)E;
+  double a = 0.0, b = 0.0, c = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) a += (double)ent_part[i];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const double n = (double)counts[e];
+    const double f = tk > 0.0 ? n / tk : 0.0;
+    if (f > 0.0) b -= f * log(f);
+    c += (n - mean) * (n - mean);
+  }
+  r0[threadIdx.x] = a;
+  r1[threadIdx.x] = b;
+  r2[threadIdx.x] = c;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) {
+      r0[threadIdx.x] += r0[threadIdx.x + st];
+      r1[threadIdx.x] += r1[threadIdx.x + st];
+      r2[threadIdx.x] += r2[threadIdx.x + st];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = T_ > 0 ? r0[0] / (double)T_ : 0.0;
+    out[1] = r1[0];
+    out[2] = mean > 0.0 ? sqrt(r2[0] / (double)E) / mean : 0.0;
+    out[3] = tk > 0.0 ? 1.0 - (double)n_kept[0] / tk : 0.0;
+  }
+}
+
 // --------------------------------------------------------------- launchers
 // K-split of the logits: about one slice per 1024 of d.  On the tiled-GEMM
 // path it is doubled while that leaves fewer tiles than CUs, slices stay
@@ -291,7 +351,8 @@ size_t route_ws_bytes(int64_t T, int d, int E) {
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
                         int E, const float* bias, const float* offset, int score,
                         int k, int renorm, int n_group, int topk_group, float* logits,
-                        int32_t* ids, float* w, float* prob_sum, void* ws, hipStream_t s) {
+                        int32_t* ids, float* w, float* prob_sum, void* ws, hipStream_t s,
+                        float* ent_part) {
   if (T == 0) {
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
@@ -323,7 +384,7 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
 #define MOE_SEL(NE_)                                                                 \
   hipLaunchKernelGGL(k_router_select<NE_>, dim3(nblk), dim3(256), 0, s, part, split, \
                      (int)T, E, offset, bias, score, k, renorm, n_group, topk_group, logits, \
-                     ids, w, psp)
+                     ids, w, psp, ent_part)
   switch (ne) {
     case 1: MOE_SEL(1); break;
     case 2: MOE_SEL(2); break;
@@ -333,6 +394,14 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
 #undef MOE_SEL
   if (prob_sum)
     hipLaunchKernelGGL(k_prob_sum, dim3(E), dim3(256), 0, s, ps_part, nblk, E, prob_sum);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
+                                const float* ent_part, int64_t T, int k, int E, double* out,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_router_health, dim3(1), dim3(256), 0, s, counts, n_kept, ent_part,
+                     (int)MOE_CEIL_DIV(T, 4), T, k, E, out);
   return hipGetLastError();
 }
 

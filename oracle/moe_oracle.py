@@ -51,6 +51,10 @@ R9  bf16 mode: the activation h is rounded to bf16 (round-to-nearest-even)
     intermediates stay exact.
 R10 Shared expert: same width F, weight 1, added to every token's output.
 R11 Optional per-expert logit offset o_e is added to the logits before scoring.
+R12 FP8 expert weights (the format the DeepSeek-V3 weights are stored in,
+    [Book 14.2.5]): OCP FP8 E4M3 codes with one fp32 scale per output channel,
+    W = value(code) * scale.  The format itself is not spelled out on the
+    pages; its public definition is restated in decode_e4m3.
 R13 Group-limited routing (node-limited routing of [Book 14.2.3], M = 4 for
     DeepSeek-V3; on one GPU the E experts are split into n_group equal,
     contiguous groups standing in for nodes): a group's score is the sum of
@@ -58,10 +62,10 @@ R13 Group-limited routing (node-limited routing of [Book 14.2.3], M = 4 for
     probability or the raw sigmoid s, without the bias - summed largest first;
     the topk_group best groups (ties to the lower group id) stay eligible and
     top-k then runs over their experts only.
-R12 FP8 expert weights (the format the DeepSeek-V3 weights are stored in,
-    [Book 14.2.5]): OCP FP8 E4M3 codes with one fp32 scale per output channel,
-    W = value(code) * scale.  The format itself is not spelled out on the
-    pages; its public definition is restated in decode_e4m3.
+R14 Router health ([Book 14.2.3]'s three signals plus the load CV of
+    [KMap]): mean per-token routing entropy of the full-row distribution
+    (sigmoid scores normalised to sum 1), entropy of the pre-drop load
+    fractions, population-std CV of the per-expert counts, and the drop rate.
 
 Parity status: every function here is pinned by the CPU tests (worked examples
 printed on the pages, closed forms, brute force and cross-tier agreement).  The
@@ -80,6 +84,7 @@ __all__ = [
     "dispatch", "silu", "round_bf16", "expert_ffn", "combine", "forward",
     "forward_token_loop", "forward_dense_masked", "balance_value",
     "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows", "group_mask",
+    "router_health",
 ]
 
 
@@ -447,6 +452,34 @@ def forward_dense_masked(X, Wg, W1, W3, W2, *, k, score_func="softmax",
     if shared is not None:
         Y = Y + expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
     return Y
+
+
+# ----------------------------------------------------------- router health --
+def router_health(logits, score_func: str, counts, n_kept: int, n_tokens: int, k: int):
+    """The three router signals [Book 14.2.3] names - routing entropy, the
+    per-expert token distribution, the token drop rate - and the expert-load
+    CV of [KMap] (std / mean of the per-expert loads), as four numbers (R14):
+
+      token_entropy  mean over tokens of -sum_e q ln q, q the full-row softmax
+                     p, or s / sum(s) for a sigmoid router (nats)
+      load_entropy   -sum_e f ln f of f_e = counts_e / (T*k), pre-drop (nats)
+      load_cv        population std of counts_e over their mean T*k / E
+      drop_rate      1 - R / (T*k)
+    """
+    q = scores(logits, score_func)
+    if score_func == "sigmoid":
+        q = q / q.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        h = -np.where(q > 0, q * np.log(q), 0.0).sum(axis=1)
+    c = np.asarray(counts, dtype=np.float64)
+    tk = float(n_tokens * k)
+    f = c / tk if tk > 0 else np.zeros_like(c)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        h_load = float(-np.where(f > 0, f * np.log(f), 0.0).sum())
+    mean = tk / c.size
+    cv = float(np.sqrt(np.mean((c - mean) ** 2)) / mean) if mean > 0 else 0.0
+    return {"token_entropy": float(h.mean()) if n_tokens else 0.0, "load_entropy": h_load,
+            "load_cv": cv, "drop_rate": 1.0 - n_kept / tk if tk > 0 else 0.0}
 
 
 # ----------------------------------------------------------------- balance --

@@ -72,6 +72,13 @@ def _full_check(inp):
     assert np.abs(ps - ps_ref).max() <= 1e-5 * max(1.0, np.abs(ps_ref).max())
     bal_ref = O.balance_stat(d["counts"], ps_ref, w.T, w.k)
     assert abs(aux["balance"].item() - bal_ref) <= 1e-5 * max(1.0, abs(bal_ref))
+    # router health: entropies, load CV, drop rate
+    hr = O.router_health(lg, w.score, d["counts"], R, w.T, w.k)
+    hg = aux["health"].cpu().numpy()
+    assert abs(hg[0] - hr["token_entropy"]) <= 1e-4 * max(1.0, hr["token_entropy"])
+    assert abs(hg[1] - hr["load_entropy"]) <= 1e-12 * max(1.0, hr["load_entropy"])
+    assert abs(hg[2] - hr["load_cv"]) <= 1e-12 * max(1.0, hr["load_cv"])
+    assert abs(hg[3] - hr["drop_rate"]) <= 1e-15
     return Y, aux
 
 

@@ -502,3 +502,27 @@ def test_group_limited_brute_force():
             kk = lg[t] if sf == "softmax" else aff[t]
             exp = sorted(allowed, key=lambda e: (-kk[e], e))[:k]
             assert ids[t].tolist() == exp
+
+
+# ------------------------------------------------------------- router health --
+def test_router_health_closed_forms():
+    E, T, k = 8, 40, 2
+    # uniform routing: entropy ln E per token, equal loads (CV 0), no drops
+    lg = np.zeros((T, E))
+    counts = np.full(E, T * k // E)
+    h = O.router_health(lg, "softmax", counts, T * k, T, k)
+    assert abs(h["token_entropy"] - math.log(E)) < 1e-12
+    assert abs(h["load_entropy"] - math.log(E)) < 1e-12
+    assert h["load_cv"] == 0.0 and h["drop_rate"] == 0.0
+    # collapse: every slot on expert 0, one-hot rows
+    lg = np.full((T, E), -1e4); lg[:, 0] = 0.0
+    counts = np.zeros(E); counts[0] = T * k
+    h = O.router_health(lg, "softmax", counts, T * k, T, k)
+    assert h["token_entropy"] < 1e-12 and h["load_entropy"] == 0.0
+    assert abs(h["load_cv"] - math.sqrt(E - 1)) < 1e-12
+    # the capacity worked example: 12 requests, 2 dropped
+    h = O.router_health(np.zeros((6, 4)), "softmax", [5, 3, 2, 2], 10, 6, 2)
+    assert abs(h["drop_rate"] - 1.0 / 6.0) < 1e-15
+    # sigmoid scores are normalised per row: equal logits give ln E too
+    h = O.router_health(np.full((3, E), 0.7), "sigmoid", counts, T * k, 3, k)
+    assert abs(h["token_entropy"] - math.log(E)) < 1e-12
