@@ -25,6 +25,12 @@ and its section:
   case 1: the minimal top-k routing pseudo-code (router -> top-k -> softmax
   over the k kept scores -> weighted sum of the chosen experts).
 * [Study pitfalls] same note, "pitfalls": the router softmax runs in fp32.
+* [Blog frontier] oscine.io "MoE 03: efficiency frontiers", the section on
+  the further frontier: expert-choice routing, each expert picks the C tokens
+  it suits best.
+* [Explainer routing] smallfiredragon.com "Mixture of Experts (MoE) in depth"
+  (Chinese), the routing-mechanism list: expert-choice routing lets every
+  expert pick its tokens, so the number of experts per token varies.
 
 Readings where the pages are silent or ambiguous (each one also listed in the
 design notes of the repository):
@@ -67,6 +73,18 @@ R14 Router health ([Book 14.2.3]'s three signals plus the load CV of
     (sigmoid scores normalised to sum 1), entropy of the pre-drop load
     fractions, population-std CV of the per-expert counts, and the drop rate.
 
+R20 Expert-choice routing ([Book 14.2.3] "two selection paradigms", [Blog
+    frontier], [Explainer routing]): the scores are the token-choice router's
+    (full-row softmax over experts, or the sigmoid affinity); expert e takes
+    the min(C, T) tokens with the highest score in its column, ties to the
+    lower token index, with C the capacity formula's value for the layer's
+    mean experts per token k (c = 1 when no factor is given).  A token's gate
+    for an expert that took it is its score, with no renormalisation (the
+    number of experts per token is not fixed); a token no expert took gets
+    only the shared expert.  Rows are grouped by expert, tokens ascending
+    inside; slot s = t*E + e.
+(R15-R19 concern the device comparison and the inputs, not this module.)
+
 Parity status: every function here is pinned by the CPU tests (worked examples
 printed on the pages, closed forms, brute force and cross-tier agreement).  The
 bf16 rounding of h (R9) is a reading, pinned only by its own RNE unit test; the
@@ -84,7 +102,8 @@ __all__ = [
     "dispatch", "silu", "round_bf16", "expert_ffn", "combine", "forward",
     "forward_token_loop", "forward_dense_masked", "balance_value",
     "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows", "group_mask",
-    "router_health",
+    "router_health", "expert_choice", "expert_choice_dispatch", "forward_expert_choice",
+    "forward_expert_choice_loop",
 ]
 
 
@@ -452,6 +471,127 @@ def forward_dense_masked(X, Wg, W1, W3, W2, *, k, score_func="softmax",
     if shared is not None:
         Y = Y + expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
     return Y
+
+
+# ----------------------------------------------------------- expert choice --
+def expert_choice(logits, score_func: str, C: int):
+    """Expert-choice selection (R20): each expert takes a fixed number of
+    tokens from the batch [Book 14.2.3], the C it scores highest [Blog
+    frontier].
+
+    The score matrix is the token-choice router's (softmax across the E
+    experts of each token, or the sigmoid affinity).  Column e is ranked by
+    score, highest first, ties to the lower token index; the first min(C, T)
+    tokens are taken.  Returns (mask [T,E] bool, gates [T,E] = score where
+    taken, else 0, scores [T,E]).
+    """
+    p = scores(logits, score_func)
+    T, E = p.shape
+    if C < 0:
+        raise ValueError("C must be >= 0")
+    take = min(int(C), T)
+    mask = np.zeros((T, E), dtype=bool)
+    for e in range(E):
+        # a stable sort of -score keeps equal scores in ascending token order
+        order = np.argsort(-p[:, e], kind="stable")
+        mask[order[:take], e] = True
+    return mask, np.where(mask, p, 0.0), p
+
+
+def expert_choice_dispatch(mask):
+    """Row layout of an expert-choice assignment (R20): slot s = t*E + e;
+    the taken slots grouped by expert, ascending token index inside (the
+    same grouping as ``dispatch``).  Returns counts[E] (tokens per expert),
+    offsets[E+1], sorted_slot[R], slot_row[T*E] (-1 where not taken), n_kept.
+    """
+    mask = np.asarray(mask, dtype=bool)
+    T, E = mask.shape
+    offsets = [0]
+    sorted_slot = []
+    slot_row = np.full(T * E, -1, dtype=np.int64)
+    for e in range(E):
+        for t in np.flatnonzero(mask[:, e]).tolist():
+            slot_row[t * E + e] = len(sorted_slot)
+            sorted_slot.append(t * E + e)
+        offsets.append(len(sorted_slot))
+    counts = np.diff(np.array(offsets, dtype=np.int64))
+    return {"counts": counts, "kept": counts.copy(),
+            "offsets": np.array(offsets, dtype=np.int64),
+            "sorted_slot": np.array(sorted_slot, dtype=np.int64),
+            "slot_row": slot_row, "n_kept": len(sorted_slot)}
+
+
+def forward_expert_choice(X, Wg, W1, W3, W2, *, C, score_func="softmax", offset=None,
+                          shared=None, bf16_h=False, logits=None, mask=None):
+    """Tier 1 of an expert-choice layer (R20): score, let every expert take
+    its C tokens, run each expert on its rows, then combine with the scores
+    as gates plus the shared expert (R10).  ``logits`` replaces the oracle's
+    own scoring and ``mask`` the selection (e.g. the device's, once checked).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    T, d = X.shape
+    E = np.asarray(Wg).shape[1]
+    own = router_logits(X, Wg, offset)
+    lg = own if logits is None else np.asarray(logits, dtype=np.float64)
+    m, g, p = expert_choice(lg, score_func, C)
+    if mask is not None:
+        m = np.asarray(mask, dtype=bool)
+        g = np.where(m, p, 0.0)
+    disp = expert_choice_dispatch(m)
+    rows = np.zeros((disp["n_kept"], d))
+    for e in range(E):
+        a, b = disp["offsets"][e], disp["offsets"][e + 1]
+        if b > a:
+            tok = disp["sorted_slot"][a:b] // E
+            rows[a:b] = expert_ffn(X[tok], W1[e], W3[e], W2[e], bf16_h)
+    sh = None
+    if shared is not None:
+        sh = expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
+    Y = combine(rows, disp["slot_row"], g, sh)
+    return {"logits": own, "route_logits": lg, "mask": m, "gates": g, "probs": p,
+            "dispatch": disp, "rows": rows, "shared": sh, "Y": Y}
+
+
+def forward_expert_choice_loop(X, Wg, W1, W3, W2, *, C, score_func="softmax",
+                               offset=None, shared=None):
+    """Tier 0 of an expert-choice layer: plain Python loops over experts and
+    tokens (R20).  Only for tiny shapes."""
+    X = np.asarray(X, dtype=np.float64).tolist()
+    Wg = np.asarray(Wg, dtype=np.float64).tolist()
+    T, d, E = len(X), len(X[0]), len(Wg[0])
+    prob = []
+    for t in range(T):
+        sc = [sum(X[t][i] * Wg[i][e] for i in range(d)) for e in range(E)]
+        if offset is not None:
+            sc = [sc[e] + float(offset[e]) for e in range(E)]
+        if score_func == "softmax":
+            mx = max(sc)
+            ex = [math.exp(v - mx) for v in sc]
+            prob.append([v / sum(ex) for v in ex])
+        else:
+            prob.append([1.0 / (1.0 + math.exp(-v)) for v in sc])
+
+    def swiglu(x, w1, w3, w2):
+        F = len(w1[0])
+        h = []
+        for f in range(F):
+            a = sum(x[i] * w1[i][f] for i in range(d))
+            u = sum(x[i] * w3[i][f] for i in range(d))
+            h.append(a / (1.0 + math.exp(-a)) * u)
+        return [sum(h[f] * w2[f][j] for f in range(F)) for j in range(d)]
+
+    Y = [[0.0] * d for _ in range(T)]
+    for e in range(E):
+        ranked = sorted(range(T), key=lambda t: (-prob[t][e], t))
+        w1, w3, w2 = (np.asarray(W[e], np.float64).tolist() for W in (W1, W3, W2))
+        for t in ranked[:min(C, T)]:
+            y = swiglu(X[t], w1, w3, w2)
+            Y[t] = [a + prob[t][e] * b for a, b in zip(Y[t], y)]
+    if shared is not None:
+        s1, s3, s2 = (np.asarray(W, np.float64).tolist() for W in shared)
+        for t in range(T):
+            Y[t] = [a + b for a, b in zip(Y[t], swiglu(X[t], s1, s3, s2))]
+    return np.array(Y, dtype=np.float64)
 
 
 # ----------------------------------------------------------- router health --

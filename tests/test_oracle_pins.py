@@ -526,3 +526,143 @@ def test_router_health_closed_forms():
     # sigmoid scores are normalised per row: equal logits give ln E too
     h = O.router_health(np.full((3, E), 0.7), "sigmoid", counts, T * k, 3, k)
     assert abs(h["token_entropy"] - math.log(E)) < 1e-12
+
+
+# ----------------------------------------------------------- expert choice --
+def test_expert_choice_hand_example():
+    # Two experts, four tokens, C = 2.  Token 0's logits are equal (p = 1/2
+    # each), token 1 leans to expert 0, token 2 to expert 1, token 3 is equal
+    # again.  Expert 0 ranks t1 (p ~ .95) then t0 and t3 tied at exactly 1/2,
+    # resolved to the lower index; expert 1 symmetrically.  So token 0 is
+    # taken by both experts and token 3 by none: the two consequences
+    # [Book 14.2.3] states for expert choice.
+    lg = np.array([[3.0, 3.0], [2.0, -1.0], [-1.0, 2.0], [-5.0, -5.0]])
+    mask, g, p = O.expert_choice(lg, "softmax", 2)
+    assert mask.tolist() == [[True, True], [True, False], [False, True], [False, False]]
+    assert g[0].tolist() == [0.5, 0.5] and g[3].tolist() == [0.0, 0.0]
+    assert abs(g[1, 0] - 1.0 / (1.0 + math.exp(-3.0))) < 1e-15
+    # every expert takes exactly C tokens: the load is balanced by construction
+    assert mask.sum(axis=0).tolist() == [2, 2]
+    disp = O.expert_choice_dispatch(mask)
+    # slots t*E + e: expert 0 holds t0, t1 (slots 0, 2); expert 1 holds t0, t2 (1, 5)
+    assert disp["sorted_slot"].tolist() == [0, 2, 1, 5]
+    assert disp["slot_row"].tolist() == [0, 2, 1, -1, -1, 3, -1, -1]
+    assert disp["offsets"].tolist() == [0, 2, 4]
+
+
+@settings(max_examples=30, deadline=None)
+@given(st.data())
+def test_expert_choice_brute_force(data):
+    # the taken set of each expert maximises the sum of its scores over all
+    # C-subsets of tokens (unique for continuous random scores)
+    import itertools
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    T = data.draw(st.integers(1, 8))
+    E = data.draw(st.integers(1, 4))
+    C = data.draw(st.integers(0, T + 2))
+    score = data.draw(st.sampled_from(["softmax", "sigmoid"]))
+    lg = rng.normal(size=(T, E)) * 2.0
+    mask, g, p = O.expert_choice(lg, score, C)
+    take = min(C, T)
+    for e in range(E):
+        best = max(itertools.combinations(range(T), take), key=lambda S: sum(p[list(S), e]))
+        assert sorted(np.flatnonzero(mask[:, e]).tolist()) == sorted(best)
+    assert (mask.sum(axis=0) == take).all()
+    assert np.array_equal(g, np.where(mask, p, 0.0))
+    disp = O.expert_choice_dispatch(mask)
+    ss, sr = disp["sorted_slot"], disp["slot_row"]
+    assert np.array_equal(sr[ss], np.arange(ss.size))
+    assert (sr >= 0).sum() == E * take
+    assert disp["offsets"].tolist() == [e * take for e in range(E + 1)]
+
+
+def test_expert_choice_single_expert_takes_first_tokens():
+    # E = 1 with a softmax router: every token scores exactly 1, so the tie
+    # rule alone decides: the first C tokens in batch order
+    mask, g, _ = O.expert_choice(np.random.default_rng(3).normal(size=(9, 1)), "softmax", 4)
+    assert np.flatnonzero(mask[:, 0]).tolist() == [0, 1, 2, 3]
+    assert (g[:4, 0] == 1.0).all()
+
+
+def test_expert_choice_full_capacity_is_dense_mixture():
+    # C >= T: every expert takes every token, so the layer is the dense
+    # mixture y = sum_e p_e E_e(x) over all experts, written out here
+    rng = np.random.default_rng(11)
+    X, Wg, W1, W3, W2, sh = _rand_layer(rng, 6, 5, 3, 4, True)
+    Y = O.forward_expert_choice(X, Wg, W1, W3, W2, C=6, shared=sh)["Y"]
+    lg = X @ Wg
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+
+    def swiglu(a, b, c):
+        z = X @ a
+        return ((z / (1.0 + np.exp(-z))) * (X @ b)) @ c
+    dense = sum(p[:, e:e + 1] * swiglu(W1[e], W3[e], W2[e]) for e in range(3)) + swiglu(*sh)
+    assert np.allclose(Y, dense, atol=1e-13, rtol=0)
+
+
+def test_expert_choice_output_depends_on_the_batch():
+    # [Book 14.2.3]: under expert choice a token's output depends on the other
+    # tokens of the batch; under token choice it does not.  One sigmoid
+    # expert with C = 1: token 0 (logit 0.5) is taken while token 1's logit
+    # is 0; raise token 1's logit to 1 and token 0 loses its expert.
+    rng = np.random.default_rng(4)
+    W1, W3, W2 = rng.normal(size=(1, 1, 2)), rng.normal(size=(1, 1, 2)), rng.normal(size=(1, 2, 1))
+    Wg = np.array([[1.0]])
+    a = O.forward_expert_choice(np.array([[0.5], [0.0]]), Wg, W1, W3, W2, C=1,
+                                score_func="sigmoid")["Y"]
+    b = O.forward_expert_choice(np.array([[0.5], [1.0]]), Wg, W1, W3, W2, C=1,
+                                score_func="sigmoid")["Y"]
+    y0 = O.expert_ffn(np.array([[0.5]]), W1[0], W3[0], W2[0])[0, 0]
+    assert abs(a[0, 0] - y0 / (1.0 + math.exp(-0.5))) < 1e-15 and a[1, 0] == 0.0
+    assert b[0, 0] == 0.0 and b[1, 0] != 0.0
+    # token choice over two experts: token 0's output ignores token 1
+    Wg2 = np.array([[1.0, -1.0]])
+    W1b, W3b, W2b = (np.concatenate([W, W * 0.5]) for W in (W1, W3, W2))
+    ta = O.forward(np.array([[0.5], [0.0]]), Wg2, W1b, W3b, W2b, k=1)["Y"]
+    tb = O.forward(np.array([[0.5], [1.0]]), Wg2, W1b, W3b, W2b, k=1)["Y"]
+    assert ta[0, 0] == tb[0, 0]
+
+
+@settings(max_examples=15, deadline=None)
+@given(st.data())
+def test_expert_choice_tiers_agree(data):
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    T = data.draw(st.integers(1, 10))
+    d = data.draw(st.integers(1, 5))
+    E = data.draw(st.integers(1, 5))
+    F = data.draw(st.integers(1, 4))
+    C = data.draw(st.integers(0, T + 1))
+    score = data.draw(st.sampled_from(["softmax", "sigmoid"]))
+    shared = data.draw(st.booleans())
+    X, Wg, W1, W3, W2, sh = _rand_layer(rng, T, d, E, F, shared)
+    offset = rng.normal(size=E) if data.draw(st.booleans()) else None
+    kw = dict(C=C, score_func=score, offset=offset, shared=sh)
+    y1 = O.forward_expert_choice(X, Wg, W1, W3, W2, **kw)["Y"]
+    y0 = O.forward_expert_choice_loop(X, Wg, W1, W3, W2, **kw)
+    assert np.abs(y1 - y0).max() <= 1e-12 * max(1.0, np.abs(y0).max())
+
+
+def test_expert_choice_pins_catch_planted_mistakes(monkeypatch):
+    good = O.expert_choice
+    # 9. lowest scores taken instead of the highest
+    monkeypatch.setattr(O, "expert_choice",
+                        lambda lg, sf, C: good(-np.asarray(lg, np.float64), sf, C))
+    with pytest.raises(AssertionError):
+        test_expert_choice_hand_example()
+    # 10. ties resolved towards the higher token index
+    def ties_high(lg, sf, C):
+        m, g, p = good(np.asarray(lg, np.float64)[::-1], sf, C)
+        return m[::-1], g[::-1], p[::-1]
+    monkeypatch.setattr(O, "expert_choice", ties_high)
+    with pytest.raises(AssertionError):
+        test_expert_choice_single_expert_takes_first_tokens()
+    # 11. gates renormalised per token as in token choice
+    def renormed(lg, sf, C):
+        m, g, p = good(lg, sf, C)
+        s = g.sum(axis=1, keepdims=True)
+        return m, np.where(s > 0, g / np.where(s > 0, s, 1.0), 0.0), p
+    monkeypatch.setattr(O, "expert_choice", renormed)
+    with pytest.raises(AssertionError):
+        test_expert_choice_hand_example()
+    monkeypatch.setattr(O, "expert_choice", good)
