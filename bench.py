@@ -97,10 +97,15 @@ def cpu_baseline(w, inp, target_s=15.0):
     X = f64(inp["X"])
 
     def run(S):
-        cap = O.capacity(w.cf, S, w.k, w.E) if w.cf else None
         t0 = time.perf_counter()
-        O.forward(X[:S], Wg, W1, W3, W2, k=w.k, score_func=w.score, renorm=w.renorm,
-                  bias=bias, offset=off, cap=cap, shared=sh, bf16_h=(w.dtype == "bf16"))
+        if w.routing == "expert":
+            C = min(S, O.capacity(w.cf or 1.0, S, w.k, w.E))
+            O.forward_expert_choice(X[:S], Wg, W1, W3, W2, C=C, score_func=w.score, offset=off,
+                                    shared=sh, bf16_h=(w.dtype == "bf16"))
+        else:
+            cap = O.capacity(w.cf, S, w.k, w.E) if w.cf else None
+            O.forward(X[:S], Wg, W1, W3, W2, k=w.k, score_func=w.score, renorm=w.renorm,
+                      bias=bias, offset=off, cap=cap, shared=sh, bf16_h=(w.dtype == "bf16"))
         return time.perf_counter() - t0
     # grow the sample (doubling) until one run takes >= target_s / 4, then
     # repeat it so the timed CPU work is about target_s
@@ -170,9 +175,11 @@ def main():
     torch.cuda.synchronize()
     kept = probe.aux["offsets"].diff().cpu().numpy()
     n_kept = int(probe.aux["n_kept"].item())
-    balance = float(probe.aux["balance"].item())
-    health = dict(zip(("token_entropy", "load_entropy", "load_cv", "drop_rate"),
-                      (float(v) for v in probe.aux["health"].cpu().tolist())))
+    balance = health = None
+    if "balance" in probe.aux:        # top-k routing only
+        balance = float(probe.aux["balance"].item())
+        health = dict(zip(("token_entropy", "load_entropy", "load_cv", "drop_rate"),
+                          (float(v) for v in probe.aux["health"].cpu().tolist())))
     del probe
     torch.cuda.empty_cache()
     fwd = moe.Forward(layer, inp["X"], aux=False)
@@ -239,6 +246,7 @@ def main():
                    "expert_weights": "fp8 e4m3 + per-channel fp32 scales" if w.wdtype == "fp8"
                    else w.dtype,
                    "n_shared": w.n_shared, "router": w.score, "capacity_factor": w.cf,
+                   "routing": "expert choice" if w.routing == "expert" else "top-k",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"flops": layer_flops, "bytes": layer_bytes,

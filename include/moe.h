@@ -6,6 +6,7 @@
  * Knowledge Map page "Mixture of Experts (MoE)":
  *   score     l = X W_g (+ optional per-expert offset)          -> moe_route
  *   select    top-k, gates renormalised inside the chosen set   -> moe_route
+ *             or every expert takes its top-C tokens  -> moe_route_expert_choice
  *   dispatch  stable sort of token slots by expert, capacity    -> moe_dispatch
  *   experts   grouped SwiGLU GEMM, m_i rows per expert          -> moe_grouped_ffn
  *   combine   gate-weighted sum through the inverse permutation -> moe_combine
@@ -26,7 +27,7 @@
  *   - dtype: MOE_BF16 (bf16 storage, fp32 accumulation, fp32 router scores)
  *     or MOE_F32.  Integers are int32.
  *   - Supported shapes: d and F multiples of 128, 1 <= E <= 256, 1 <= k <= E,
- *     k <= 16, T >= 0.  Otherwise MOE_EUNSUPPORTED.
+ *     k <= 16 (top-k routing), T >= 0.  Otherwise MOE_EUNSUPPORTED.
  *   - Errors: arguments are validated on the host before anything is
  *     launched; a negative return means nothing was enqueued (except
  *     MOE_EHIP, which reports a failed launch).  moe_last_error() returns a
@@ -48,6 +49,9 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
  * scale per output channel (W = value(code) * scale; bf16 layers only). */
 enum moe_wtype { MOE_W_DTYPE = 0, MOE_W_FP8 = 1 };
 enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+/* Who chooses: every token its top-k experts, or every expert its top-C
+ * tokens (moe_route_expert_choice). */
+enum moe_routing { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 };
 enum moe_status {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* invalid argument (null pointer, k > E, ...)     */
@@ -100,6 +104,37 @@ int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
               int k, int renorm, int n_group, int topk_group, float* logits,
               int32_t* topk_ids, float* topk_w, float* prob_sum, void* ws,
               size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------- expert-choice route --
+ * Expert-choice routing (LLM Internals 14.2.3, the expert-choice paradigm:
+ * every expert takes a fixed number of tokens from the batch; oscine.io
+ * "MoE 03: efficiency frontiers", expert-choice routing: each expert picks
+ * the C tokens it scores highest).  Scores as in moe_route: the full-row
+ * softmax over the E experts (MOE_SOFTMAX) or the sigmoid affinity
+ * (MOE_SIGMOID); no bias, no groups.  Expert e takes the Ce = min(C, T)
+ * tokens with the highest score in column e, ties to the lower token index;
+ * the decision is taken on fp64 keys (log p, or the logit for sigmoid).  A
+ * token may be taken by several experts or by none.  Slot s = t*E + e.
+ *   X[T][d], Wg[E][d] (dtype); logit_offset[E] fp32 or NULL; C >= 0.
+ * Outputs (device):
+ *   logits[T][E]      fp32 logits (with the offset) or NULL
+ *   offsets[E+1]      int32, offsets[e] = e * Ce
+ *   sorted_slot[E*Ce] int32 slots t*E + e of the taken tokens, grouped by
+ *                     expert, ascending token index inside; or NULL
+ *   slot_row[T*E]     int32 row of slot t*E + e in that order, -1 if the
+ *                     expert did not take the token
+ *   gates[T*E]        fp32 score of the taken slots (no renormalisation:
+ *                     the number of experts per token varies), 0 elsewhere
+ * Feed offsets / sorted_slot (row r's token = sorted_slot[r] / E) to
+ * moe_grouped_ffn and slot_row / gates with k = E to moe_combine.
+ */
+size_t moe_route_expert_choice_workspace_size(int64_t T, int d, int E);
+int moe_route_expert_choice(const void* X, int dtype, int64_t T, int d,
+                            const void* Wg, int E, const float* logit_offset,
+                            int score, int64_t C, float* logits,
+                            int32_t* offsets, int32_t* sorted_slot,
+                            int32_t* slot_row, float* gates, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------- dispatch --
  * Dispatch permutation with an optional capacity drop (LLM Internals 14.2.1
@@ -166,6 +201,7 @@ int moe_grouped_ffn_fp8(const void* A, const int32_t* row_token,
  *             + shared[t][:]          (if shared != NULL)
  * accumulated in fp32 and rounded once to dtype.  Dropped slots add nothing.
  *   Yrows[.][d] fp32, slot_row[T*k], topk_w[T][k] fp32, shared[T][d] fp32.
+ * 1 <= k <= 256 (expert-choice routing passes k = E).
  */
 int moe_combine(const float* Yrows, const int32_t* slot_row,
                 const float* topk_w, int64_t T, int k, int d,
@@ -207,6 +243,16 @@ typedef struct moe_layer {
   const float* Ws2_scale;  /* [d]                                            */
   int n_group;             /* group-limited routing as in moe_route; <= 1 off */
   int topk_group;
+  int routing;             /* MOE_TOKEN_CHOICE, or MOE_EXPERT_CHOICE: every
+                              expert takes C = min(T, moe_capacity(cf, T, k,
+                              E)) tokens (cf = 1 when capacity_factor <= 0;
+                              k is then the mean experts per token), as in
+                              moe_route_expert_choice.  Needs renorm = 0, no
+                              bias and n_group <= 1.  moe_aux then holds
+                              slot_row and topk_w as [T][E] (slot t*E + e),
+                              sorted_slot as [E*C], counts[e] = C, n_kept =
+                              E*C; topk_ids, prob_sum, balance and health must
+                              be NULL.                                        */
 } moe_layer;
 
 /* Optional device outputs of moe_forward; any member may be NULL. */
@@ -220,7 +266,8 @@ typedef struct moe_aux {
   int32_t* sorted_slot;    /* [T*k]   */
   int32_t* slot_row;       /* [T*k]   */
   int32_t* n_kept;         /* [1]     */
-  float* Yrows;            /* [T*k + n_shared*T][d] expert output rows       */
+  float* Yrows;            /* [R_max + n_shared*T][d] expert output rows,
+                              R_max = T*k (E*C with expert choice)          */
   double* balance;         /* [1]     */
   double* health;          /* [4] router health (LLM Internals 14.2.3's three
                               signals, AI Knowledge Map's load CV): mean

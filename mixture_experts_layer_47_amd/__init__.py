@@ -5,8 +5,8 @@ this package is its Python binding plus the seeded synthetic workloads.
 """
 from ._lib import (MoeError, MoeLayer, Forward, balance, capacity, combine, dispatch,  # noqa: F401
                    forward, grouped_ffn, last_error, layer_from_inputs, lib, route,
-                   timing_enable, timing_read)
+                   route_expert_choice, timing_enable, timing_read)
 
 __all__ = ["MoeError", "MoeLayer", "Forward", "balance", "capacity", "combine", "dispatch",
            "forward", "grouped_ffn", "last_error", "layer_from_inputs", "lib", "route",
-           "timing_enable", "timing_read"]
+           "route_expert_choice", "timing_enable", "timing_read"]

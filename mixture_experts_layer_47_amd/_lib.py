@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_W_DTYPE, MOE_W_FP8 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
           -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
 EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_route",
+           "moe_route_expert_choice_workspace_size", "moe_route_expert_choice",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_fp8",
            "moe_combine",
@@ -49,7 +51,8 @@ class MoeLayerC(ctypes.Structure):
                 ("W1_scale", ctypes.c_void_p), ("W3_scale", ctypes.c_void_p),
                 ("W2_scale", ctypes.c_void_p), ("Ws1_scale", ctypes.c_void_p),
                 ("Ws3_scale", ctypes.c_void_p), ("Ws2_scale", ctypes.c_void_p),
-                ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int)]
+                ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
+                ("routing", ctypes.c_int)]
 
 
 class MoeAuxC(ctypes.Structure):
@@ -68,6 +71,9 @@ def _declare(L):
         "moe_capacity": (I64, [D, I64, I, I]),
         "moe_route_workspace_size": (SZ, [I64, I, I]),
         "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_route_expert_choice_workspace_size": (SZ, [I64, I, I]),
+        "moe_route_expert_choice": (I, [P, I, I64, I, P, I, P, I, I64, P, P, P, P, P, P, SZ,
+                                        P]),
         "moe_dispatch_workspace_size": (SZ, [I64, I, I]),
         "moe_dispatch": (I, [P, I64, I, I, I64, P, P, P, P, P, P, I, I, P, P, SZ, P]),
         "moe_grouped_ffn_workspace_size": (SZ, [I64, I, I, I, I]),
@@ -163,6 +169,32 @@ def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
     return {"ids": ids, "w": w, "logits": lg, "prob_sum": ps}
 
 
+def route_expert_choice(X, Wg, C, score="softmax", offset=None, want_logits=True):
+    """Every expert takes its min(C, T) highest-scoring tokens.  Returns
+    offsets [E+1], sorted_slot [E*Ce] (slot t*E + e), slot_row and gates
+    [T, E], and the logits."""
+    T, d = X.shape
+    E = Wg.shape[0]
+    dev = X.device
+    Ce = min(int(C), T)
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = {"offsets": torch.empty(E + 1, **i32),
+           "sorted_slot": torch.empty(max(E * Ce, 1), **i32),
+           "slot_row": torch.empty((T, E), **i32),
+           "gates": torch.empty((T, E), dtype=torch.float32, device=dev),
+           "logits": torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits
+           else None}
+    L = lib()
+    ws = _workspace(L.moe_route_expert_choice_workspace_size(T, d, E), dev)
+    _check(L.moe_route_expert_choice(_ptr(X), _dtype_code(X), T, d, _ptr(Wg), E, _ptr(offset),
+                                     _score_code(score), int(C), _ptr(out["logits"]),
+                                     _ptr(out["offsets"]), _ptr(out["sorted_slot"]),
+                                     _ptr(out["slot_row"]), _ptr(out["gates"]), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    out["sorted_slot"] = out["sorted_slot"][:E * Ce]
+    return out
+
+
 def dispatch(ids, E, capacity=0, X=None):
     T, k = ids.shape
     dev = ids.device
@@ -240,6 +272,13 @@ class MoeLayer:
     shared_scales: Optional[tuple] = None  # and the shared expert's three scale vectors
     n_group: int = 1                       # group-limited routing (1 = off)
     topk_group: int = 1
+    routing: str = "token"                 # "token" (top-k) or "expert" (expert choice)
+
+    def expert_capacity(self, T: int) -> int:
+        """Tokens per expert under expert-choice routing: min(T, C)."""
+        E = self.W1.shape[0]
+        cf = self.capacity_factor if self.capacity_factor and self.capacity_factor > 0 else 1.0
+        return min(T, capacity(cf, T, self.k, E)) if T > 0 else 0
 
     def cstruct(self) -> MoeLayerC:
         E, F, d = self.W1.shape
@@ -253,7 +292,8 @@ class MoeLayer:
             self.Wg.data_ptr(), _addr(self.bias), _addr(self.offset), self.W1.data_ptr(),
             self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]),
             MOE_W_FP8 if fp8 else MOE_W_DTYPE, _addr(q[0]), _addr(q[1]), _addr(q[2]),
-            _addr(qs[0]), _addr(qs[1]), _addr(qs[2]), int(self.n_group), int(self.topk_group))
+            _addr(qs[0]), _addr(qs[1]), _addr(qs[2]), int(self.n_group), int(self.topk_group),
+            {"token": MOE_TOKEN_CHOICE, "expert": MOE_EXPERT_CHOICE}[self.routing])
         return self._keep
 
 
@@ -268,7 +308,7 @@ def layer_from_inputs(inp: dict) -> MoeLayer:
                     score=w.score, renorm=w.renorm, bias=inp["bias"], offset=inp["offset"],
                     shared=inp["shared"], capacity_factor=w.cf or 0.0,
                     scales=inp.get("scales"), shared_scales=inp.get("shared_scales"),
-                    n_group=w.n_group, topk_group=w.topk_group)
+                    n_group=w.n_group, topk_group=w.topk_group, routing=w.routing)
 
 
 class Forward:
@@ -287,7 +327,22 @@ class Forward:
         self.Y = torch.empty((T, d), dtype=X.dtype, device=dev)
         self.aux = {}
         self.caux = MoeAuxC()
-        if aux:
+        if aux and layer.routing == "expert":
+            i32 = dict(dtype=torch.int32, device=dev)
+            Ce = layer.expert_capacity(T)
+            rows = E * Ce + (T if layer.shared else 0)
+            self.aux = {
+                "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+                "topk_w": torch.empty((T, E), dtype=torch.float32, device=dev),
+                "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+                "sorted_slot": torch.empty(max(E * Ce, 1), **i32),
+                "slot_row": torch.empty((T, E), **i32),
+                "n_kept": torch.empty(1, **i32),
+                "Yrows": torch.empty((max(rows, 1), d), dtype=torch.float32, device=dev),
+            }
+            for n, t in self.aux.items():
+                setattr(self.caux, n, t.data_ptr())
+        elif aux:
             i32 = dict(dtype=torch.int32, device=dev)
             rows = T * k + (T if layer.shared else 0)
             self.aux = {

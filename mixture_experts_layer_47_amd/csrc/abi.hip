@@ -142,6 +142,33 @@ int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
                     "moe_route");
 }
 
+// ------------------------------------------------------ expert-choice route
+size_t moe_route_expert_choice_workspace_size(int64_t T, int d, int E) {
+  if (T < 0 || d <= 0 || E <= 0) return 0;
+  return route_ec_ws_bytes(T, d, E);
+}
+
+int moe_route_expert_choice(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
+                            const float* logit_offset, int score, int64_t C, float* logits,
+                            int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                            float* gates, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((rc = check_router_dims(T, d, E, 1))) return rc;
+  MOE_REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_EINVAL, "score %d unknown", score);
+  MOE_REQUIRE(C >= 0, MOE_EINVAL, "C = %lld < 0", (long long)C);
+  MOE_REQUIRE(T * (int64_t)E + T <= INT32_MAX, MOE_EUNSUPPORTED, "T*E too large for int32 indices");
+  MOE_REQUIRE(offsets != nullptr, MOE_EINVAL, "NULL offsets");
+  MOE_REQUIRE(T == 0 || (X && Wg && slot_row && gates), MOE_EINVAL,
+              "NULL X, Wg, slot_row or gates");
+  if ((rc = check_ws(ws, ws_bytes, route_ec_ws_bytes(T, d, E)))) return rc;
+  const int Ce = (int)(C < T ? C : T);
+  return hip_status(launch_route_ec(X, dtype, T, d, Wg, E, logit_offset, score, Ce, logits,
+                                    offsets, nullptr, nullptr, sorted_slot, slot_row, gates,
+                                    nullptr, 0, ws, (hipStream_t)stream),
+                    "moe_route_expert_choice");
+}
+
 // ---------------------------------------------------------------- dispatch
 size_t moe_dispatch_workspace_size(int64_t T, int k, int E) {
   if (T < 0 || k < 1 || E < 1) return 0;
@@ -233,8 +260,9 @@ int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w
   int rc;
   if ((rc = check_dtype(dtype))) return rc;
   MOE_REQUIRE(T >= 0 && k >= 1, MOE_EINVAL, "need T >= 0 and k >= 1");
-  MOE_REQUIRE(k <= 16, MOE_EUNSUPPORTED, "k = %d > 16 is not supported", k);
+  MOE_REQUIRE(k <= 256, MOE_EUNSUPPORTED, "k = %d > 256 is not supported", k);
   MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a positive multiple of 128", d);
+  MOE_REQUIRE(T * (int64_t)k <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large");
   MOE_REQUIRE(T == 0 || (Yrows && slot_row && topk_w && Y), MOE_EINVAL,
               "NULL Yrows, slot_row, topk_w or Y");
   return hip_status(launch_combine(Yrows, nullptr, slot_row, topk_w, T, k, d, shared, nullptr, Y,
@@ -257,10 +285,26 @@ struct FwdLayout {
       total;
 };
 
+bool expert_choice(const moe_layer* L) { return L->routing == MOE_EXPERT_CHOICE; }
+
+// Tokens each expert takes under expert-choice routing: min(T, C) with
+// C = ceil(cf * T * k / E), cf = 1 when no factor is set.  Factors outside
+// moe_capacity's range give T (an upper bound; check_layer rejects them).
+int64_t ec_capacity(const moe_layer* L, int64_t T) {
+  const double cf = L->capacity_factor > 0 ? L->capacity_factor : 1.0;
+  if (!(cf >= 1e-15 && cf <= 1e15)) return T;
+  const long double est = (long double)cf * (long double)T * L->k / L->E;
+  if (!(est < (long double)T)) return T;
+  const int64_t c = exact_capacity(cf, T, L->k, L->E);
+  return c < T ? c : T;
+}
+
 FwdLayout fwd_layout(const moe_layer* L, int64_t T) {
   FwdLayout o;
-  const int64_t Tk = T * (int64_t)L->k;
-  const int64_t rows = Tk + (L->n_shared ? T : 0);
+  const bool ec = expert_choice(L);
+  const int64_t slots = T * (int64_t)(ec ? L->E : L->k);          // [T][k] or [T][E]
+  const int64_t routed = ec ? L->E * ec_capacity(L, T) : T * (int64_t)L->k;
+  const int64_t rows = routed + (L->n_shared ? T : 0);
   const int G = L->E + (L->n_shared ? 1 : 0);
   size_t at = 0;
   auto take = [&](size_t bytes) {
@@ -268,15 +312,15 @@ FwdLayout fwd_layout(const moe_layer* L, int64_t T) {
     at += align256(bytes > 0 ? bytes : 1);
     return here;
   };
-  o.route = take(route_ws_bytes(T, L->d, L->E));
-  o.ids = take((size_t)Tk * 4);
-  o.w = take((size_t)Tk * 4);
+  o.route = take(ec ? route_ec_ws_bytes(T, L->d, L->E) : route_ws_bytes(T, L->d, L->E));
+  o.ids = take((size_t)slots * 4);
+  o.w = take((size_t)slots * 4);
   o.psum = take((size_t)L->E * 4);
   o.counts = take((size_t)L->E * 4);
   o.offsets = take((size_t)(L->E + 2) * 4);
   o.nkept = take(4);
-  o.sorted = take((size_t)Tk * 4);
-  o.slotrow = take((size_t)Tk * 4);
+  o.sorted = take((size_t)routed * 4);
+  o.slotrow = take((size_t)slots * 4);
   o.rowtok = take((size_t)rows * 4);
   o.hist = take(dispatch_ws_bytes(T, L->k, L->E));
   o.ent = take((size_t)MOE_CEIL_DIV(T, 4) * 4);
@@ -303,6 +347,17 @@ int check_layer(const moe_layer* L, int64_t T) {
   MOE_REQUIRE(L->wtype == MOE_W_DTYPE || L->wtype == MOE_W_FP8, MOE_EINVAL, "wtype %d unknown",
               L->wtype);
   if ((rc = check_groups(L->E, L->k, L->n_group, L->topk_group))) return rc;
+  MOE_REQUIRE(L->routing == MOE_TOKEN_CHOICE || L->routing == MOE_EXPERT_CHOICE, MOE_EINVAL,
+              "routing %d unknown", L->routing);
+  if (expert_choice(L)) {
+    MOE_REQUIRE(!L->renorm && !L->bias && L->n_group <= 1, MOE_EINVAL,
+                "expert-choice routing takes no renorm, bias or groups");
+    MOE_REQUIRE(!(L->capacity_factor > 0) ||
+                    (L->capacity_factor >= 1e-15 && L->capacity_factor <= 1e15),
+                MOE_EINVAL, "capacity factor %g out of range", L->capacity_factor);
+    MOE_REQUIRE(T * (int64_t)L->E + T <= INT32_MAX, MOE_EUNSUPPORTED,
+                "T*E too large for int32 indices");
+  }
   if (L->wtype == MOE_W_FP8) {
     MOE_REQUIRE(L->dtype == MOE_BF16, MOE_EUNSUPPORTED, "FP8 weights need a bf16 layer");
     MOE_REQUIRE(L->W1_scale && L->W3_scale && L->W2_scale, MOE_EINVAL, "NULL weight scales");
@@ -310,6 +365,54 @@ int check_layer(const moe_layer* L, int64_t T) {
                 "NULL shared-expert weight scales");
   }
   return MOE_OK;
+}
+}  // namespace
+
+namespace {
+// moe_forward with expert-choice routing: route and select in one step
+// (offsets are e * C, known on the host), then the same grouped SwiGLU and
+// a combine over the E slots of every token.
+int forward_expert_choice(const moe_layer* L, const void* X, int64_t T, void* Y,
+                          const moe_aux* aux, const FwdLayout& o, void* ws, void* stream) {
+  moe_aux none;
+  memset(&none, 0, sizeof(none));
+  const moe_aux& a = aux ? *aux : none;
+  MOE_REQUIRE(!a.topk_ids && !a.prob_sum && !a.balance && !a.health, MOE_EINVAL,
+              "topk_ids, prob_sum, balance and health are top-k routing outputs; pass NULL "
+              "with expert-choice routing");
+  const int64_t C = ec_capacity(L, T);
+  char* w = (char*)ws;
+  auto pick = [&](void* user, size_t off) { return user ? user : (void*)(w + off); };
+  float* gw = (float*)pick(a.topk_w, o.w);
+  int32_t* offsets = (int32_t*)(w + o.offsets);            // E + 2 entries
+  int32_t* nkept = (int32_t*)pick(a.n_kept, o.nkept);
+  int32_t* slotrow = (int32_t*)pick(a.slot_row, o.slotrow);
+  int32_t* rowtok = (int32_t*)(w + o.rowtok);
+  float* yrows = (float*)pick(a.Yrows, o.yrows);
+  hipStream_t s = (hipStream_t)stream;
+  const int ns = L->n_shared ? 1 : 0;
+
+  timing_mark("begin", s, 1);
+  hipError_t e = launch_route_ec(X, L->dtype, T, L->d, L->Wg, L->E, L->logit_offset, L->score,
+                                 (int)C, a.logits, offsets, a.counts, nkept, a.sorted_slot,
+                                 slotrow, gw, rowtok, ns ? (int)T : 0, w + o.route, s);
+  timing_mark("route", s);
+  const float* part2 = nullptr;
+  const WeightScales q{L->W1_scale, L->W3_scale, L->W2_scale, L->Ws1_scale, L->Ws3_scale,
+                       L->Ws2_scale};
+  if (e == hipSuccess)
+    e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
+                           L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, L->E * C + ns * T,
+                           yrows, w + o.ffn, s, a.Yrows != nullptr, &part2,
+                           L->wtype == MOE_W_FP8 ? &q : nullptr);
+  if (e == hipSuccess)
+    e = launch_combine(yrows, part2, slotrow, gw, T, L->E, L->d, nullptr, ns ? nkept : nullptr,
+                       Y, L->dtype, s);
+  timing_mark("combine", s);
+  if (e == hipSuccess && a.offsets)
+    e = hipMemcpyAsync(a.offsets, offsets, (size_t)(L->E + 1) * 4, hipMemcpyDeviceToDevice, s);
+  timing_mark("aux", s);
+  return hip_status(e, "moe_forward");
 }
 }  // namespace
 
@@ -325,6 +428,7 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   MOE_REQUIRE(T == 0 || (X && Y), MOE_EINVAL, "NULL X or Y");
   const FwdLayout o = fwd_layout(L, T);
   if ((rc = check_ws(ws, ws_bytes, o.total))) return rc;
+  if (expert_choice(L)) return forward_expert_choice(L, X, T, Y, aux, o, ws, stream);
   int64_t cap = 0;
   if (L->capacity_factor > 0) {
     cap = moe_capacity(L->capacity_factor, T, L->k, L->E);

@@ -3,7 +3,9 @@
 // read back through the inverse permutation (slot_row), plus the shared
 // expert's row.  Dropped slots (row -1) add nothing.  fp32 accumulation in a
 // fixed order (j = 0..k-1, then the shared row), one rounding to the output
-// type, no atomics.
+// type, no atomics.  k may reach 256 (expert-choice routing passes k = E
+// with one slot per expert); the kept slots are first compacted in LDS in
+// slot order, so the sum only visits them.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,11 +20,27 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
                                                  const int32_t* __restrict__ shared_row0,
                                                  OutT* __restrict__ Y) {
   const int t = blockIdx.x;
-  __shared__ int32_t rows[16];
-  __shared__ float gw[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int32_t rows[256];
+  __shared__ float gw[256];
+  __shared__ int nw[4];
+  int32_t r = -1;
+  float g = 0.f;
   if (threadIdx.x < (unsigned)k) {
-    rows[threadIdx.x] = slot_row[(size_t)t * k + threadIdx.x];
-    gw[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    r = slot_row[(size_t)t * k + threadIdx.x];
+    g = w[(size_t)t * k + threadIdx.x];
+  }
+  const uint64_t kept = __ballot(r >= 0);
+  if (lane == 0) nw[wave] = __popcll(kept);
+  __syncthreads();
+  int at = 0;
+  for (int i = 0; i < wave; ++i) at += nw[i];
+  const int n = (nw[0] + nw[1]) + (nw[2] + nw[3]);
+  if (r >= 0) {
+    const uint64_t below = lane ? (kept & (~0ull >> (64 - lane))) : 0ull;
+    at += __popcll(below);
+    rows[at] = r;
+    gw[at] = g;
   }
   __syncthreads();
   const float* sh = nullptr;
@@ -35,16 +53,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
   }
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < n; ++j) {
       const int r = rows[j];
-      if (r < 0) continue;
       float4 y = *(const float4*)(Yrows + (size_t)r * d + c);
       if (Yrows2) {   // K-split partials are summed first, in split order
         const float4 y2 = *(const float4*)(Yrows2 + (size_t)r * d + c);
         y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
       }
-      const float g = gw[j];
-      acc.x += g * y.x; acc.y += g * y.y; acc.z += g * y.z; acc.w += g * y.w;
+      const float gj = gw[j];
+      acc.x += gj * y.x; acc.y += gj * y.y; acc.z += gj * y.z; acc.w += gj * y.w;
     }
     if (sh) {
       float4 y = *(const float4*)(sh + c);

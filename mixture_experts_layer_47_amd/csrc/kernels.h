@@ -21,6 +21,17 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
 hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
                                 const float* ent_part, int64_t T, int k, int E, double* out,
                                 hipStream_t s);
+// Expert-choice routing: every expert takes C (<= T) tokens.  Writes
+// offsets[E+1] (+ offsets[E+1] = E*C + tail_rows when tail_rows > 0),
+// slot_row and gates [T][E] (slot t*E + e; -1 / 0 where not taken) and,
+// when non-NULL, counts[E] (= C), n_kept (= E*C), sorted_slot[E*C],
+// row_token[E*C + tail_rows] (the tail rows map to tokens 0..tail_rows-1).
+size_t route_ec_ws_bytes(int64_t T, int d, int E);
+hipError_t launch_route_ec(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
+                           const float* offset, int score, int C, float* logits,
+                           int32_t* offsets, int32_t* counts, int32_t* n_kept,
+                           int32_t* sorted_slot, int32_t* slot_row, float* gates,
+                           int32_t* row_token, int tail_rows, void* ws, hipStream_t s);
 hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E,
                           double* out, hipStream_t s);
 

@@ -322,6 +322,193 @@ __global__ __launch_bounds__(256) void k_router_health(const int32_t* __restrict
   }
 }
 
+// --------------------------------------------------------------------------
+// Expert-choice routing (LLM Internals 14.2.3, the expert-choice paradigm;
+// oscine.io "MoE 03", expert-choice routing): expert e takes the C tokens
+// with the highest score in its column, ties to the lower token index.
+//
+// Scores: keysT[e][t] in fp64, the log of the full-row softmax probability
+// l - logsumexp(l) (same order as p), or the logit itself for a sigmoid
+// router (same order as s).  One wave per token; 16 tokens per block go
+// through LDS so that each expert's row of keys is written in 128-B runs.
+constexpr int kEcTok = 16;
+
+template <int NE>
+__global__ __launch_bounds__(256) void k_ec_scores(const float* __restrict__ part, int nsplit,
+                                                   int T_, int E,
+                                                   const float* __restrict__ offset, int score,
+                                                   float* __restrict__ logits,
+                                                   double* __restrict__ keysT) {
+  __shared__ double tile[kEcTok][NE * 64 + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kEcTok;
+  for (int r = 0; r < kEcTok / 4; ++r) {
+    const int tl = wave * (kEcTok / 4) + r;
+    const int t = t0 + tl;
+    const bool tok_ok = t < T_;
+    float l[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      float v = -INFINITY;
+      if (tok_ok && e < E) {
+        v = 0.f;
+        for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T_ + t) * E + e];
+        if (offset) v += offset[e];
+        if (logits) logits[(size_t)t * E + e] = v;
+      }
+      l[i] = v;
+    }
+    double lse = 0.0;
+    if (score == MOE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) m = fmaxf(m, l[i]);
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      double z = 0.0;
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (tok_ok && lane + 64 * i < E) z += exp((double)l[i] - (double)m);
+      for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+      lse = tok_ok ? (double)m + log(z) : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + 64 * i;
+      // + 0.0 turns a -0.0 key into +0.0, so equal keys have equal bits
+      if (e < E) tile[tl][e] = tok_ok ? ((double)l[i] - lse) + 0.0 : 0.0;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < E * kEcTok; idx += 256) {
+    const int e = idx / kEcTok, tl = idx % kEcTok;
+    if (t0 + tl < T_) keysT[(size_t)e * T_ + t0 + tl] = tile[tl][e];
+  }
+}
+
+// Order-preserving map of a finite double onto uint64.
+__device__ __forceinline__ uint64_t ord_key(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Selection: one 1024-thread block per expert.  An 8-pass MSB-first radix
+// select over the 64-bit keys finds the C-th largest key K and how many keys
+// equal to K to take (`need`); one ordered pass then takes every key > K and
+// the first `need` keys == K in token order, and compacts the taken tokens in
+// token order with block-wide ballot scans.  Integer-only decisions on the
+// fp64 keys: run-to-run identical.
+__global__ __launch_bounds__(1024) void k_ec_select(
+    const double* __restrict__ keysT, int T_, int E, int C, int score,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+    float* __restrict__ gates, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ counts,
+    int32_t* __restrict__ n_kept, int tail_rows) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const double* kk = keysT + (size_t)e * T_;
+  __shared__ int hist[256];
+  __shared__ int s_digit, s_above;
+  __shared__ int wsum[2][16];
+  if (tid == 0) {
+    offsets[e] = e * C;
+    if (counts) counts[e] = C;
+    if (e == 0) {
+      offsets[E] = E * C;
+      if (tail_rows > 0) offsets[E + 1] = E * C + tail_rows;
+      if (n_kept) n_kept[0] = E * C;
+    }
+  }
+  if (row_token)   // the shared expert's rows follow the E * C routed rows
+    for (int t = e * 1024 + tid; t < tail_rows; t += E * 1024) row_token[E * C + t] = t;
+
+  uint64_t prefix = 0, mask = 0;
+  int need = C;                       // 1 <= need <= #keys matching prefix
+  if (C > 0) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int t = tid; t < T_; t += 1024) {
+        const uint64_t u = ord_key(kk[t]);
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane L owns bins 255-4L .. 252-4L; counts run from the top bin down
+        int c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; tot += c[j]; }
+        int incl = tot;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int n = __shfl_up(incl, o);
+          if (lane >= o) incl += n;
+        }
+        int run = incl - tot;
+        if (run < need && need <= incl) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (run + c[j] >= need) { s_digit = 255 - 4 * lane - j; s_above = run; break; }
+            run += c[j];
+          }
+        }
+      }
+      __syncthreads();
+      need -= s_above;
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= 0xFFull << shift;
+    }
+  }
+
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int base_eq = 0, base_pos = 0;
+  for (int c0 = 0; c0 < T_; c0 += 1024) {
+    const int t = c0 + tid;
+    const bool v = t < T_;
+    const double key = v ? kk[t] : 0.0;
+    const uint64_t u = ord_key(key);
+    const bool gt = v && C > 0 && u > prefix;
+    const bool eq = v && C > 0 && u == prefix;
+    const uint64_t be = __ballot(eq);
+    if (lane == 0) wsum[0][wave] = __popcll(be);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int x = wsum[0][w];
+      pre += w < wave ? x : 0;
+      tot += x;
+    }
+    const bool take = gt || (eq && base_eq + pre + __popcll(be & lt) < need);
+    const uint64_t bt = __ballot(take);
+    if (lane == 0) wsum[1][wave] = __popcll(bt);
+    __syncthreads();
+    int pre2 = 0, tot2 = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int x = wsum[1][w];
+      pre2 += w < wave ? x : 0;
+      tot2 += x;
+    }
+    if (v) {
+      const size_t slot = (size_t)t * E + e;
+      if (take) {
+        const int row = e * C + base_pos + pre2 + __popcll(bt & lt);
+        const double g = score == MOE_SOFTMAX ? exp(key) : 1.0 / (1.0 + exp(-key));
+        if (sorted_slot) sorted_slot[row] = (int32_t)slot;
+        if (row_token) row_token[row] = t;
+        slot_row[slot] = row;
+        gates[slot] = (float)g;
+      } else {
+        slot_row[slot] = -1;
+        gates[slot] = 0.f;
+      }
+    }
+    base_eq += tot;
+    base_pos += tot2;
+    __syncthreads();                  // wsum is rewritten by the next chunk
+  }
+}
+
 // --------------------------------------------------------------- launchers
 // K-split of the logits: about one slice per 1024 of d.  On the tiled-GEMM
 // path it is doubled while that leaves fewer tiles than CUs, slices stay
@@ -348,6 +535,36 @@ size_t route_ws_bytes(int64_t T, int d, int E) {
   return b;
 }
 
+// Logit partials part[split][T][E] (the first region of ws); returns the
+// split through *split_out and the rest of ws through *rest.
+static hipError_t launch_logit_partials(const void* X, int dtype, int64_t T, int d,
+                                        const void* Wg, int E, void* ws, hipStream_t s,
+                                        float** part_out, int* split_out, char** rest) {
+  const int split = router_split(T, d, E, dtype);
+  const int kstep = 128;   // keep slices a multiple of both lane steps
+  const int dchunk = MOE_CEIL_DIV(MOE_CEIL_DIV(d, split), kstep) * kstep;
+  char* p = (char*)ws;
+  float* part = (float*)p;  p += align256((size_t)split * T * E * sizeof(float));
+  char* ps_region = p;      p += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));
+  *part_out = part;
+  *split_out = split;
+  *rest = ps_region;
+  if (router_gemm_ok(dtype, T, d, E, split)) {
+    // many experts: the LDS-tiled GEMM reads X once and W_g once per M-tile
+    return launch_router_gemm(X, Wg, T, d, E, split, part, p, s);
+  }
+  const int wpt = E > 48 ? 4 : E > 16 ? 2 : 1;   // waves per token group (divides 4)
+  dim3 g1((unsigned)MOE_CEIL_DIV(T, 16 * (4 / wpt)), (unsigned)MOE_CEIL_DIV(E, 16 * wpt),
+          (unsigned)split);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
+                       (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk, wpt);
+  else
+    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
+                       (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk, wpt);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
                         int E, const float* bias, const float* offset, int score,
                         int k, int renorm, int n_group, int topk_group, float* logits,
@@ -357,27 +574,12 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
   }
-  const int split = router_split(T, d, E, dtype);
-  const int kstep = 128;   // keep slices a multiple of both lane steps
-  const int dchunk = MOE_CEIL_DIV(MOE_CEIL_DIV(d, split), kstep) * kstep;
-  char* p = (char*)ws;
-  float* part = (float*)p;  p += align256((size_t)split * T * E * sizeof(float));
-  float* ps_part = (float*)p; p += align256((size_t)MOE_CEIL_DIV(T, 4) * E * sizeof(float));
-  if (router_gemm_ok(dtype, T, d, E, split)) {
-    // many experts: the LDS-tiled GEMM reads X once and W_g once per M-tile
-    hipError_t e = launch_router_gemm(X, Wg, T, d, E, split, part, p, s);
-    if (e != hipSuccess) return e;
-  } else {
-    const int wpt = E > 48 ? 4 : E > 16 ? 2 : 1;   // waves per token group (divides 4)
-    dim3 g1((unsigned)MOE_CEIL_DIV(T, 16 * (4 / wpt)), (unsigned)MOE_CEIL_DIV(E, 16 * wpt),
-            (unsigned)split);
-    if (dtype == MOE_BF16)
-      hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, s,
-                         (const uint16_t*)X, (const uint16_t*)Wg, part, (int)T, d, E, dchunk, wpt);
-    else
-      hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, s,
-                         (const float*)X, (const float*)Wg, part, (int)T, d, E, dchunk, wpt);
-  }
+  float* part;
+  int split;
+  char* rest;
+  hipError_t err = launch_logit_partials(X, dtype, T, d, Wg, E, ws, s, &part, &split, &rest);
+  if (err != hipSuccess) return err;
+  float* ps_part = (float*)rest;
   const int nblk = (int)MOE_CEIL_DIV(T, 4);
   float* psp = prob_sum ? ps_part : nullptr;
   const int ne = MOE_CEIL_DIV(E, 64);
@@ -408,6 +610,41 @@ hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
 hipError_t launch_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k,
                           int E, double* out, hipStream_t s) {
   hipLaunchKernelGGL(k_balance, dim3(1), dim3(256), 0, s, counts, prob_sum, T, k, E, out);
+  return hipGetLastError();
+}
+
+size_t route_ec_ws_bytes(int64_t T, int d, int E) {
+  return route_ws_bytes(T, d, E) + align256((size_t)T * E * sizeof(double));
+}
+
+hipError_t launch_route_ec(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
+                           const float* offset, int score, int C, float* logits,
+                           int32_t* offsets, int32_t* counts, int32_t* n_kept,
+                           int32_t* sorted_slot, int32_t* slot_row, float* gates,
+                           int32_t* row_token, int tail_rows, void* ws, hipStream_t s) {
+  double* keysT = (double*)((char*)ws + route_ws_bytes(T, d, E));
+  if (T > 0) {
+    float* part;
+    int split;
+    char* rest;
+    hipError_t err = launch_logit_partials(X, dtype, T, d, Wg, E, ws, s, &part, &split, &rest);
+    if (err != hipSuccess) return err;
+    const unsigned nb = (unsigned)MOE_CEIL_DIV(T, kEcTok);
+    const int ne = MOE_CEIL_DIV(E, 64);
+#define MOE_ECS(NE_)                                                                      \
+  hipLaunchKernelGGL(k_ec_scores<NE_>, dim3(nb), dim3(256), 0, s, part, split, (int)T, E, \
+                     offset, score, logits, keysT)
+    switch (ne) {
+      case 1: MOE_ECS(1); break;
+      case 2: MOE_ECS(2); break;
+      case 3: MOE_ECS(3); break;
+      default: MOE_ECS(4); break;
+    }
+#undef MOE_ECS
+  }
+  hipLaunchKernelGGL(k_ec_select, dim3(E), dim3(1024), 0, s, keysT, (int)T, E, C, score,
+                     sorted_slot, slot_row, gates, row_token, offsets, counts, n_kept,
+                     tail_rows);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ class Workload:
     wdtype: str = "same"           # "same" | "fp8" (E4M3 expert weights, bf16 layer)
     n_group: int = 1               # group-limited routing: groups of E / n_group experts
     topk_group: int = 1            # groups a token may use
+    routing: str = "token"         # "token" (top-k) | "expert" (each expert takes C tokens)
     seed: int = 0                  # seed of the weights
     x_seed: int | None = None      # seed of X (defaults to ``seed``)
     note: str = field(default="", compare=False)
@@ -95,6 +96,15 @@ for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
     WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", wdtype="fp8",
                                                  note=WORKLOADS[_n].note + ", FP8 weights")
 
+# Expert-choice routing on the Mixtral and DeepSeek-V3 shapes: every expert
+# takes C = T*k/E tokens (1024 and 128), the same number of rows as top-k.
+WORKLOADS["mixtral_prefill_ec"] = WORKLOADS["mixtral_prefill"].with_(
+    name="mixtral_prefill_ec", routing="expert", renorm=False,
+    note="Mixtral-8x7B-shaped prefill, expert choice, 1024 tokens per expert")
+WORKLOADS["dsv3_prefill_ec"] = WORKLOADS["dsv3_prefill"].with_(
+    name="dsv3_prefill_ec", routing="expert", renorm=False, bias_std=None,
+    note="DeepSeek-V3-shaped prefill, expert choice (sigmoid scores), 128 tokens per expert")
+
 # Reduced versions: same routing rule and dtype, sizes the CPU oracle finishes
 # in seconds, with several tiles per expert and ragged tails.
 SMALL = {
@@ -114,6 +124,12 @@ for _n in ("dsv3_prefill", "dsv3_decode", "switch_capacity", "mixtral_prefill"):
     SMALL[_n + "_fp8"] = SMALL[_n].with_(name=SMALL[_n].name + "_fp8", wdtype="fp8")
 SMALL["dsv3_prefill_grouped"] = SMALL["dsv3_prefill"].with_(
     name="dsv3_prefill_grouped_small", n_group=8, topk_group=4)
+SMALL["mixtral_prefill_ec"] = SMALL["mixtral_prefill"].with_(
+    name="mixtral_prefill_ec_small", routing="expert", renorm=False)
+SMALL["dsv3_prefill_ec"] = SMALL["dsv3_prefill"].with_(
+    name="dsv3_prefill_ec_small", routing="expert", renorm=False, bias_std=None)
+SMALL["tiny_fp32_ec"] = SMALL["tiny_fp32"].with_(
+    name="tiny_fp32_ec", routing="expert", renorm=False, cf=1.25)
 SMALL["mixtral_grouped"] = SMALL["mixtral_prefill"].with_(
     name="mixtral_grouped_small", E=16, k=4, n_group=4, topk_group=2)
 

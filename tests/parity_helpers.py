@@ -129,3 +129,30 @@ def check_rows(got, ref, bf16, label="", output_rounding=False):
               f"(tol {tol})", flush=True)
     assert e_cmp <= tol, f"{label} rel err {e_cmp:.3e} > {tol}"
     return e
+
+
+EC_TIE = 1e-12         # expert-choice scores closer than this may order either way
+
+
+def check_expert_choice(slot_row, gates, lg, score, C):
+    """The device's expert-choice assignment against the oracle's, both on
+    the device's fp32 logits.  Every expert must take exactly min(C, T)
+    tokens; a column that differs from the oracle's is accepted only when
+    every token it took scores within EC_TIE of every token it left (a
+    near-tie, both choices correct).  Gates must be the oracle's scores on
+    taken slots and exactly 0 elsewhere.  Returns (mask, near-tie columns)."""
+    lg = np.asarray(lg, np.float64)
+    T, E = lg.shape
+    mask_ref, g_ref, p = O.expert_choice(lg, score, C)
+    sr = np.asarray(slot_row).reshape(T, E)
+    mask = sr >= 0
+    assert (mask.sum(axis=0) == min(C, T)).all(), "an expert took the wrong number of tokens"
+    bad = np.flatnonzero((mask != mask_ref).any(axis=0))
+    for e in bad:
+        lo = p[mask[:, e], e].min()
+        hi = p[~mask[:, e], e].max()
+        assert lo >= hi - EC_TIE, f"expert {e}: taken score {lo} < left score {hi}"
+    g = np.asarray(gates, np.float64).reshape(T, E)
+    assert (g[~mask] == 0).all()
+    check_gates(g[mask], p[mask])
+    return mask, int(bad.size)

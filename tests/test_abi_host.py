@@ -137,7 +137,7 @@ def test_ffn_and_combine_validation(L):
     assert ffn(dt=3) == -1
     assert ffn(wsb=10) == -3
     assert L.moe_combine(1, 1, 1, 16, 0, 256, None, 1, 1, None) == -1
-    assert L.moe_combine(1, 1, 1, 16, 17, 256, None, 1, 1, None) == -2
+    assert L.moe_combine(1, 1, 1, 16, 257, 256, None, 1, 1, None) == -2
     assert L.moe_combine(None, 1, 1, 16, 2, 256, None, 1, 1, None) == -1
     assert L.moe_balance(None, 1, 16, 2, 8, 1, None) == -1
 
@@ -160,3 +160,62 @@ def test_forward_validation(L):
     assert fwd(lay(W2=None)) == -1
     assert fwd(lay(), X=None) == -1
     assert fwd(lay(), wsb=100) == -3
+
+
+def test_expert_choice_route_validation(L):
+    def call(**o):
+        a = dict(X=1, dt=1, T=16, d=256, Wg=1, E=8, off=None, score=0, C=4, lg=None, offs=1,
+                 ss=None, sr=1, g=1, ws=256, wsb=1 << 30)
+        a.update(o)
+        return L.moe_route_expert_choice(a["X"], a["dt"], a["T"], a["d"], a["Wg"], a["E"],
+                                         a["off"], a["score"], a["C"], a["lg"], a["offs"],
+                                         a["ss"], a["sr"], a["g"], a["ws"], a["wsb"], None)
+    assert call(C=-1) == -1
+    assert call(score=3) == -1
+    assert call(offs=None) == -1
+    assert call(sr=None) == -1
+    assert call(g=None) == -1
+    assert call(X=None) == -1
+    assert call(E=0) == -1
+    assert call(E=257) == -2
+    assert call(d=100) == -2
+    assert call(T=1 << 27, E=64) == -2          # T*E beyond int32 indices
+    assert call(wsb=8) == -3
+    assert call(ws=None) == -1
+    # keys in fp64 for every (token, expert): the workspace grows with T*E
+    assert (L.moe_route_expert_choice_workspace_size(4096, 7168, 256)
+            >= L.moe_route_workspace_size(4096, 7168, 256) + 4096 * 256 * 8)
+
+
+def test_expert_choice_forward_validation(L):
+    def lay(**o):
+        a = dict(dtype=1, score=0, renorm=0, d=256, E=8, k=2, F=512, ns=0, cf=0.0, Wg=1,
+                 bias=None, off=None, W1=1, W3=1, W2=1, Ws1=None, Ws3=None, Ws2=None)
+        a.update(o)
+        layer = _lib.MoeLayerC(*a.values())
+        layer.routing = _lib.MOE_EXPERT_CHOICE
+        return layer
+
+    def fwd(layer, T=16, aux=None, wsb=1 << 40):
+        return L.moe_forward(ctypes.byref(layer), 1, T, 1, aux, 256, wsb, None)
+    assert fwd(lay(renorm=1)) == -1             # gates are the scores, not renormalised
+    assert fwd(lay(score=1, bias=1)) == -1      # no selection bias
+    bad = lay()
+    bad.n_group, bad.topk_group = 2, 1
+    assert fwd(bad) == -1                       # no groups
+    assert fwd(lay(cf=1e300)) == -1
+    other = lay()
+    other.routing = 2
+    assert fwd(other) == -1
+    for name in ("topk_ids", "prob_sum", "balance", "health"):
+        aux = _lib.MoeAuxC()
+        setattr(aux, name, 256)
+        assert fwd(lay(), aux=ctypes.byref(aux)) == -1, name
+        assert "expert-choice" in _lib.last_error()
+    # workspace: [T][E] slot arrays and E*C routed rows
+    T, E, k, d, F = 4096, 256, 8, 7168, 2048
+    tc = lay(d=d, E=E, k=k, F=F)
+    tc.routing = _lib.MOE_TOKEN_CHOICE
+    ec = lay(d=d, E=E, k=k, F=F)
+    assert (L.moe_forward_workspace_size(ctypes.byref(ec), T)
+            > L.moe_forward_workspace_size(ctypes.byref(tc), T))

@@ -27,7 +27,7 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.routing == "token"])
 def test_fullsize_workload(name):
     w = WORKLOADS[name]
     print(f"[case] fullsize {name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
@@ -99,3 +99,57 @@ def test_fullsize_workload(name):
     assert abs(aux["balance"].item() - bal) <= 1e-5 * max(1.0, bal)
     print(f"[info] {name}: R={R} dropped={w.T * w.k - R} touched={touched.size} "
           f"balance={bal:.4f}", flush=True)
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.routing == "expert"])
+def test_fullsize_expert_choice(name):
+    """Expert-choice layers at full size: the assignment of every expert on
+    every token (validated against the oracle on the device's logits), the
+    row layout bit-exactly, sampled expert and shared rows, and the combine
+    recomputed by the oracle from the device's rows."""
+    w = WORKLOADS[name]
+    print(f"[case] fullsize {name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}", flush=True)
+    inp = make_inputs(w, DEV)
+    layer = moe.layer_from_inputs(inp)
+    Y, aux = moe.forward(layer, inp["X"], aux=True)
+    torch.cuda.synchronize()
+    bf16 = w.dtype == "bf16"
+    rng = np.random.default_rng(4321)
+    X = inp["X"]
+    lg = H.np64(aux["logits"])
+    ts = np.sort(rng.choice(w.T, size=min(64, w.T), replace=False))
+    xs = H.np64(X[torch.as_tensor(ts, device=DEV)])
+    off = None if inp["offset"] is None else H.np64(inp["offset"])
+    H.check_logits(lg[ts], O.router_logits(xs, H.np64(inp["Wg"]).T, off))
+
+    Ce = min(w.T, O.capacity(w.cf or 1.0, w.T, w.k, w.E))
+    mask, ties = H.check_expert_choice(H.np64(aux["slot_row"]).astype(np.int64),
+                                       H.np64(aux["topk_w"]), lg, w.score, Ce)
+    print(f"[info] {name}: C={Ce}, near-tie experts {ties}, tokens taken by no expert "
+          f"{int((~mask.any(axis=1)).sum())}", flush=True)
+    d = O.expert_choice_dispatch(mask)
+    R = d["n_kept"]
+    assert R == w.E * Ce and int(aux["n_kept"].item()) == R
+    assert aux["offsets"].cpu().tolist() == d["offsets"].tolist()
+    assert aux["slot_row"].cpu().reshape(-1).tolist() == d["slot_row"].tolist()
+    assert aux["sorted_slot"].cpu()[:R].tolist() == d["sorted_slot"].tolist()
+
+    for e in rng.choice(w.E, size=min(3, w.E), replace=False):
+        a, b = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        rsel = np.sort(rng.choice(np.arange(a, b), size=min(8, b - a), replace=False))
+        tok = d["sorted_slot"][rsel] // w.E
+        xr = H.np64(X[torch.as_tensor(tok, device=DEV)])
+        W1, W3, W2 = H.expert_logical(inp, int(e))
+        ref = O.expert_ffn(xr, W1, W3, W2, bf16_h=bf16)
+        got = H.np64(aux["Yrows"][torch.as_tensor(rsel, device=DEV)])
+        H.check_rows(got, ref, bf16, f"{name} expert {e} rows")
+    if inp["shared"] is not None:
+        ss = inp.get("shared_scales") or (None, None, None)
+        s1, s3, s2 = (H.weights64(t, sc).T for t, sc in zip(inp["shared"], ss))
+        ref = O.expert_ffn(xs, s1, s3, s2, bf16_h=bf16)
+        got = H.np64(aux["Yrows"][torch.as_tensor(R + ts, device=DEV)])
+        H.check_rows(got, ref, bf16, f"{name} shared rows")
+    rows = H.np64(aux["Yrows"])
+    sh = rows[R:R + w.T] if inp["shared"] is not None else None
+    Yref = O.combine(rows[:R], d["slot_row"], H.np64(aux["topk_w"]), sh)
+    H.check_rows(H.np64(Y), Yref, bf16, f"{name} Y (combine)", output_rounding=True)

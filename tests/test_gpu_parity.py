@@ -82,12 +82,101 @@ def _full_check(inp):
     return Y, aux
 
 
+def _ec_capacity(w):
+    return min(w.T, O.capacity(w.cf or 1.0, w.T, w.k, w.E)) if w.T else 0
+
+
+def _full_check_ec(inp):
+    """Expert-choice forward: every step against the oracle on the device's
+    logits; the device's assignment is validated first (near-ties aside it
+    must be the oracle's), then the rows, layout and output use it."""
+    w = inp["workload"]
+    layer = moe.layer_from_inputs(inp)
+    Y, aux = moe.forward(layer, inp["X"], aux=True)
+    torch.cuda.synchronize()
+    L = H.logical(inp)
+    lg = H.np64(aux["logits"])
+    H.check_logits(lg, O.router_logits(L["X"], L["Wg"], L["offset"]))
+    Ce = _ec_capacity(w)
+    mask, ties = H.check_expert_choice(H.np64(aux["slot_row"]).astype(np.int64),
+                                       H.np64(aux["topk_w"]), lg, w.score, Ce)
+    assert ties == 0, "near-tie reordering in a small workload"
+    bf16 = w.dtype == "bf16"
+    ref = O.forward_expert_choice(L["X"], L["Wg"], L["W1"], L["W3"], L["W2"], C=Ce,
+                                  score_func=w.score, offset=L["offset"], shared=L["shared"],
+                                  bf16_h=bf16, logits=lg, mask=mask)
+    d = ref["dispatch"]
+    R = d["n_kept"]
+    assert R == w.E * Ce and int(aux["n_kept"].item()) == R
+    assert aux["counts"].cpu().tolist() == [Ce] * w.E
+    assert aux["offsets"].cpu().tolist() == d["offsets"].tolist()
+    assert aux["slot_row"].cpu().reshape(-1).tolist() == d["slot_row"].tolist()
+    assert aux["sorted_slot"].cpu()[:R].tolist() == d["sorted_slot"].tolist()
+    rows = H.np64(aux["Yrows"])
+    if R:
+        H.check_rows(rows[:R], ref["rows"], bf16, f"{w.name} expert rows")
+    if ref["shared"] is not None:
+        H.check_rows(rows[R:R + w.T], ref["shared"], bf16, f"{w.name} shared rows")
+    H.check_rows(H.np64(Y), ref["Y"], bf16, f"{w.name} Y", output_rounding=True)
+    untaken = ~mask.any(axis=1)
+    print(f"[info] {w.name}: C={Ce}, tokens taken by no expert {int(untaken.sum())}, "
+          f"most experts on one token {int(mask.sum(axis=1).max()) if w.T else 0}", flush=True)
+    if ref["shared"] is None and untaken.any():
+        assert (H.np64(Y)[untaken] == 0).all()
+    return Y, aux, mask
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small_workloads(name):
     w = SMALL[name]
-    _announce(f"forward {w.name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F}")
+    _announce(f"forward {w.name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F} routing={w.routing}")
     inp = make_inputs(w, DEV)
-    _full_check(inp)
+    if w.routing == "expert":
+        _full_check_ec(inp)
+    else:
+        _full_check(inp)
+
+
+EC_EDGE = {
+    "T1": Workload("ec_T1", T=1, d=256, E=8, k=2, F=256, routing="expert", renorm=False,
+                   seed=31),
+    "E1_ties": Workload("ec_E1", T=70, d=128, E=1, k=1, F=128, routing="expert",
+                        renorm=False, cf=0.5, seed=32),
+    "dense_cap": Workload("ec_dense", T=40, d=256, E=4, k=2, F=256, dtype="f32",
+                          routing="expert", renorm=False, cf=8.0, seed=33),
+    "decode_sigmoid_shared": Workload("ec_decode", T=16, d=512, E=32, k=8, F=256,
+                                      score="sigmoid", n_shared=1, routing="expert",
+                                      renorm=False, seed=34),
+    "many_chunks": Workload("ec_chunks", T=2500, d=128, E=8, k=2, F=128, routing="expert",
+                            renorm=False, cf=0.75, seed=35),
+    "E256_fp8": Workload("ec_E256_fp8", T=96, d=256, E=256, k=8, F=128, score="sigmoid",
+                         routing="expert", renorm=False, wdtype="fp8", seed=36),
+}
+
+
+@pytest.mark.parametrize("name", list(EC_EDGE))
+def test_forward_expert_choice_edge_cases(name):
+    w = EC_EDGE[name]
+    _announce(f"expert-choice edge {name}")
+    inp = make_inputs(w, DEV)
+    Y, aux, mask = _full_check_ec(inp)
+    if name == "E1_ties":
+        # every softmax score is 1: the tie rule takes the first C tokens
+        assert np.flatnonzero(mask[:, 0]).tolist() == list(range(_ec_capacity(w)))
+    if name == "dense_cap":
+        assert mask.all()          # C >= T: every expert takes every token
+
+
+def test_expert_choice_empty_batch():
+    w = Workload("ec_empty", T=0, d=256, E=8, k=2, F=256, routing="expert", renorm=False,
+                 seed=37)
+    _announce("expert-choice empty batch")
+    inp = make_inputs(w, DEV)
+    Y, aux = moe.forward(moe.layer_from_inputs(inp), inp["X"], aux=True)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 256)
+    assert aux["counts"].cpu().tolist() == [0] * 8
+    assert int(aux["n_kept"].item()) == 0
 
 
 EDGE = {
@@ -188,6 +277,37 @@ def test_route_entry_point(score, ng, tg):
     assert np.allclose(H.np64(r["prob_sum"]), p.sum(axis=0), rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("score,T,E,C", [("softmax", 333, 32, 40), ("sigmoid", 333, 32, 40),
+                                         ("softmax", 100, 8, 100), ("softmax", 100, 8, 150),
+                                         ("sigmoid", 50, 256, 3), ("softmax", 1, 4, 1),
+                                         ("softmax", 64, 8, 0), ("softmax", 2500, 8, 700),
+                                         ("sigmoid", 3000, 64, 47)])
+def test_route_expert_choice_entry_point(score, T, E, C):
+    _announce(f"moe_route_expert_choice {score} T={T} E={E} C={C}")
+    w = Workload("ec_route", T=T, d=256, E=E, k=1, F=128, score=score, seed=T + E)
+    inp = make_inputs(w, DEV)
+    X = inp["X"]
+    if T >= 8:
+        # duplicated tokens: equal logits rows give exact score ties
+        X[1:8:2] = X[0:8:2]
+    r = moe.route_expert_choice(X, inp["Wg"], C, score)
+    torch.cuda.synchronize()
+    L = H.logical(inp)
+    lg = H.np64(r["logits"])
+    H.check_logits(lg, O.router_logits(H.np64(X), L["Wg"]))
+    mask, ties = H.check_expert_choice(H.np64(r["slot_row"]).astype(np.int64),
+                                       H.np64(r["gates"]), lg, score, C)
+    print(f"[info] near-tie experts {ties}", flush=True)
+    d = O.expert_choice_dispatch(mask)
+    assert r["offsets"].cpu().tolist() == d["offsets"].tolist()
+    assert r["sorted_slot"].cpu().tolist() == d["sorted_slot"].tolist()
+    assert r["slot_row"].cpu().reshape(-1).tolist() == d["slot_row"].tolist()
+    for i in range(0, min(T, 8) - 1, 2):
+        if (lg[i] == lg[i + 1]).all():
+            # bit-equal scores: a token is never taken while its earlier twin is left
+            assert not (mask[i + 1] & ~mask[i]).any()
+
+
 @pytest.mark.parametrize("T,k,E,C", [(1, 1, 1, 0), (100, 2, 8, 0), (1000, 8, 256, 0),
                                      (1000, 8, 256, 20), (3000, 1, 64, 40), (777, 3, 5, 1),
                                      (5000, 4, 17, 900)])
@@ -283,13 +403,15 @@ def test_forward_ksplit_paths_agree():
     assert torch.equal(Y_plain, Y_aux)
 
 
-def test_combine_entry_point():
-    _announce("moe_combine")
-    T, k, d = 257, 3, 384
+@pytest.mark.parametrize("T,k,d,keep", [(257, 3, 384, 0.5), (64, 256, 256, 0.05),
+                                        (40, 64, 128, 0.3), (9, 16, 128, 0.0)])
+def test_combine_entry_point(T, k, d, keep):
+    _announce(f"moe_combine T={T} k={k} d={d}")
     g = torch.Generator().manual_seed(9)
     R = 600
     rows = torch.randn((R, d), generator=g)
-    sr = torch.randint(-1, R, (T * k,), generator=g, dtype=torch.int32)
+    sr = torch.randint(0, R, (T * k,), generator=g, dtype=torch.int32)
+    sr[torch.rand((T * k,), generator=g) >= keep] = -1
     w = torch.rand((T, k), generator=g)
     sh = torch.randn((T, d), generator=g)
     for dt in (torch.float32, torch.bfloat16):
