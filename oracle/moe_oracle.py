@@ -83,6 +83,20 @@ R20 Expert-choice routing ([Book 14.2.3] "two selection paradigms", [Blog
     number of experts per token is not fixed); a token no expert took gets
     only the shared expert.  Rows are grouped by expert, tokens ascending
     inside; slot s = t*E + e.
+R21 Overflow re-route ([KMap capacity], the second/backup option: the
+    overflowing requests go to other experts that still have room, so the
+    token keeps its full set of paths): one backup round after the capacity
+    drop.  Token t's backups are its next choices after the top-k, in the
+    same key order.  The m-th dropped slot of token t (j ascending) proposes
+    the token's m-th backup; experts accept proposals in slot order while
+    they have room (C minus the slots kept in the first pass); a proposal
+    that finds no room, or a slot without a backup, stays dropped.  A
+    re-routed slot keeps its gate.  An expert's rows are its first-pass slots
+    in slot order followed by its accepted proposals in slot order.
+R22 Bias update (the load rule of DeepSeek-V3's auxiliary-loss-free
+    balancing, [Book 14.2.3]): after a step, expert e's selection bias moves
+    by -gamma when its load (pre-drop count) is above the mean T*k/E, by
+    +gamma when below, and stays when equal.
 (R15-R19 concern the device comparison and the inputs, not this module.)
 
 Parity status: every function here is pinned by the CPU tests (worked examples
@@ -103,7 +117,7 @@ __all__ = [
     "forward_token_loop", "forward_dense_masked", "balance_value",
     "balance_stat", "expert_weight_shapes", "decode_e4m3", "dequantize_rows", "group_mask",
     "router_health", "expert_choice", "expert_choice_dispatch", "forward_expert_choice",
-    "forward_expert_choice_loop",
+    "forward_expert_choice_loop", "bias_update", "backup_experts",
 ]
 
 
@@ -223,20 +237,27 @@ def route(logits, k, score_func, renorm, bias=None, n_group=1, topk_group=1):
 
 
 # ---------------------------------------------------------------- dispatch --
-def dispatch(ids, n_experts: int, cap=None):
+def dispatch(ids, n_experts: int, cap=None, backups=None):
     """Step 4 [Book 14.2.1] with the capacity drop of [KMap capacity].
 
     Slot s = t*k + j.  Its rank is the number of earlier slots that chose the
-    same expert (R6); it is kept iff rank < C.  Returns a dict with
-      counts[E]      pre-drop requests per expert
-      kept[E]        min(counts, C)
+    same expert (R6); it is kept iff rank < C.  With ``backups`` [T, B] (the
+    tokens' next choices after their top-k, -1 for none) the dropped slots
+    get one backup round (R21).  Returns a dict with
+      counts[E]      pre-drop requests per expert (top-k choices)
+      kept[E]        rows per expert (min(counts, C), plus accepted backups)
       offsets[E+1]   exclusive scan of kept
-      sorted_slot[R] kept slots grouped by expert, increasing slot order inside
+      sorted_slot[R] kept slots grouped by expert, first-pass slots then
+                     re-routed ones, increasing slot order inside each part
       slot_row[T*k]  row of slot s in the sorted buffer, -1 if dropped
+      expert[T*k]    expert that computes slot s, -1 if dropped
       n_kept         R
-    Written as a plain first-come loop over slots.
+      n_rerouted     slots placed by the backup round
+    Written as plain first-come loops over slots.
     """
-    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    ids = np.asarray(ids, dtype=np.int64)
+    flat = ids.reshape(-1)
+    k = ids.shape[1] if ids.ndim == 2 else 1
     E = int(n_experts)
     counts = [0] * E
     rank = [0] * flat.size
@@ -246,26 +267,66 @@ def dispatch(ids, n_experts: int, cap=None):
         rank[s] = counts[e]
         counts[e] += 1
     C = None if cap is None or cap <= 0 else int(cap)
-    kept = [c if C is None else min(c, C) for c in counts]
-    offsets = [0]
-    for e in range(E):
-        offsets.append(offsets[-1] + kept[e])
-    R = offsets[-1]
-    sorted_slot = [-1] * R
-    slot_row = [-1] * flat.size
+    members = [[] for _ in range(E)]          # slots of each expert, in row order
+    expert = [-1] * flat.size
     for s, e in enumerate(flat.tolist()):
         if C is None or rank[s] < C:
-            row = offsets[e] + rank[s]
-            sorted_slot[row] = s
-            slot_row[s] = row
+            members[e].append(s)
+            expert[s] = e
+    n_rerouted = 0
+    if backups is not None and C is not None:
+        bk = np.asarray(backups, dtype=np.int64).reshape(flat.size // k, -1).tolist()
+        room = [C - len(members[e]) for e in range(E)]
+        for t in range(flat.size // k):
+            m = 0                                  # dropped slots of token t so far
+            for j in range(k):
+                s = t * k + j
+                if expert[s] >= 0:
+                    continue
+                m += 1
+                if m > len(bk[t]) or bk[t][m - 1] < 0:
+                    continue
+                e = bk[t][m - 1]
+                if room[e] > 0:                    # accepted in slot order
+                    room[e] -= 1
+                    members[e].append(s)
+                    expert[s] = e
+                    n_rerouted += 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + len(members[e]))
+    sorted_slot = [s for e in range(E) for s in members[e]]
+    slot_row = [-1] * flat.size
+    for row, s in enumerate(sorted_slot):
+        slot_row[s] = row
     return {
         "counts": np.array(counts, dtype=np.int64),
-        "kept": np.array(kept, dtype=np.int64),
+        "kept": np.array([len(m) for m in members], dtype=np.int64),
         "offsets": np.array(offsets, dtype=np.int64),
         "sorted_slot": np.array(sorted_slot, dtype=np.int64),
         "slot_row": np.array(slot_row, dtype=np.int64),
-        "n_kept": int(R),
+        "expert": np.array(expert, dtype=np.int64),
+        "n_kept": int(len(sorted_slot)),
+        "n_rerouted": n_rerouted,
     }
+
+
+def backup_experts(logits, k: int, score_func: str, bias=None, n_group: int = 1,
+                   topk_group: int = 1):
+    """Each token's next B = min(k, E - k) choices after its top-k, in the
+    selection's own key order (R21); -1 where the key is -inf (an expert
+    outside the chosen groups)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    B = min(k, E - k)
+    _, key = select_topk(lg, k, score_func, bias, n_group, topk_group)
+    bk = np.full((T, B), -1, dtype=np.int64)
+    for t in range(T):
+        order = np.argsort(-key[t], kind="stable")      # the top-k's own order
+        for m, e in enumerate(order[k:k + B].tolist()):
+            if key[t, e] > -np.inf:
+                bk[t, m] = e
+    return bk
 
 
 # ------------------------------------------------------------- expert FFN --
@@ -324,7 +385,7 @@ def expert_ffn(x, W1, W3, W2, bf16_h: bool = False):
 # ----------------------------------------------------------------- forward --
 def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
             bias=None, offset=None, cap=None, shared=None, bf16_h=False,
-            logits=None, n_group=1, topk_group=1):
+            logits=None, n_group=1, topk_group=1, reroute=False):
     """Tier 1: the six steps of [Book 14.2.1] with per-expert matmuls.
 
     X[T,d]; Wg[d,E]; W1,W3[E,d,F]; W2[E,F,d]; shared = (W1s[d,F], W3s[d,F],
@@ -338,7 +399,8 @@ def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
     own = router_logits(X, Wg, offset)
     lg = own if logits is None else np.asarray(logits, dtype=np.float64)
     ids, g, p = route(lg, k, score_func, renorm, bias, n_group, topk_group)
-    disp = dispatch(ids, E, cap)
+    bk = backup_experts(lg, k, score_func, bias, n_group, topk_group) if reroute else None
+    disp = dispatch(ids, E, cap, bk)
     rows = np.zeros((disp["n_kept"], d))
     for e in range(E):
         a, b = disp["offsets"][e], disp["offsets"][e + 1]
@@ -349,7 +411,7 @@ def forward(X, Wg, W1, W3, W2, *, k, score_func="softmax", renorm=True,
     if shared is not None:
         sh = expert_ffn(X, shared[0], shared[1], shared[2], bf16_h)
     Y = combine(rows, disp["slot_row"], g, sh)
-    return {"logits": own, "route_logits": lg, "ids": ids, "gates": g,
+    return {"logits": own, "route_logits": lg, "ids": ids, "gates": g, "backups": bk,
             "probs": p, "dispatch": disp, "rows": rows, "shared": sh, "Y": Y}
 
 
@@ -620,6 +682,24 @@ def router_health(logits, score_func: str, counts, n_kept: int, n_tokens: int, k
     cv = float(np.sqrt(np.mean((c - mean) ** 2)) / mean) if mean > 0 else 0.0
     return {"token_entropy": float(h.mean()) if n_tokens else 0.0, "load_entropy": h_load,
             "load_cv": cv, "drop_rate": 1.0 - n_kept / tk if tk > 0 else 0.0}
+
+
+# ------------------------------------------------------------ bias update --
+def bias_update(bias, counts, n_tokens: int, k: int, gamma: float):
+    """One step of the selection-bias rule [Book 14.2.3] (R22): overloaded
+    experts (count above the mean load T*k/E) lose gamma, underloaded ones
+    gain gamma.  The comparison count > T*k/E is made as count*E > T*k in
+    integers, so a load equal to the mean is recognised exactly."""
+    b = np.asarray(bias, dtype=np.float64).copy()
+    c = [int(v) for v in np.asarray(counts).tolist()]
+    E = len(c)
+    tk = int(n_tokens) * int(k)
+    for e in range(E):
+        if c[e] * E > tk:
+            b[e] -= gamma
+        elif c[e] * E < tk:
+            b[e] += gamma
+    return b
 
 
 # ----------------------------------------------------------------- balance --

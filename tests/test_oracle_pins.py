@@ -666,3 +666,135 @@ def test_expert_choice_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_expert_choice_hand_example()
     monkeypatch.setattr(O, "expert_choice", good)
+
+
+# -------------------------------------------------------------- bias update --
+def test_bias_update_page_rule():
+    # the capacity example's loads [5, 3, 2, 2] (mean 12/4 = 3): the
+    # overloaded expert loses gamma, the loaded-at-mean one stays, the two
+    # underloaded ones gain gamma; gamma = 0.001 as the report used
+    b = O.bias_update([0.5, -0.25, 0.0, 1.0], [5, 3, 2, 2], 6, 2, 0.001)
+    assert b.tolist() == [0.5 - 0.001, -0.25, 0.001, 1.0 + 0.001]
+    # gamma = 0 (the report's final phase) leaves the bias unchanged
+    assert O.bias_update([0.1, 0.2], [7, 1], 4, 2, 0.0).tolist() == [0.1, 0.2]
+    # a fractional mean: 3 tokens, top-1, 2 experts -> mean 1.5, nobody equal
+    assert O.bias_update([0.0, 0.0], [2, 1], 3, 1, 1.0).tolist() == [-1.0, 1.0]
+
+
+def test_bias_update_balances_a_skewed_router():
+    # the rule's purpose: with a fixed skewed sigmoid router, repeated
+    # updates move the selection toward equal loads (load CV falls)
+    rng = np.random.default_rng(12)
+    T, E, k = 512, 16, 2
+    lg = rng.normal(size=(T, E)) + np.linspace(0.0, 2.0, E)[None, :]
+    b = np.zeros(E)
+
+    def loads(bias):
+        ids, _ = O.select_topk(lg, k, "sigmoid", bias)
+        return np.bincount(ids.reshape(-1), minlength=E)
+    cv0 = loads(b).std() / (T * k / E)
+    for _ in range(200):
+        b = O.bias_update(b, loads(b), T, k, 0.01)
+    cv1 = loads(b).std() / (T * k / E)
+    assert cv1 < 0.5 * cv0
+    assert b[-1] < 0.0 < b[0]          # the popular expert is pushed down
+
+
+# ----------------------------------------------------------- overflow re-route --
+# The capacity worked example [KMap capacity]: 4 experts, 6 tokens, top-2,
+# C = 3; expert 0 receives 5 requests and overflows by 2 (tokens 3 and 4).
+_RR_IDS = [[0, 1], [0, 1], [0, 1], [0, 2], [0, 3], [2, 3]]
+
+
+def test_reroute_restores_the_dropped_paths():
+    # token 3's backup is expert 3, token 4's is expert 2; both have room
+    # (2 of 3 slots used), so no request is lost
+    bk = [[2], [2], [2], [3], [2], [0]]
+    d = O.dispatch(_RR_IDS, 4, 3, bk)
+    assert d["counts"].tolist() == [5, 3, 2, 2]
+    assert d["kept"].tolist() == [3, 3, 3, 3] and d["n_kept"] == 12 and d["n_rerouted"] == 2
+    # rows: first-pass slots of each expert in slot order, then its re-routed slots
+    assert d["sorted_slot"].tolist() == [0, 2, 4, 1, 3, 5, 7, 10, 8, 9, 11, 6]
+    assert d["slot_row"].tolist() == [0, 3, 1, 4, 2, 5, 11, 6, 8, 9, 7, 10]
+    assert d["expert"].tolist() == [0, 1, 0, 1, 0, 1, 3, 2, 2, 3, 2, 3]
+    # without backups the same two requests are dropped
+    plain = O.dispatch(_RR_IDS, 4, 3)
+    assert plain["n_kept"] == 10 and plain["slot_row"][6] == -1 and plain["slot_row"][8] == -1
+
+
+def test_reroute_to_a_full_expert_stays_dropped():
+    # token 3's backup is expert 1, already full: it stays dropped; token 4
+    # still gets expert 2
+    bk = [[2], [2], [2], [1], [2], [0]]
+    d = O.dispatch(_RR_IDS, 4, 3, bk)
+    assert d["slot_row"][6] == -1 and d["expert"][8] == 2 and d["n_kept"] == 11
+
+
+def test_backup_experts_follow_the_key_order():
+    lg = np.array([[0.1, 3.0, 2.0, -1.0, 1.0]])
+    assert O.backup_experts(lg, 2, "softmax").tolist() == [[4, 0]]
+    assert O.backup_experts(lg, 3, "softmax").tolist() == [[0, 3]]
+    assert O.backup_experts(lg, 5, "softmax").shape == (1, 0)
+    # group-limited: experts outside the chosen groups are never backups
+    lg2 = np.array([[5.0, 4.0, 0.0, 0.1]])          # groups {0,1}, {2,3}; one group used
+    assert O.backup_experts(lg2, 1, "softmax", n_group=2, topk_group=1).tolist() == [[1]]
+    assert O.backup_experts(lg2, 2, "softmax", n_group=2, topk_group=1).tolist() == [[-1, -1]]
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.data())
+def test_reroute_invariants(data):
+    rng = np.random.default_rng(data.draw(st.integers(0, 2**31)))
+    T = data.draw(st.integers(1, 30))
+    E = data.draw(st.integers(2, 8))
+    k = data.draw(st.integers(1, E - 1))
+    C = data.draw(st.integers(1, max(1, T * k // E + 2)))
+    lg = rng.normal(size=(T, E)) + np.linspace(0, 2, E)
+    ids, _ = O.select_topk(lg, k, "softmax")
+    bk = O.backup_experts(lg, k, "softmax")
+    plain = O.dispatch(ids, E, C)
+    d = O.dispatch(ids, E, C, bk)
+    ex = d["expert"].reshape(T, k)
+    assert (d["kept"] <= C).all()                      # no expert over capacity
+    assert d["n_kept"] == plain["n_kept"] + d["n_rerouted"] >= plain["n_kept"]
+    for t in range(T):
+        placed = [e for e in ex[t].tolist() if e >= 0]
+        assert len(placed) == len(set(placed))         # never two rows on one expert
+        for j in range(k):
+            if plain["slot_row"][t * k + j] >= 0:       # first-pass slots unchanged
+                assert ex[t, j] == ids[t, j]
+            elif ex[t, j] >= 0:                         # re-routed: to a backup
+                assert ex[t, j] in bk[t].tolist() and ex[t, j] not in ids[t].tolist()
+    ss, sr = d["sorted_slot"], d["slot_row"]
+    assert np.array_equal(sr[ss], np.arange(ss.size))
+    # a backup is refused only when its expert is full
+    for t in range(T):
+        m = 0
+        for j in range(k):
+            s = t * k + j
+            if plain["slot_row"][s] >= 0:
+                continue
+            m += 1
+            if m <= bk.shape[1] and bk[t, m - 1] >= 0 and d["slot_row"][s] < 0:
+                assert d["kept"][bk[t, m - 1]] == C
+    # no backups, or an unlimited capacity: the plain dispatch
+    assert np.array_equal(O.dispatch(ids, E, T * k, bk)["slot_row"],
+                          O.dispatch(ids, E, None)["slot_row"])
+
+
+def test_reroute_pins_catch_planted_mistakes(monkeypatch):
+    good = O.dispatch
+    # 12. backups accepted without checking the room left
+    def no_room_check(ids, E, cap=None, backups=None):
+        return good(ids, E, cap, backups) if backups is None else good(ids, E, None)
+    monkeypatch.setattr(O, "dispatch", no_room_check)
+    with pytest.raises(AssertionError):
+        test_reroute_to_a_full_expert_stays_dropped()
+    monkeypatch.setattr(O, "dispatch", good)
+    # 13. every dropped slot of a token proposes the same (first) backup
+    bko = O.backup_experts
+    monkeypatch.setattr(O, "backup_experts",
+                        lambda *a, **kw: np.repeat(bko(*a, **kw)[:, :1], 2, axis=1))
+    with pytest.raises(AssertionError):
+        test_backup_experts_follow_the_key_order()
+    monkeypatch.setattr(O, "backup_experts", bko)
