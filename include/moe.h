@@ -97,13 +97,17 @@ int64_t moe_capacity(double cf, int64_t N, int k, int E);
  *   topk_ids[T][k]   int32, key descending, ties to the lower expert id
  *   topk_w[T][k]     fp32 gates in the same order
  *   prob_sum[E]      fp32 sum over tokens of the full-row p (or s), or NULL
+ *   backup_ids[T][n_backup]  the next n_backup choices after the top-k in
+ *                    the same key order (-1 for an expert outside the
+ *                    chosen groups), for moe_dispatch's overflow re-route;
+ *                    0 <= n_backup <= min(k, E - k); NULL when n_backup = 0
  */
 size_t moe_route_workspace_size(int64_t T, int d, int E);
 int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg,
               int E, const float* bias, const float* logit_offset, int score,
               int k, int renorm, int n_group, int topk_group, float* logits,
-              int32_t* topk_ids, float* topk_w, float* prob_sum, void* ws,
-              size_t ws_bytes, void* stream);
+              int32_t* topk_ids, float* topk_w, float* prob_sum, int n_backup,
+              int32_t* backup_ids, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------- expert-choice route --
  * Expert-choice routing (LLM Internals 14.2.3, the expert-choice paradigm:
@@ -149,15 +153,24 @@ int moe_route_expert_choice(const void* X, int dtype, int64_t T, int d,
  *                      increasing slot order inside an expert
  *   slot_row[T*k]      row of slot s in the sorted order, -1 if dropped
  *   n_kept[1]          number of kept slots R
+ * Optional overflow re-route (AI Knowledge Map "MoE", the second/backup
+ * way of handling a capacity overflow): with capacity > 0 and n_backup > 0,
+ * backup_ids[T][n_backup] (moe_route's) give one backup round after the
+ * drop.  The m-th dropped slot of token t (j ascending) proposes
+ * backup_ids[t][m-1] (-1: none); experts accept proposals in slot order while
+ * they have room (capacity minus their first-pass rows); the rest stay
+ * dropped.  An expert's rows are then its first-pass slots followed by its
+ * accepted proposals, each in slot order; offsets / n_kept count both.
  * Optional gather (step 4's data movement): if X and X_sorted are non-NULL,
  *   X_sorted[r][:] = X[sorted_slot[r] / k][:] for r < n_kept (dtype, [.,d]).
  */
 size_t moe_dispatch_workspace_size(int64_t T, int k, int E);
 int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E,
-                 int64_t capacity, int32_t* counts, int32_t* offsets,
-                 int32_t* sorted_slot, int32_t* slot_row, int32_t* n_kept,
-                 const void* X, int dtype, int d, void* X_sorted, void* ws,
-                 size_t ws_bytes, void* stream);
+                 int64_t capacity, const int32_t* backup_ids, int n_backup,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                 int32_t* slot_row, int32_t* n_kept, const void* X, int dtype,
+                 int d, void* X_sorted, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /* --------------------------------------------------------- grouped FFN --
  * Grouped SwiGLU expert FFN (LLM Internals 14.2.1 step 5; one expert is the
@@ -207,6 +220,17 @@ int moe_combine(const float* Yrows, const int32_t* slot_row,
                 const float* topk_w, int64_t T, int k, int d,
                 const float* shared, void* Y, int dtype, void* stream);
 
+/* Selection-bias update (LLM Internals 14.2.3: DeepSeek-V3 keeps a per-expert
+ * bias that is not learned by back-propagation; after each step overloaded
+ * experts lose gamma and underloaded ones gain gamma; the report used
+ * gamma = 0.001, then 0).  In place on device memory:
+ *   bias[e] -= gamma  if counts[e] > T*k/E,
+ *   bias[e] += gamma  if counts[e] < T*k/E,  unchanged if equal
+ * (compared exactly as counts[e]*E vs T*k).  counts[E]: the step's pre-drop
+ * loads (moe_dispatch's or moe_aux's counts); gamma finite and >= 0. */
+int moe_bias_update(const int32_t* counts, int64_t T, int k, int E,
+                    float gamma, float* bias, void* stream);
+
 /* Balance statistic E * sum_e f_e P_e (LLM Internals 14.2.3 balance loss
  * without alpha): f_e = counts[e] / (T*k), P_e = prob_sum[e] / T.
  * Writes one fp64 value to device memory `out`. */
@@ -253,6 +277,9 @@ typedef struct moe_layer {
                               sorted_slot as [E*C], counts[e] = C, n_kept =
                               E*C; topk_ids, prob_sum, balance and health must
                               be NULL.                                        */
+  int reroute;             /* 1: overflow re-route of moe_dispatch with
+                              min(k, E - k) backups per token (top-k routing
+                              with a capacity factor); 0: overflow dropped   */
 } moe_layer;
 
 /* Optional device outputs of moe_forward; any member may be NULL. */

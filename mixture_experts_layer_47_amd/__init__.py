@@ -3,10 +3,12 @@
 The compute path is the HIP library ``libmoe.so`` (C ABI: include/moe.h);
 this package is its Python binding plus the seeded synthetic workloads.
 """
-from ._lib import (MoeError, MoeLayer, Forward, balance, capacity, combine, dispatch,  # noqa: F401
+from ._lib import (MoeError, MoeLayer, Forward, balance, bias_update, capacity,  # noqa: F401
+                   combine, dispatch,
                    forward, grouped_ffn, last_error, layer_from_inputs, lib, route,
                    route_expert_choice, timing_enable, timing_read)
 
-__all__ = ["MoeError", "MoeLayer", "Forward", "balance", "capacity", "combine", "dispatch",
+__all__ = ["MoeError", "MoeLayer", "Forward", "balance", "bias_update", "capacity", "combine",
+           "dispatch",
            "forward", "grouped_ffn", "last_error", "layer_from_inputs", "lib", "route",
            "route_expert_choice", "timing_enable", "timing_read"]

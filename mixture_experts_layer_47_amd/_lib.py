@@ -27,7 +27,7 @@ EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_ro
            "moe_route_expert_choice_workspace_size", "moe_route_expert_choice",
            "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_fp8",
-           "moe_combine",
+           "moe_combine", "moe_bias_update",
            "moe_balance", "moe_forward_workspace_size", "moe_forward", "moe_timing_enable",
            "moe_timing_read")
 
@@ -52,7 +52,7 @@ class MoeLayerC(ctypes.Structure):
                 ("W2_scale", ctypes.c_void_p), ("Ws1_scale", ctypes.c_void_p),
                 ("Ws3_scale", ctypes.c_void_p), ("Ws2_scale", ctypes.c_void_p),
                 ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
-                ("routing", ctypes.c_int)]
+                ("routing", ctypes.c_int), ("reroute", ctypes.c_int)]
 
 
 class MoeAuxC(ctypes.Structure):
@@ -70,17 +70,18 @@ def _declare(L):
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_capacity": (I64, [D, I64, I, I]),
         "moe_route_workspace_size": (SZ, [I64, I, I]),
-        "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_route": (I, [P, I, I64, I, P, I, P, P, I, I, I, I, I, P, P, P, P, I, P, P, SZ, P]),
         "moe_route_expert_choice_workspace_size": (SZ, [I64, I, I]),
         "moe_route_expert_choice": (I, [P, I, I64, I, P, I, P, I, I64, P, P, P, P, P, P, SZ,
                                         P]),
         "moe_dispatch_workspace_size": (SZ, [I64, I, I]),
-        "moe_dispatch": (I, [P, I64, I, I, I64, P, P, P, P, P, P, I, I, P, P, SZ, P]),
+        "moe_dispatch": (I, [P, I64, I, I, I64, P, I, P, P, P, P, P, P, I, I, P, P, SZ, P]),
         "moe_grouped_ffn_workspace_size": (SZ, [I64, I, I, I, I]),
         "moe_grouped_ffn": (I, [P, P, P, I, P, P, P, I, I, I, I64, P, P, SZ, P]),
         "moe_grouped_ffn_fp8": (I, [P, P, P, I, P, P, P, P, P, P, I, I, I64, P, P, SZ, P]),
         "moe_combine": (I, [P, P, P, I64, I, I, P, P, I, P]),
         "moe_balance": (I, [P, P, I64, I, I, P, P]),
+        "moe_bias_update": (I, [P, I64, I, I, ctypes.c_float, P, P]),
         "moe_forward_workspace_size": (SZ, [ctypes.POINTER(MoeLayerC), I64]),
         "moe_forward": (I, [ctypes.POINTER(MoeLayerC), P, I64, P, ctypes.POINTER(MoeAuxC), P,
                             SZ, P]),
@@ -151,7 +152,7 @@ def capacity(cf: float, N: int, k: int, E: int) -> int:
 
 
 def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
-          want_logits=True, want_prob_sum=True, n_group=1, topk_group=1):
+          want_logits=True, want_prob_sum=True, n_group=1, topk_group=1, n_backup=0):
     T, d = X.shape
     E = Wg.shape[0]
     dev = X.device
@@ -159,14 +160,23 @@ def route(X, Wg, k, score="softmax", renorm=True, bias=None, offset=None,
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     lg = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
     ps = torch.empty((E,), dtype=torch.float32, device=dev) if want_prob_sum else None
+    bk = torch.empty((T, n_backup), dtype=torch.int32, device=dev) if n_backup else None
     L = lib()
     ws_n = L.moe_route_workspace_size(T, d, E)
     ws = _workspace(ws_n, dev)
     _check(L.moe_route(_ptr(X), _dtype_code(X), T, d, _ptr(Wg), E, _ptr(bias), _ptr(offset),
                        _score_code(score), int(k), int(bool(renorm)), int(n_group),
                        int(topk_group), _ptr(lg), _ptr(ids),
-                       _ptr(w), _ptr(ps), _ptr(ws), ws.numel(), _stream(dev)))
-    return {"ids": ids, "w": w, "logits": lg, "prob_sum": ps}
+                       _ptr(w), _ptr(ps), int(n_backup), _ptr(bk), _ptr(ws), ws.numel(),
+                       _stream(dev)))
+    return {"ids": ids, "w": w, "logits": lg, "prob_sum": ps, "backup": bk}
+
+
+def bias_update(counts, T, k, gamma, bias):
+    """In place: bias[e] -/+= gamma for experts above / below the mean load."""
+    _check(lib().moe_bias_update(_ptr(counts), int(T), int(k), counts.numel(), float(gamma),
+                                 _ptr(bias), _stream(bias.device)))
+    return bias
 
 
 def route_expert_choice(X, Wg, C, score="softmax", offset=None, want_logits=True):
@@ -195,7 +205,7 @@ def route_expert_choice(X, Wg, C, score="softmax", offset=None, want_logits=True
     return out
 
 
-def dispatch(ids, E, capacity=0, X=None):
+def dispatch(ids, E, capacity=0, X=None, backup=None):
     T, k = ids.shape
     dev = ids.device
     i32 = dict(dtype=torch.int32, device=dev)
@@ -209,7 +219,9 @@ def dispatch(ids, E, capacity=0, X=None):
         out["X_sorted"] = torch.empty((T * k, d), dtype=X.dtype, device=dev)
     L = lib()
     ws = _workspace(L.moe_dispatch_workspace_size(T, k, E), dev)
-    _check(L.moe_dispatch(_ptr(ids), T, k, E, int(capacity), _ptr(out["counts"]),
+    nb = 0 if backup is None else backup.shape[1]
+    _check(L.moe_dispatch(_ptr(ids), T, k, E, int(capacity), _ptr(backup), nb,
+                          _ptr(out["counts"]),
                           _ptr(out["offsets"]), _ptr(out["sorted_slot"]), _ptr(out["slot_row"]),
                           _ptr(out["n_kept"]), _ptr(X), dt, d, _ptr(out["X_sorted"]),
                           _ptr(ws), ws.numel(), _stream(dev)))
@@ -273,6 +285,7 @@ class MoeLayer:
     n_group: int = 1                       # group-limited routing (1 = off)
     topk_group: int = 1
     routing: str = "token"                 # "token" (top-k) or "expert" (expert choice)
+    reroute: bool = False                  # overflow to a backup expert instead of a drop
 
     def expert_capacity(self, T: int) -> int:
         """Tokens per expert under expert-choice routing: min(T, C)."""
@@ -293,7 +306,8 @@ class MoeLayer:
             self.W3.data_ptr(), self.W2.data_ptr(), _addr(s[0]), _addr(s[1]), _addr(s[2]),
             MOE_W_FP8 if fp8 else MOE_W_DTYPE, _addr(q[0]), _addr(q[1]), _addr(q[2]),
             _addr(qs[0]), _addr(qs[1]), _addr(qs[2]), int(self.n_group), int(self.topk_group),
-            {"token": MOE_TOKEN_CHOICE, "expert": MOE_EXPERT_CHOICE}[self.routing])
+            {"token": MOE_TOKEN_CHOICE, "expert": MOE_EXPERT_CHOICE}[self.routing],
+            int(bool(self.reroute)))
         return self._keep
 
 
@@ -308,7 +322,8 @@ def layer_from_inputs(inp: dict) -> MoeLayer:
                     score=w.score, renorm=w.renorm, bias=inp["bias"], offset=inp["offset"],
                     shared=inp["shared"], capacity_factor=w.cf or 0.0,
                     scales=inp.get("scales"), shared_scales=inp.get("shared_scales"),
-                    n_group=w.n_group, topk_group=w.topk_group, routing=w.routing)
+                    n_group=w.n_group, topk_group=w.topk_group, routing=w.routing,
+                    reroute=w.reroute)
 
 
 class Forward:

@@ -123,14 +123,24 @@ size_t moe_route_workspace_size(int64_t T, int d, int E) {
   return route_ws_bytes(T, d, E);
 }
 
+int check_backups(int k, int E, int n_backup, const int32_t* backup_ids, int64_t T) {
+  const int most = k < E - k ? k : E - k;
+  MOE_REQUIRE(n_backup >= 0 && n_backup <= most, MOE_EINVAL,
+              "n_backup = %d must be in [0, min(k, E - k) = %d]", n_backup, most);
+  MOE_REQUIRE(n_backup == 0 || T == 0 || backup_ids != nullptr, MOE_EINVAL, "NULL backup_ids");
+  return MOE_OK;
+}
+
 int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
               const float* bias, const float* logit_offset, int score, int k, int renorm,
               int n_group, int topk_group, float* logits, int32_t* topk_ids, float* topk_w,
-              float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+              float* prob_sum, int n_backup, int32_t* backup_ids, void* ws, size_t ws_bytes,
+              void* stream) {
   int rc;
   if ((rc = check_dtype(dtype))) return rc;
   if ((rc = check_router_dims(T, d, E, k))) return rc;
   if ((rc = check_groups(E, k, n_group, topk_group))) return rc;
+  if ((rc = check_backups(k, E, n_backup, backup_ids, T))) return rc;
   MOE_REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_EINVAL, "score %d unknown", score);
   MOE_REQUIRE(T == 0 || (X && Wg && topk_ids && topk_w), MOE_EINVAL, "NULL X, Wg, topk_ids or topk_w");
   MOE_REQUIRE(score == MOE_SIGMOID || bias == nullptr, MOE_EINVAL,
@@ -138,7 +148,7 @@ int moe_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
   if ((rc = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E)))) return rc;
   return hip_status(launch_route(X, dtype, T, d, Wg, E, bias, logit_offset, score, k, renorm,
                                  n_group, topk_group, logits, topk_ids, topk_w, prob_sum, ws,
-                                 (hipStream_t)stream),
+                                 (hipStream_t)stream, nullptr, n_backup, backup_ids),
                     "moe_route");
 }
 
@@ -172,15 +182,17 @@ int moe_route_expert_choice(const void* X, int dtype, int64_t T, int d, const vo
 // ---------------------------------------------------------------- dispatch
 size_t moe_dispatch_workspace_size(int64_t T, int k, int E) {
   if (T < 0 || k < 1 || E < 1) return 0;
-  return dispatch_ws_bytes(T, k, E);
+  return dispatch_ws_bytes(T, k, E) + reroute_ws_bytes(T, k, E);
 }
 
 int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E, int64_t capacity,
-                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                 int32_t* n_kept, const void* X, int dtype, int d, void* X_sorted, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 const int32_t* backup_ids, int n_backup, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_slot, int32_t* slot_row, int32_t* n_kept, const void* X,
+                 int dtype, int d, void* X_sorted, void* ws, size_t ws_bytes, void* stream) {
   MOE_REQUIRE(T >= 0, MOE_EINVAL, "T < 0");
   MOE_REQUIRE(E >= 1 && k >= 1 && k <= E, MOE_EINVAL, "need 1 <= k <= E");
+  int rc0;
+  if ((rc0 = check_backups(k, E, n_backup, backup_ids, T))) return rc0;
   MOE_REQUIRE(E <= 256, MOE_EUNSUPPORTED, "E = %d > 256 is not supported", E);
   MOE_REQUIRE(T * (int64_t)k <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large");
   MOE_REQUIRE(counts && offsets && n_kept, MOE_EINVAL, "NULL counts, offsets or n_kept");
@@ -194,10 +206,14 @@ int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E, int64_t capac
     MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_EUNSUPPORTED, "d = %d is not a positive multiple of 128", d);
   }
   int rc;
-  if ((rc = check_ws(ws, ws_bytes, dispatch_ws_bytes(T, k, E)))) return rc;
+  const size_t dws = dispatch_ws_bytes(T, k, E);
+  if ((rc = check_ws(ws, ws_bytes, dws + reroute_ws_bytes(T, k, E)))) return rc;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_dispatch(topk_ids, T, k, E, capacity, 0, counts, offsets, sorted_slot,
                                  slot_row, n_kept, nullptr, ws, s);
+  if (e == hipSuccess && capacity > 0 && n_backup > 0)
+    e = launch_reroute(topk_ids, backup_ids, n_backup, T, k, E, capacity, 0, counts, offsets,
+                       sorted_slot, slot_row, n_kept, nullptr, (char*)ws + dws, s);
   if (e == hipSuccess && gather)
     e = launch_gather(X, sorted_slot, n_kept, T * (int64_t)k, k, d, dtype == MOE_BF16 ? 2 : 4,
                       X_sorted, s);
@@ -270,6 +286,16 @@ int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w
                     "moe_combine");
 }
 
+int moe_bias_update(const int32_t* counts, int64_t T, int k, int E, float gamma, float* bias,
+                    void* stream) {
+  MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1, MOE_EINVAL, "need T >= 0, k >= 1, E >= 1");
+  MOE_REQUIRE(isfinite(gamma) && gamma >= 0.f, MOE_EINVAL, "gamma must be finite and >= 0");
+  MOE_REQUIRE(counts && bias, MOE_EINVAL, "NULL counts or bias");
+  MOE_REQUIRE(T * (int64_t)k <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large");
+  return hip_status(launch_bias_update(counts, T, k, E, gamma, bias, (hipStream_t)stream),
+                    "moe_bias_update");
+}
+
 int moe_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, int E, double* out,
                 void* stream) {
   MOE_REQUIRE(counts && prob_sum && out, MOE_EINVAL, "NULL counts, prob_sum or out");
@@ -281,9 +307,16 @@ int moe_balance(const int32_t* counts, const float* prob_sum, int64_t T, int k, 
 // ----------------------------------------------------------------- forward
 namespace {
 struct FwdLayout {
-  size_t route, ids, w, psum, counts, offsets, nkept, sorted, slotrow, rowtok, hist, ent, yrows, ffn,
-      total;
+  size_t route, ids, w, psum, counts, offsets, nkept, sorted, slotrow, rowtok, hist, ent, backup,
+      rr, yrows, ffn, total;
 };
+
+// Backup experts per token for the overflow re-route: min(k, E - k) when
+// the layer re-routes and has a capacity limit, else 0.
+int layer_backups(const moe_layer* L) {
+  if (!L->reroute || !(L->capacity_factor > 0) || L->routing != MOE_TOKEN_CHOICE) return 0;
+  return L->k < L->E - L->k ? L->k : L->E - L->k;
+}
 
 bool expert_choice(const moe_layer* L) { return L->routing == MOE_EXPERT_CHOICE; }
 
@@ -324,6 +357,8 @@ FwdLayout fwd_layout(const moe_layer* L, int64_t T) {
   o.rowtok = take((size_t)rows * 4);
   o.hist = take(dispatch_ws_bytes(T, L->k, L->E));
   o.ent = take((size_t)MOE_CEIL_DIV(T, 4) * 4);
+  o.backup = take((size_t)T * layer_backups(L) * 4);
+  o.rr = take(layer_backups(L) ? reroute_ws_bytes(T, L->k, L->E) : 0);
   o.yrows = take((size_t)rows * L->d * 4);
   o.ffn = take(ffn_ws_bytes(rows, G, L->d, L->F, L->dtype));
   o.total = at;
@@ -349,6 +384,9 @@ int check_layer(const moe_layer* L, int64_t T) {
   if ((rc = check_groups(L->E, L->k, L->n_group, L->topk_group))) return rc;
   MOE_REQUIRE(L->routing == MOE_TOKEN_CHOICE || L->routing == MOE_EXPERT_CHOICE, MOE_EINVAL,
               "routing %d unknown", L->routing);
+  MOE_REQUIRE(L->reroute == 0 || L->reroute == 1, MOE_EINVAL, "reroute must be 0 or 1");
+  MOE_REQUIRE(!(L->reroute && L->routing == MOE_EXPERT_CHOICE), MOE_EINVAL,
+              "the overflow re-route applies to top-k routing only");
   if (expert_choice(L)) {
     MOE_REQUIRE(!L->renorm && !L->bias && L->n_group <= 1, MOE_EINVAL,
                 "expert-choice routing takes no renorm, bias or groups");
@@ -456,13 +494,18 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
 
   timing_mark("begin", s, 1);
   float* ent = a.health ? (float*)(w + o.ent) : nullptr;
+  const int nb = layer_backups(L);
+  int32_t* backup = (int32_t*)(w + o.backup);
   hipError_t e = launch_route(X, L->dtype, T, L->d, L->Wg, L->E, L->bias, L->logit_offset,
                               L->score, L->k, L->renorm, L->n_group, L->topk_group, a.logits, ids,
-                              gw, psum, w + o.route, s, ent);
+                              gw, psum, w + o.route, s, ent, nb, backup);
   timing_mark("route", s);
   if (e == hipSuccess)
     e = launch_dispatch(ids, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets, sorted, slotrow,
                         nkept, rowtok, w + o.hist, s);
+  if (e == hipSuccess && nb > 0)
+    e = launch_reroute(ids, backup, nb, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets,
+                       sorted, slotrow, nkept, rowtok, w + o.rr, s);
   timing_mark("dispatch", s);
   // With a K-split down projection the combine adds the two partial slabs
   // itself, unless the caller asked for the expert rows (then they are

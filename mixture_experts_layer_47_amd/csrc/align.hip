@@ -145,6 +145,129 @@ __global__ __launch_bounds__(256) void k_align_scatter(
   }
 }
 
+// ----------------------------------------------------------------------------
+// Overflow re-route (AI Knowledge Map "MoE", capacity overflow handled by the
+// second/backup option): one backup round after the capacity drop.  The m-th
+// dropped slot of token t proposes the token's m-th backup expert; experts
+// accept proposals in slot order while they have room; accepted slots are
+// placed after the expert's first-pass rows.
+
+// props[s]: the backup expert dropped slot s proposes, or -1.
+__global__ __launch_bounds__(256) void k_rr_props(const int32_t* __restrict__ slot_row,
+                                                  const int32_t* __restrict__ backup,
+                                                  int64_t T_, int k, int nb,
+                                                  int32_t* __restrict__ props) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T_) return;
+  int m = 0;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    int p = -1;
+    if (slot_row[s] < 0) {
+      if (m < nb) p = backup[t * nb + m];
+      ++m;
+    }
+    props[s] = p;
+  }
+}
+
+// Proposal chunk bases (hist2 becomes exclusive), accepted proposals per
+// expert, and the final offsets.  meta = {first-pass offsets, first-pass
+// kept, accepted} x E.  One block, E <= 256.
+__global__ __launch_bounds__(256) void k_rr_scan(int32_t* __restrict__ hist2, int E,
+                                                 int nchunks, int64_t cap, int tail_rows,
+                                                 const int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ n_kept,
+                                                 int32_t* __restrict__ meta) {
+  __shared__ int32_t tot[256];
+  const int e = threadIdx.x;
+  if (e < E) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int h = hist2[(size_t)c * E + e];
+      hist2[(size_t)c * E + e] = run;
+      run += h;
+    }
+    const int kept1 = counts[e] < cap ? counts[e] : (int)cap;
+    const int room = (int)cap - kept1;
+    const int acc = run < room ? run : room;
+    meta[e] = offsets[e];
+    meta[E + e] = kept1;
+    meta[2 * E + e] = acc;
+    tot[e] = kept1 + acc;
+  }
+  __syncthreads();                                // old offsets read before the rewrite
+  if (e == 0) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+      offsets[i] = acc;
+      acc += tot[i];
+    }
+    offsets[E] = acc;
+    if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
+    n_kept[0] = acc;
+  }
+}
+
+// Final placement of every slot: first-pass rows move by their expert's
+// offset change; proposals are ranked in slot order (wave multisplit on
+// the proposed expert, as in k_align_scatter) and placed after the
+// expert's first-pass rows when the rank is below the accepted count.
+__global__ __launch_bounds__(256) void k_rr_place(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ props, int64_t Tk, int k,
+    int E, int nchunks, const int32_t* __restrict__ base2,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ meta,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token) {
+  __shared__ int32_t cnt_[4][256];
+  __shared__ int32_t off[256], off1[256], kept1[256], acc[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    off[e] = offsets[e];
+    off1[e] = meta[e];
+    kept1[e] = meta[E + e];
+    acc[e] = meta[2 * E + e];
+  }
+  __syncthreads();
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= nchunks) return;
+  volatile int32_t* cnt = cnt_[wave];
+  for (int e = lane; e < E; e += 64) cnt[e] = base2[(size_t)c * E + e];
+  const int nbits = nbits_for(E);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int NG = kAlignChunk / 64;
+  for (int g = 0; g < NG; ++g) {
+    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const bool in = s < Tk;
+    const int p = in ? props[s] : -1;
+    const bool v = p >= 0;
+    const int e = v ? p : 0;
+    const uint64_t eq = match_id(e, v, nbits);
+    int rank = 0;
+    if (v) rank = cnt[e] + __popcll(eq & lt);
+    __builtin_amdgcn_wave_barrier();
+    if (v && (eq & lt) == 0) cnt[e] = rank + __popcll(eq);
+    if (in) {
+      int row = -1;
+      if (v) {
+        if (rank < acc[e]) row = off[e] + kept1[e] + rank;
+      } else {
+        const int r1 = slot_row[s];
+        if (r1 >= 0) {
+          const int e1 = ids[s];
+          row = off[e1] + (r1 - off1[e1]);
+        }
+      }
+      slot_row[s] = row;
+      if (row >= 0) {
+        sorted_slot[row] = (int32_t)s;
+        if (row_token) row_token[row] = (int32_t)(s / k);
+      }
+    }
+  }
+}
+
 // Rows of the shared expert: row_token[R + t] = t, R read on the device.
 __global__ __launch_bounds__(256) void k_tail_tokens(const int32_t* __restrict__ n_kept,
                                                      int T_, int32_t* __restrict__ row_token) {
@@ -201,6 +324,38 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
   if (nch > 0)
     hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(256), 0, s, ids, Tk, k, E, nch, cap,
                        hist, offsets, sorted_slot, slot_row, row_token);
+  if (row_token && tail_rows > 0)
+    hipLaunchKernelGGL(k_tail_tokens, dim3((unsigned)MOE_CEIL_DIV(tail_rows, 256)), dim3(256),
+                       0, s, n_kept, tail_rows, row_token);
+  return hipGetLastError();
+}
+
+size_t reroute_ws_bytes(int64_t T, int k, int E) {
+  const int64_t Tk = T * (int64_t)k;
+  const int nch = align_nchunks(Tk) > 0 ? align_nchunks(Tk) : 1;
+  return align256((size_t)nch * E * sizeof(int32_t)) + align256((size_t)Tk * sizeof(int32_t) + 4) +
+         align256((size_t)3 * E * sizeof(int32_t));
+}
+
+hipError_t launch_reroute(const int32_t* ids, const int32_t* backup, int nb, int64_t T, int k,
+                          int E, int64_t cap, int tail_rows, const int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                          int32_t* n_kept, int32_t* row_token, void* ws, hipStream_t s) {
+  const int64_t Tk = T * (int64_t)k;
+  if (Tk <= 0 || cap <= 0 || nb <= 0) return hipSuccess;
+  const int nch = align_nchunks(Tk);
+  char* p = (char*)ws;
+  int32_t* hist2 = (int32_t*)p;  p += align256((size_t)nch * E * sizeof(int32_t));
+  int32_t* props = (int32_t*)p;  p += align256((size_t)Tk * sizeof(int32_t) + 4);
+  int32_t* meta = (int32_t*)p;
+  hipLaunchKernelGGL(k_rr_props, dim3((unsigned)MOE_CEIL_DIV(T, 256)), dim3(256), 0, s, slot_row,
+                     backup, T, k, nb, props);
+  const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
+  hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(256), 0, s, props, Tk, E, nch, hist2);
+  hipLaunchKernelGGL(k_rr_scan, dim3(1), dim3(256), 0, s, hist2, E, nch, cap, tail_rows, counts,
+                     offsets, n_kept, meta);
+  hipLaunchKernelGGL(k_rr_place, dim3(nblk), dim3(256), 0, s, ids, props, Tk, k, E, nch, hist2,
+                     offsets, meta, sorted_slot, slot_row, row_token);
   if (row_token && tail_rows > 0)
     hipLaunchKernelGGL(k_tail_tokens, dim3((unsigned)MOE_CEIL_DIV(tail_rows, 256)), dim3(256),
                        0, s, n_kept, tail_rows, row_token);

@@ -15,7 +15,10 @@ size_t route_ws_bytes(int64_t T, int d, int E);
 hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* Wg, int E,
                         const float* bias, const float* offset, int score, int k, int renorm,
                         int n_group, int topk_group, float* logits, int32_t* ids, float* w,
-                        float* prob_sum, void* ws, hipStream_t s, float* ent_part = nullptr);
+                        float* prob_sum, void* ws, hipStream_t s, float* ent_part = nullptr,
+                        int n_backup = 0, int32_t* backup = nullptr);
+hipError_t launch_bias_update(const int32_t* counts, int64_t T, int k, int E, float gamma,
+                              float* bias, hipStream_t s);
 // {token entropy, load entropy, load CV, drop rate}; ent_part holds one
 // partial per block of four tokens (written by launch_route).
 hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
@@ -42,6 +45,15 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
                            int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                            int32_t* slot_row, int32_t* n_kept, int32_t* row_token, void* ws,
                            hipStream_t s);
+// One backup round after the capacity drop (cap > 0): launch_dispatch's
+// slot_row / sorted_slot / offsets / n_kept / row_token are rewritten with
+// the dropped slots' accepted backup experts (backup[T][nb], -1 = none).
+// ws: at least reroute_ws_bytes(T, k, E).
+size_t reroute_ws_bytes(int64_t T, int k, int E);
+hipError_t launch_reroute(const int32_t* ids, const int32_t* backup, int nb, int64_t T, int k,
+                          int E, int64_t cap, int tail_rows, const int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                          int32_t* n_kept, int32_t* row_token, void* ws, hipStream_t s);
 hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_t* n_kept,
                          int64_t Tk, int k, int d, int elem_bytes, void* Xs, hipStream_t s);
 

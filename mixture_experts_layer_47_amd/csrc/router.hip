@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_router_select(
     const float* __restrict__ offset, const float* __restrict__ bias, int score,
     int k, int renorm, int n_group, int topk_group, float* __restrict__ logits,
     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part,
-    float* __restrict__ ent_part) {
+    float* __restrict__ ent_part, int nb, int32_t* __restrict__ backup) {
   __shared__ float sp[4][NE * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -189,11 +189,13 @@ __global__ __launch_bounds__(256) void k_router_select(
     }
   }
   if (n_group > 1) limit_groups<NE>(key, aff, E, k, n_group, topk_group, lane);
-  // Iterative wave arg-max, k rounds; lane j keeps the j-th winner.
+  // Iterative wave arg-max, k rounds (plus nb backup rounds: the next
+  // choices in the same key order, -1 for an ineligible expert); lane j
+  // keeps the j-th winner.
   uint32_t taken = 0;
   int my_id = 0;
   double my_val = 0.0, tot = 0.0;
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < k + nb; ++j) {
     double bk = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -209,13 +211,14 @@ __global__ __launch_bounds__(256) void k_router_select(
     for (int i = 0; i < NE; ++i) if (i == oi) mine = s64[i];
     const double val = __shfl(mine, ol);
     if (lane == ol) taken |= 1u << oi;
-    if (lane == j) { my_id = bi; my_val = val; }
-    tot += val;                                  // fixed order j = 0..k-1
+    if (lane == j) { my_id = (bk == -INFINITY) ? -1 : bi; my_val = val; }
+    if (j < k) tot += val;                       // fixed order j = 0..k-1
   }
   if (tok_ok && lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     wts[(size_t)t * k + lane] = (float)(renorm ? my_val / tot : my_val);
   }
+  if (tok_ok && lane >= k && lane < k + nb) backup[(size_t)t * nb + lane - k] = my_id;
   if (ent_part) {  // per-block partial of the tokens' routing entropies
     // q = p, or s / sum(s) for a sigmoid router; -sum q ln q in fp32
     float zs = 0.f;
@@ -569,7 +572,7 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
                         int E, const float* bias, const float* offset, int score,
                         int k, int renorm, int n_group, int topk_group, float* logits,
                         int32_t* ids, float* w, float* prob_sum, void* ws, hipStream_t s,
-                        float* ent_part) {
+                        float* ent_part, int n_backup, int32_t* backup) {
   if (T == 0) {
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
@@ -586,7 +589,7 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
 #define MOE_SEL(NE_)                                                                 \
   hipLaunchKernelGGL(k_router_select<NE_>, dim3(nblk), dim3(256), 0, s, part, split, \
                      (int)T, E, offset, bias, score, k, renorm, n_group, topk_group, logits, \
-                     ids, w, psp, ent_part)
+                     ids, w, psp, ent_part, n_backup, backup)
   switch (ne) {
     case 1: MOE_SEL(1); break;
     case 2: MOE_SEL(2); break;
@@ -604,6 +607,26 @@ hipError_t launch_router_health(const int32_t* counts, const int32_t* n_kept,
                                 hipStream_t s) {
   hipLaunchKernelGGL(k_router_health, dim3(1), dim3(256), 0, s, counts, n_kept, ent_part,
                      (int)MOE_CEIL_DIV(T, 4), T, k, E, out);
+  return hipGetLastError();
+}
+
+// Selection-bias update (LLM Internals 14.2.3, DeepSeek-V3's load rule):
+// bias[e] -= gamma if counts[e] > T*k/E, += gamma if below, unchanged if
+// equal; the comparison counts[e]*E vs T*k is exact in integers.
+__global__ __launch_bounds__(256) void k_bias_update(const int32_t* __restrict__ counts,
+                                                     int64_t tk, int E, float gamma,
+                                                     float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = (int64_t)counts[e] * E;
+  if (load > tk) bias[e] -= gamma;
+  else if (load < tk) bias[e] += gamma;
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int64_t T, int k, int E, float gamma,
+                              float* bias, hipStream_t s) {
+  hipLaunchKernelGGL(k_bias_update, dim3((unsigned)MOE_CEIL_DIV(E, 256)), dim3(256), 0, s,
+                     counts, T * (int64_t)k, E, gamma, bias);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ class Workload:
     n_group: int = 1               # group-limited routing: groups of E / n_group experts
     topk_group: int = 1            # groups a token may use
     routing: str = "token"         # "token" (top-k) | "expert" (each expert takes C tokens)
+    reroute: bool = False          # capacity overflow re-routed to a backup expert
     seed: int = 0                  # seed of the weights
     x_seed: int | None = None      # seed of X (defaults to ``seed``)
     note: str = field(default="", compare=False)
@@ -105,6 +106,11 @@ WORKLOADS["dsv3_prefill_ec"] = WORKLOADS["dsv3_prefill"].with_(
     name="dsv3_prefill_ec", routing="expert", renorm=False, bias_std=None,
     note="DeepSeek-V3-shaped prefill, expert choice (sigmoid scores), 128 tokens per expert")
 
+# The skewed Switch layer with its overflow re-routed to each token's second choice.
+WORKLOADS["switch_capacity_reroute"] = WORKLOADS["switch_capacity"].with_(
+    name="switch_capacity_reroute", reroute=True,
+    note="Switch-style top-1, skewed, CF 1.0, overflow re-routed to the second choice")
+
 # Reduced versions: same routing rule and dtype, sizes the CPU oracle finishes
 # in seconds, with several tiles per expert and ragged tails.
 SMALL = {
@@ -130,6 +136,13 @@ SMALL["dsv3_prefill_ec"] = SMALL["dsv3_prefill"].with_(
     name="dsv3_prefill_ec_small", routing="expert", renorm=False, bias_std=None)
 SMALL["tiny_fp32_ec"] = SMALL["tiny_fp32"].with_(
     name="tiny_fp32_ec", routing="expert", renorm=False, cf=1.25)
+SMALL["switch_capacity_reroute"] = SMALL["switch_capacity"].with_(
+    name="switch_capacity_reroute_small", reroute=True)
+SMALL["dsv3_prefill_reroute"] = SMALL["dsv3_prefill"].with_(
+    name="dsv3_prefill_reroute_small", cf=1.0, reroute=True)
+SMALL["mixtral_grouped_reroute"] = SMALL["mixtral_prefill"].with_(
+    name="mixtral_grouped_reroute_small", E=16, k=4, n_group=4, topk_group=2, cf=0.9,
+    reroute=True)
 SMALL["mixtral_grouped"] = SMALL["mixtral_prefill"].with_(
     name="mixtral_grouped_small", E=16, k=4, n_group=4, topk_group=2)
 

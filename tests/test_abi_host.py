@@ -74,11 +74,12 @@ def test_down_projection_split_decision(L):
 
 def _route(L, **over):
     a = dict(X=1, dtype=1, T=16, d=256, Wg=1, E=8, bias=None, off=None, score=0, k=2, renorm=1,
-             ng=1, tg=1, logits=None, ids=1, w=1, ps=None, ws=256, ws_bytes=1 << 30, stream=None)
+             ng=1, tg=1, logits=None, ids=1, w=1, ps=None, nb=0, bk=None, ws=256,
+             ws_bytes=1 << 30, stream=None)
     a.update(over)
     return L.moe_route(a["X"], a["dtype"], a["T"], a["d"], a["Wg"], a["E"], a["bias"], a["off"],
                        a["score"], a["k"], a["renorm"], a["ng"], a["tg"], a["logits"], a["ids"],
-                       a["w"], a["ps"], a["ws"], a["ws_bytes"], a["stream"])
+                       a["w"], a["ps"], a["nb"], a["bk"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_route_validation(L):
@@ -103,15 +104,21 @@ def test_route_validation(L):
     assert _route(L, ws=None) == -1
     assert _route(L, ws=257) == -1              # misaligned workspace
     assert "workspace" in _lib.last_error()
+    # backups: at most min(k, E - k) per token, and a buffer for them
+    assert _route(L, nb=1) == -1                # NULL backup_ids
+    assert _route(L, nb=3, bk=1) == -1          # more backups than k
+    assert _route(L, k=6, nb=3, bk=1) == -1     # more backups than E - k
+    assert _route(L, nb=-1) == -1
 
 
 def test_dispatch_validation(L):
-    base = dict(ids=1, T=16, k=2, E=8, cap=0, counts=1, offsets=1, sorted=1, slot=1, nk=1,
-                X=None, dt=1, d=0, Xs=None, ws=256, wsb=1 << 30)
+    base = dict(ids=1, T=16, k=2, E=8, cap=0, bk=None, nb=0, counts=1, offsets=1, sorted=1,
+                slot=1, nk=1, X=None, dt=1, d=0, Xs=None, ws=256, wsb=1 << 30)
 
     def call(**o):
         a = dict(base, **o)
-        return L.moe_dispatch(a["ids"], a["T"], a["k"], a["E"], a["cap"], a["counts"],
+        return L.moe_dispatch(a["ids"], a["T"], a["k"], a["E"], a["cap"], a["bk"], a["nb"],
+                              a["counts"],
                               a["offsets"], a["sorted"], a["slot"], a["nk"], a["X"], a["dt"],
                               a["d"], a["Xs"], a["ws"], a["wsb"], None)
     assert call(k=9) == -1
@@ -121,6 +128,11 @@ def test_dispatch_validation(L):
     assert call(Xs=1, X=1, d=100) == -2
     assert call(E=257, k=1) == -2
     assert call(wsb=0) == -3
+    assert call(cap=4, nb=1) == -1              # backups announced, none given
+    assert call(cap=4, nb=3, bk=1) == -1        # more than k
+    # the workspace covers the re-route's scratch as well
+    assert (L.moe_dispatch_workspace_size(4096, 8, 256)
+            >= 2 * 4 * 256 * 4 + 4096 * 8 * 4)
 
 
 def test_ffn_and_combine_validation(L):
@@ -219,3 +231,33 @@ def test_expert_choice_forward_validation(L):
     ec = lay(d=d, E=E, k=k, F=F)
     assert (L.moe_forward_workspace_size(ctypes.byref(ec), T)
             > L.moe_forward_workspace_size(ctypes.byref(tc), T))
+
+
+def test_bias_update_validation(L):
+    assert L.moe_bias_update(None, 16, 2, 8, 0.001, 1, None) == -1
+    assert L.moe_bias_update(1, 16, 2, 8, 0.001, None, None) == -1
+    assert L.moe_bias_update(1, 16, 0, 8, 0.001, 1, None) == -1
+    assert L.moe_bias_update(1, 16, 2, 8, -0.5, 1, None) == -1
+    assert L.moe_bias_update(1, 16, 2, 8, float("nan"), 1, None) == -1
+
+
+def test_reroute_layer_validation(L):
+    def lay(**o):
+        a = dict(dtype=1, score=0, renorm=1, d=256, E=8, k=2, F=512, ns=0, cf=1.0, Wg=1,
+                 bias=None, off=None, W1=1, W3=1, W2=1, Ws1=None, Ws3=None, Ws2=None)
+        a.update(o)
+        return _lib.MoeLayerC(*a.values())
+
+    def fwd(layer, T=16):
+        return L.moe_forward(ctypes.byref(layer), 1, T, 1, None, 256, 1 << 40, None)
+    bad = lay()
+    bad.reroute = 2
+    assert fwd(bad) == -1
+    ec = lay(renorm=0)
+    ec.routing, ec.reroute = _lib.MOE_EXPERT_CHOICE, 1
+    assert fwd(ec) == -1
+    # re-routing needs room for min(k, E - k) backups per token in the workspace
+    rr = lay()
+    rr.reroute = 1
+    assert (L.moe_forward_workspace_size(ctypes.byref(rr), 4096)
+            > L.moe_forward_workspace_size(ctypes.byref(lay()), 4096))

@@ -58,7 +58,9 @@ def test_fullsize_workload(name):
 
     # --- D1: dispatch on every slot, bit-exact
     cap = O.capacity(w.cf, w.T, w.k, w.E) if w.cf else None
-    d = O.dispatch(ids, w.E, cap)
+    bk = (O.backup_experts(lg, w.k, w.score, bias, w.n_group, w.topk_group) if w.reroute
+          else None)
+    d = O.dispatch(ids, w.E, cap, bk)
     R = d["n_kept"]
     assert int(aux["n_kept"].item()) == R
     assert aux["counts"].cpu().numpy().tolist() == d["counts"].tolist()
@@ -97,7 +99,8 @@ def test_fullsize_workload(name):
     assert np.abs(ps - p_ref.sum(axis=0)).max() <= 1e-4 * max(1.0, ps.max())
     bal = O.balance_stat(d["counts"], p_ref.sum(axis=0), w.T, w.k)
     assert abs(aux["balance"].item() - bal) <= 1e-5 * max(1.0, bal)
-    print(f"[info] {name}: R={R} dropped={w.T * w.k - R} touched={touched.size} "
+    print(f"[info] {name}: R={R} dropped={w.T * w.k - R} re-routed={d['n_rerouted']} "
+          f"touched={touched.size} "
           f"balance={bal:.4f}", flush=True)
 
 

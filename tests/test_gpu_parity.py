@@ -27,7 +27,7 @@ def _oracle_forward(inp, lg_gpu):
     return O.forward(L["X"], L["Wg"], L["W1"], L["W3"], L["W2"], k=w.k, score_func=w.score,
                      renorm=w.renorm, bias=L["bias"], offset=L["offset"], cap=cap,
                      shared=L["shared"], bf16_h=(w.dtype == "bf16"), logits=lg_gpu,
-                     n_group=w.n_group, topk_group=w.topk_group), cap
+                     n_group=w.n_group, topk_group=w.topk_group, reroute=w.reroute), cap
 
 
 def _full_check(inp):
@@ -46,9 +46,13 @@ def _full_check(inp):
                        keys if w.score == "sigmoid" else None)
     assert ties == 0, "near-tie reordering in a small workload"
     H.check_gates(H.np64(aux["topk_w"]), ref["gates"])
-    # D1: dispatch bit-exact
+    # D1: dispatch bit-exact (with the backup round when the layer re-routes)
     d = ref["dispatch"]
     R = d["n_kept"]
+    if w.reroute:
+        print(f"[info] {w.name}: re-routed {d['n_rerouted']} of "
+              f"{w.T * w.k - O.dispatch(ref['ids'], w.E, cap)['n_kept']} dropped slots",
+              flush=True)
     assert int(aux["n_kept"].item()) == R
     assert aux["counts"].cpu().numpy().tolist() == d["counts"].tolist()
     assert aux["offsets"].cpu().numpy().tolist() == d["offsets"].tolist()
@@ -63,7 +67,8 @@ def _full_check(inp):
     # C: layer output
     H.check_rows(H.np64(Y), ref["Y"], bf16, f"{w.name} Y", output_rounding=True)
     # dropped-everything tokens are exactly zero
-    dead = (np.asarray(d["slot_row"]).reshape(w.T, w.k) < 0).all(axis=1)
+    dead = (np.asarray(d["slot_row"]).reshape(w.T, w.k) < 0).all(axis=1) if w.T else \
+        np.zeros(0, bool)
     if ref["shared"] is None and dead.any():
         assert (H.np64(Y)[dead] == 0).all()
     # B: prob_sum and the balance statistic
@@ -275,6 +280,21 @@ def test_route_entry_point(score, ng, tg):
     H.check_ids(H.np64(r["ids"]).astype(np.int64), ids, keys)
     H.check_gates(H.np64(r["w"]), g)
     assert np.allclose(H.np64(r["prob_sum"]), p.sum(axis=0), rtol=1e-5, atol=1e-5)
+    # backups: the next choices in the same key order
+    rb = moe.route(inp["X"], inp["Wg"], w.k, w.score, w.renorm, bias=inp["bias"], n_group=ng,
+                   topk_group=tg, n_backup=min(w.k, w.E - w.k))
+    torch.cuda.synchronize()
+    assert torch.equal(rb["ids"], r["ids"]) and torch.equal(rb["w"], r["w"])
+    bk_ref = O.backup_experts(lg, w.k, w.score, L["bias"], ng, tg)
+    bk = H.np64(rb["backup"]).astype(np.int64)
+    if w.score == "softmax":
+        assert np.array_equal(bk, bk_ref)
+    else:   # near-ties aside; the device's picks must hold keys equal to the oracle's
+        diff = np.flatnonzero((bk != bk_ref).any(axis=1))
+        for t in diff:
+            kg = np.where(bk[t] >= 0, keys[t, np.maximum(bk[t], 0)], -np.inf)
+            kr = np.where(bk_ref[t] >= 0, keys[t, np.maximum(bk_ref[t], 0)], -np.inf)
+            assert np.allclose(kg, kr, atol=H.SIGMOID_TIE, rtol=0), t
 
 
 @pytest.mark.parametrize("score,T,E,C", [("softmax", 333, 32, 40), ("sigmoid", 333, 32, 40),
@@ -311,16 +331,24 @@ def test_route_expert_choice_entry_point(score, T, E, C):
 @pytest.mark.parametrize("T,k,E,C", [(1, 1, 1, 0), (100, 2, 8, 0), (1000, 8, 256, 0),
                                      (1000, 8, 256, 20), (3000, 1, 64, 40), (777, 3, 5, 1),
                                      (5000, 4, 17, 900)])
-def test_dispatch_entry_point(T, k, E, C):
-    _announce(f"moe_dispatch T={T} k={k} E={E} C={C}")
+@pytest.mark.parametrize("reroute", [False, True])
+def test_dispatch_entry_point(T, k, E, C, reroute):
+    _announce(f"moe_dispatch T={T} k={k} E={E} C={C} reroute={reroute}")
     g = torch.Generator().manual_seed(T * 31 + E)
-    # skewed distinct ids per token
+    # skewed distinct ids per token; the next choices are the backups
     pri = torch.rand((T, E), generator=g) * torch.linspace(1.0, 3.0, E)
-    ids = torch.topk(pri, k, dim=1).indices.to(torch.int32)
+    nb = min(k, E - k) if reroute else 0
+    order = torch.topk(pri, k + nb, dim=1).indices.to(torch.int32)
+    ids = order[:, :k].contiguous()
+    bk = order[:, k:].contiguous() if nb else None
+    if nb:
+        bk[::7, -1] = -1                   # some tokens without a last backup
     X = torch.randn((T, 128), generator=g).to(torch.bfloat16)
-    out = moe.dispatch(ids.to(DEV), E, C, X=X.to(DEV))
+    out = moe.dispatch(ids.to(DEV), E, C, X=X.to(DEV),
+                       backup=None if bk is None else bk.to(DEV))
     torch.cuda.synchronize()
-    ref = O.dispatch(ids.numpy(), E, C if C > 0 else None)
+    ref = O.dispatch(ids.numpy(), E, C if C > 0 else None,
+                     None if bk is None else bk.numpy())
     R = ref["n_kept"]
     assert int(out["n_kept"].item()) == R
     assert out["counts"].cpu().tolist() == ref["counts"].tolist()
@@ -423,6 +451,26 @@ def test_combine_entry_point(T, k, d, keep):
                      output_rounding=True)
         if dt == torch.float32:
             assert H.rel_err(H.np64(Y), ref) <= 1e-6
+
+
+def test_bias_update_entry_point():
+    """The load rule on the capacity example's loads [5, 3, 2, 2] and on a
+    random 256-expert step, against the oracle (one fp32 addition each)."""
+    _announce("moe_bias_update")
+    b = torch.tensor([0.5, -0.25, 0.0, 1.0], device=DEV)
+    moe.bias_update(torch.tensor([5, 3, 2, 2], dtype=torch.int32, device=DEV), 6, 2, 0.001, b)
+    ref = O.bias_update([0.5, -0.25, 0.0, 1.0], [5, 3, 2, 2], 6, 2, 0.001)
+    assert np.allclose(H.np64(b), ref, rtol=0, atol=2 ** -23)
+    assert b[1].item() == -0.25                      # load at the mean: unchanged
+    g = torch.Generator().manual_seed(3)
+    counts = torch.randint(0, 260, (256,), generator=g, dtype=torch.int32)
+    counts[:4] = 128                                 # 4096 * 8 / 256 = 128: the mean
+    b0 = torch.randn(256, generator=g) * 0.01
+    b = b0.to(DEV)
+    moe.bias_update(counts.to(DEV), 4096, 8, 0.001, b)
+    ref = O.bias_update(b0.double().numpy(), counts.numpy(), 4096, 8, 0.001)
+    assert np.abs(H.np64(b) - ref).max() <= 2 ** -24 * 0.05 + 1e-9
+    assert torch.equal(b[:4].cpu(), b0[:4])
 
 
 def test_balance_entry_point_page_example():
