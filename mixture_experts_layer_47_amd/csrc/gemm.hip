@@ -35,6 +35,7 @@
 //     accumulators before one rounding of h to the storage type.
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -56,12 +57,6 @@ __device__ __forceinline__ void mma_32x32(f32x16& acc, const u32x4& a, const u32
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
 
-template <typename T>
-__device__ __forceinline__ void store_h(T* p, float v);
-template <>
-__device__ __forceinline__ void store_h<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
-template <>
-__device__ __forceinline__ void store_h<float>(float* p, float v) { *p = v; }
 
 constexpr int kThreads = 256;   // four waves per block
 
@@ -119,12 +114,16 @@ __device__ __forceinline__ void load_frags(u32x4* f, const u32x4* pa, const u32x
 }
 
 // MFMAs of one substep for the first NV 32-row blocks of the wave's tile.
+// The weight fragment is the MFMA's first operand, so each accumulator holds
+// a transposed 32x32 block: lane & 31 selects the token row, and element
+// 4q + e (q, e < 4) the output column 8q + 4 (lane >> 5) + e, i.e. every
+// lane owns runs of four consecutive outputs of one row.
 template <typename T, int NV, int FM, int FN>
 __device__ __forceinline__ void mma_substep(f32x16 (&acc)[FM][FN], const u32x4* f) {
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) mma_32x32<T>(acc[i][j], f[i], f[FM + j]);
+    for (int j = 0; j < FN; ++j) mma_32x32<T>(acc[i][j], f[FM + j], f[i]);
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -238,14 +237,30 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
   if constexpr (NV > 0) mma_substep<T, NV, FM, FN>(acc, f1);
 }
 
-// Tile epilogue.  32x32 C layout: lane holds column (lane & 31) and rows
-// 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.  Row offsets are compile-
-// time constants compared with the tile's remaining rows, and addresses are
-// formed from the tile's first row.
+// Tile epilogue.  Accumulator layout (see mma_substep): lane & 31 is the
+// row inside a 32-row block, element 4q + e the column 8q + 4 (lane >> 5) + e
+// of a 32-column block, so every lane stores runs of four consecutive
+// outputs of its row: 8 bytes of bf16 h or 16 bytes of fp32 y per store.
+// Rows past the tile's last row are masked per lane.
 //   GLU : out = H (type T), h = silu(gate) * up rounded once
 //   else: split 0 writes fp32 to out, split ks > 0 to slab ks - 1 of out2
 // With SC (FP8 weights) the accumulators are first multiplied by the
 // per-output-channel scales: gate by sc0[n], up by sc1[n], down by sc0[n].
+template <typename T>
+__device__ __forceinline__ void store4_h(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4_h<uint16_t>(uint16_t* p, float a, float b, float c,
+                                                   float d) {
+  uint2 v;
+  v.x = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  v.y = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+  *(uint2*)p = v;
+}
+template <>
+__device__ __forceinline__ void store4_h<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+
 template <typename T, int BN, int BNT, int WN, int FM, int FN, bool GLU, bool SC = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __restrict__ out,
                                            float* __restrict__ out2, int ks, int max_rows, int N,
@@ -254,50 +269,63 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __
                                            const float* __restrict__ sc1 = nullptr) {
   constexpr int FNH = GLU ? FN / 2 : FN;
   constexpr int WCOLS = BNT / WN;
-  const int lrow0 = arow0 + (lane >> 5) * 4;          // this lane's first row
-  const int rem = rows - lrow0;                        // rows this lane may store
-  const size_t row0 = (size_t)(rbeg + lrow0);
+  const int lr = arow0 + (lane & 31);                 // this lane's row in block 0
+  const int cq = 4 * (lane >> 5);                     // column offset inside 8-column runs
   if constexpr (GLU) {
-    const int c0 = n0 + wn * (BN / WN) + (lane & 31);
-    float sg[FNH], su[FNH];
+    const int cb = n0 + wn * (BN / WN) + cq;
+    float4 sg[FNH][4], su[FNH][4];
 #pragma unroll
-    for (int j = 0; j < FNH; ++j) {
-      sg[j] = SC ? sc0[c0 + j * 32] : 1.f;
-      su[j] = SC ? sc1[c0 + j * 32] : 1.f;
-    }
-    T* H = (T*)out + row0 * N + c0;
+    for (int j = 0; j < FNH; ++j)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int q = 0; q < 4; ++q) {
+        sg[j][q] = SC ? *(const float4*)(sc0 + cb + j * 32 + 8 * q) : make_float4(1.f, 1.f, 1.f, 1.f);
+        su[j][q] = SC ? *(const float4*)(sc1 + cb + j * 32 + 8 * q) : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = i * 32 + (r >> 2) * 8 + (r & 3);
-        if (off < rem) {
+    for (int i = 0; i < FM; ++i) {
+      const int row = lr + i * 32;
+      if (row < rows) {
+        T* H = (T*)out + (size_t)(rbeg + row) * N + cb;
 #pragma unroll
-          for (int j = 0; j < FNH; ++j) {
-            const float g = SC ? acc[i][j][r] * sg[j] : acc[i][j][r];
-            const float u = SC ? acc[i][j + FNH][r] * su[j] : acc[i][j + FNH][r];
-            store_h<T>(H + (size_t)off * N + j * 32, silu_f(g) * u);
+        for (int j = 0; j < FNH; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& g = acc[i][j];
+            const f32x16& u = acc[i][j + FNH];
+            const float4 a = sg[j][q], b = su[j][q];
+            store4_h<T>(H + j * 32 + 8 * q,
+                        silu_f(g[4 * q] * a.x) * (u[4 * q] * b.x),
+                        silu_f(g[4 * q + 1] * a.y) * (u[4 * q + 1] * b.y),
+                        silu_f(g[4 * q + 2] * a.z) * (u[4 * q + 2] * b.z),
+                        silu_f(g[4 * q + 3] * a.w) * (u[4 * q + 3] * b.w));
           }
-        }
       }
+    }
   } else {
-    const int c0 = n0 + wn * WCOLS + (lane & 31);
-    float sy[FN];
+    const int cb = n0 + wn * WCOLS + cq;
+    float4 sy[FN][4];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) sy[j] = SC ? sc0[c0 + j * 32] : 1.f;
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sy[j][q] = SC ? *(const float4*)(sc0 + cb + j * 32 + 8 * q) : make_float4(1.f, 1.f, 1.f, 1.f);
     float* Yb = ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N;
-    float* Y = Yb + row0 * N + c0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int row = lr + i * 32;
+      if (row < rows) {
+        float* Y = Yb + (size_t)(rbeg + row) * N + cb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = i * 32 + (r >> 2) * 8 + (r & 3);
-        if (off < rem) {
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            Y[(size_t)off * N + j * 32] = SC ? acc[i][j][r] * sy[j] : acc[i][j][r];
-        }
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& y = acc[i][j];
+            const float4 c = sy[j][q];
+            *(float4*)(Y + j * 32 + 8 * q) = make_float4(y[4 * q] * c.x, y[4 * q + 1] * c.y,
+                                                         y[4 * q + 2] * c.z, y[4 * q + 3] * c.w);
+          }
       }
+    }
   }
 }
 
@@ -410,7 +438,9 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 // bf16 activations, bf16 or FP8 (E4M3) weights; tiles with BM, BNT multiples
 // of 32.  A stage covers 64 K-elements (KB = 128) or 32 (KB = 64): KB bytes of
 // every A row and, for bf16 weights, of every B row (KB / 2 bytes for FP8).
-// NBUF stages live in a ring of distinct LDS arrays.  global_load_lds moves
+// The A parts of NBA stages and the B parts of NBB >= NBA stages live in two
+// rings of distinct LDS arrays, so weight rows (streamed from HBM) can be
+// fetched further ahead than the activation rows (mostly L2 / MALL hits).  global_load_lds moves
 // 16 B per lane from global memory straight into LDS (lane L of one wave
 // instruction fills bytes [16 L, 16 L + 16) of a 1 KB block = 1024 / rowbytes
 // rows), so stages never pass through registers.  LDS row r keeps chunk c
@@ -420,14 +450,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 // registers (exact: every E4M3 value is a bf16 value); the per-output-channel
 // scales are applied to the fp32 accumulators in the epilogue.
 //
-// Iteration s (stage s in buffer s mod NBUF):
-//   wait until this wave's copies of stage s have landed (those of the
-//   NBUF - 2 later stages may still be in flight) and its LDS reads are done
-//   barrier: every wave's copies of stage s are visible, and buffer
-//   (s - 1) mod NBUF is no longer read
-//   start the copies of stage s + NBUF - 1 into buffer (s - 1) mod NBUF
+// Iteration s (A part of stage s in A buffer s mod NBA, B part in B buffer
+// s mod NBB):
+//   wait until this wave's copies of stage s have landed (later copies may
+//   still be in flight) and its LDS reads are done
+//   barrier: every wave's copies of stage s are visible, and the buffers of
+//   stage s - 1 are no longer read
+//   start the copies of A part s + NBA - 1 and B part s + NBB - 1 into the
+//   buffers stage s - 1 used
 //   per k16 substep: MFMA the previous substep's fragments | read this one's
-// Copies past the last stage re-fetch it (in bounds, never read), so every
+// Copies past the last stage re-fetch it (in bounds, never read), and the
+// prologue issues stand-in copies in place of negative stages, so every
 // wave always has the same number of copies in flight.
 template <int RB>
 __device__ __forceinline__ int swz_rb(int r) {       // RB = row bytes per stage
@@ -455,25 +488,31 @@ struct StageGeo {
   static constexpr int SZ = BM * CPA + BNT * CPB;                // 16-B slots per stage
 };
 
-// Copies of one stage: instruction i of wave w fills A rows (w CA + i) RPA ..
-// + RPA and B rows (w CB + i) RPB .. + RPB of the buffer.  pa[i], pb[i]: this
-// lane's source of copy i at stage 0; koff is the stage's first K element.
-template <int BM, int BNT, int KB, bool Q8, typename TB>
-__device__ __forceinline__ void dma_stage(u32x4* buf,
-                                          const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                          const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
-                                          int koff, int wave) {
+// Copies of one stage's A or B part: instruction i of wave w fills A rows
+// (w CA + i) RPA .. + RPA of an A buffer, or B rows (w CB + i) RPB .. + RPB
+// of a B buffer.  pa[i], pb[i]: this lane's source of copy i at stage 0;
+// koff is the stage's first K element.
+template <int BM, int BNT, int KB, bool Q8>
+__device__ __forceinline__ void dma_a(u32x4* buf,
+                                      const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
+                                      int koff, int wave) {
   using G = StageGeo<BM, BNT, KB, Q8>;
 #pragma unroll
   for (int i = 0; i < G::CA; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
                                      (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA), 16,
                                      0, 0);
+}
+template <int BM, int BNT, int KB, bool Q8, typename TB>
+__device__ __forceinline__ void dma_b(u32x4* buf,
+                                      const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                      int koff, int wave) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
 #pragma unroll
   for (int i = 0; i < G::CB; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(pb[i] + koff),
-                                     (void*)(buf + G::BOFF + ((wave * G::CB + i) * G::RPB) * G::CPB),
-                                     16, 0, 0);
+                                     (void*)(buf + ((wave * G::CB + i) * G::RPB) * G::CPB), 16,
+                                     0, 0);
 }
 
 // Eight E4M3 bytes -> eight bf16 in MFMA operand order (byte i is element i),
@@ -525,13 +564,14 @@ struct FragAddr {
 // MFMAs and fragment reads of one stage held in `cur`: per k16 substep, MFMA
 // the previous substep's fragments while reading this one's.
 template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, bool Q8>
-__device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cur,
-                                          u32x4 (&f0)[FM + FN], u32x4 (&f1)[FM + FN],
-                                          const FragAddr& fr, bool with_copies) {
+__device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* curA,
+                                          const u32x4* curB, u32x4 (&f0)[FM + FN],
+                                          u32x4 (&f1)[FM + FN], const FragAddr& fr,
+                                          bool with_copies) {
   using G = StageGeo<BM, BNT, KB, Q8>;
   constexpr int NSUB = KB / 32;              // k16 substeps per stage
-  const u32x4* pa = cur + fr.fa;
-  const u32x4* pb = cur + G::BOFF + fr.fb;
+  const u32x4* pa = curA + fr.fa;
+  const u32x4* pb = curB + fr.fb;
 #pragma unroll
   for (int q = 0; q < NSUB; q += 2) {
     load_frags_dma<NV, FM, FN, BN, GLU, G::CPA, G::CPB, Q8>(f0, pa, pb, fr.cs[q], fr.csb[q],
@@ -567,59 +607,90 @@ __device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cu
   }
 }
 
-template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBUF, bool Q8,
-          typename TB>
-__device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring& rb,
+constexpr int gcd_i(int a, int b) { return b ? gcd_i(b, a % b) : a; }
+
+// One iteration of the ring (see above) for stage s = s0 + h, h a
+// compile-time position in the ring period.
+template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
+          bool Q8, typename TB, int H>
+__device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra, const Ring& rb,
+                                          const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
+                                          const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                          int s, int nk, u32x4 (&f0)[FM + FN],
+                                          u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
+  constexpr int BK = KB / 2;                 // K-elements per stage
+  // The last copy stage s needs is its A part when NBB > NBA (its B part was
+  // issued earlier); after it come this iteration's B copies and NBA - 2
+  // more iterations of copies.
+  constexpr int WAITN = (NBB > NBA ? G::CB : 0) + (NBA - 2) * (G::CA + G::CB);
+  wait_vm_lgkm<WAITN>();
+  __builtin_amdgcn_s_barrier();
+  const int ta = s + NBA - 1, tb = s + NBB - 1;
+  dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa, (ta < nk ? ta : nk - 1) * BK, wave);
+  dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
+                             wave);
+  if constexpr (NV > 0)
+    stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(H % NBA, ra), ring(H % NBB, rb),
+                                                    f0, f1, fr, true);
+}
+
+template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
+          bool Q8, typename TB, int... Hs>
+__device__ __forceinline__ void ring_period(f32x16 (&acc)[FM][FN], const Ring& ra,
+                                            const Ring& rb,
+                                            const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
+                                            const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                            int s0, int nk, int limit, u32x4 (&f0)[FM + FN],
+                                            u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave,
+                                            std::integer_sequence<int, Hs...>) {
+  // limit: stages of this period to run (the whole period in the loop, the
+  // remainder in the tail); uniform across the block
+  ((Hs < limit ? ring_step<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB, Hs>(
+                     acc, ra, rb, pa, pb, s0 + Hs, nk, f0, f1, fr, wave)
+               : (void)0),
+   ...);
+}
+
+template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
+          bool Q8, typename TB>
+__device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring& ra,
+                                              const Ring& rb,
                                               const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
                                               const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
                                               int nk, const FragAddr& fr, int wave) {
-  using G = StageGeo<BM, BNT, KB, Q8>;
+  static_assert(NBA >= 2 && NBB >= NBA, "A ring of >= 2 buffers, B ring at least as deep");
   constexpr int NF = FM + FN;
-  constexpr int BK = KB / 2;                 // K-elements per stage
-  // The last buffer first receives a throw-away copy (stage 0 again), so the
-  // copies in flight when the loop is entered target the same buffers, in
-  // the same order, as at the end of every loop iteration.
-  dma_stage<BM, BNT, KB, Q8, TB>(ring(NBUF - 1, rb), pa, pb, 0, wave);
+  constexpr int BK = KB / 2;
+  constexpr int P = NBA / gcd_i(NBA, NBB) * NBB;       // ring period
+  // Prologue: virtual iterations i = -(NBB - 1) .. -1 issue what iteration i
+  // would (A part i + NBA - 1, B part i + NBB - 1); a negative A stage is a
+  // stand-in copy of stage 0 into the buffer it would use.
 #pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    dma_stage<BM, BNT, KB, Q8, TB>(ring(p, rb), pa, pb, (p < nk ? p : nk - 1) * BK, wave);
+  for (int i = -(NBB - 1); i < 0; ++i) {
+    const int sa = i + NBA - 1, sb = i + NBB - 1;
+    dma_a<BM, BNT, KB, Q8>(ring(((sa % NBA) + NBA) % NBA, ra), pa,
+                           (sa < 0 ? 0 : (sa < nk ? sa : nk - 1)) * BK, wave);
+    dma_b<BM, BNT, KB, Q8, TB>(ring(sb % NBB, rb), pb, (sb < nk ? sb : nk - 1) * BK, wave);
+  }
   u32x4 f0[NF], f1[NF];
 #pragma unroll
   for (int x = 0; x < NF; ++x) f1[x] = u32x4{0u, 0u, 0u, 0u};
-  const int nfull = nk - nk % NBUF;
-  for (int s0 = 0; s0 < nfull; s0 += NBUF) {
-#pragma unroll
-    for (int h = 0; h < NBUF; ++h) {
-      const int s = s0 + h;
-      wait_vm_lgkm<(NBUF - 2) * (G::CA + G::CB)>();
-      __builtin_amdgcn_s_barrier();
-      const int t = s + NBUF - 1;
-      dma_stage<BM, BNT, KB, Q8, TB>(ring((h + NBUF - 1) % NBUF, rb), pa, pb,
-                                     (t < nk ? t : nk - 1) * BK, wave);
-      if constexpr (NV > 0)
-        stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(h, rb), f0, f1, fr, true);
-    }
-  }
-  // Tail (nk mod NBUF stages): their copies were all started inside the loop
-  // (copies are issued NBUF - 1 stages ahead), so only waits remain.
-  for (int s = nfull; s < nk; ++s) {
-    wait_vm_lgkm<0>();
-    __builtin_amdgcn_s_barrier();
-    if constexpr (NV > 0) {
-      const int h = s % NBUF;
-#pragma unroll
-      for (int c = 0; c < NBUF; ++c)
-        if (h == c)
-          stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(c, rb), f0, f1, fr, false);
-    }
-  }
+  const int nfull = nk - nk % P;
+  for (int s0 = 0; s0 < nfull; s0 += P)
+    ring_period<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB>(
+        acc, ra, rb, pa, pb, s0, nk, P, f0, f1, fr, wave, std::make_integer_sequence<int, P>{});
+  if (nfull < nk)
+    ring_period<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB>(
+        acc, ra, rb, pa, pb, nfull, nk, nk - nfull, f0, f1, fr, wave,
+        std::make_integer_sequence<int, P>{});
   if constexpr (NV > 0) mma_substep<uint16_t, NV, FM, FN>(acc, f1);
   wait_vm_lgkm<0>();   // no copy may still be landing when the block ends
 }
 
 // TB = uint16_t (bf16 weights) or uint8_t (E4M3 weights, Q8, with scales
 // sc0/sc1 [G][N] and sc0l/sc1l [N] for group g_last).
-template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8>
+template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8, int NBB>
 __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
@@ -637,15 +708,19 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
   static_assert(WM * WN == 4 && (KB == 64 || KB == 128 || (Q8 && KB == 256)) && (!Q8 || KB >= 128),
                 "four waves; A rows of 64 or 128 B (256 B with FP8 weights, whose rows are half)");
-  static_assert(NBUF >= 2 && NBUF <= 6, "stage ring of 2..6 buffers");
+  static_assert(NBUF >= 2 && NBUF <= 4 && NBB >= NBUF && NBB <= 6,
+                "A ring of 2..4 buffers, B ring of NBUF..6");
   static_assert(G::CA >= 1 && G::CB >= 1 && BM % (4 * G::RPA) == 0 && BNT % (4 * G::RPB) == 0 &&
                 FM >= 1 && FN >= 1 && (!GLU || FN % 2 == 0), "tile shape");
   // GLU: a copy instruction's rows never straddle the W1 / W3 halves
   static_assert(!GLU || BN % G::RPB == 0, "gate/up halves split on copy rows");
-  constexpr int SZ = G::SZ;
-  __shared__ u32x4 L0[SZ], L1[SZ], L2[NBUF > 2 ? SZ : 1], L3[NBUF > 3 ? SZ : 1],
-      L4[NBUF > 4 ? SZ : 1], L5[NBUF > 5 ? SZ : 1];
-  const Ring rb{L0, L1, L2, L3, L4, L5};
+  // Buffers the rings do not use are never referenced, so they take no LDS.
+  constexpr int SZA = BM * G::CPA, SZB = BNT * G::CPB;
+  __shared__ u32x4 LA0[SZA], LA1[SZA], LA2[SZA], LA3[SZA];
+  __shared__ u32x4 LB0[SZB], LB1[SZB], LB2[SZB], LB3[SZB], LB4[SZB], LB5[SZB];
+  const Ring ra{LA0, LA1, NBUF > 2 ? LA2 : LA0, NBUF > 3 ? LA3 : LA0, LA0, LA0};
+  const Ring rb{LB0, LB1, NBB > 2 ? LB2 : LB0, NBB > 3 ? LB3 : LB0, NBB > 4 ? LB4 : LB0,
+                NBB > 5 ? LB5 : LB0};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -710,19 +785,27 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
+  // 32-row blocks holding real rows; tiles 8 blocks tall run an even
+  // count (one block past the rows at most: computed, never stored), which
+  // halves the loop instantiations
+  int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
+  if constexpr (FM > 4) nv = min(FM, (nv + 1) & ~1);
+  static_assert(FM <= 8, "at most eight 32-row blocks per wave");
 #define MOE_DMA_LOOP(NV_)                                                                     \
-  main_loop_dma<NV_, BM, BN, BNT, FM, FN, GLU, KB, NBUF, Q8, TB>(acc, rb, pa, pb, nk, fr, wave)
+  main_loop_dma<NV_, BM, BN, BNT, FM, FN, GLU, KB, NBUF, NBB, Q8, TB>(acc, ra, rb, pa, pb, nk, fr, \
+                                                                     wave)
   if (nv >= FM) {
     MOE_DMA_LOOP(FM);
   } else if (nv == 0) {
     MOE_DMA_LOOP(0);
-  } else {
+  } else if constexpr (FM <= 4) {
     if constexpr (FM > 1) { if (nv == 1) MOE_DMA_LOOP(1); }
     if constexpr (FM > 2) { if (nv == 2) MOE_DMA_LOOP(2); }
     if constexpr (FM > 3) { if (nv == 3) MOE_DMA_LOOP(3); }
+  } else {
+    if (nv == 2) MOE_DMA_LOOP(2);
     if constexpr (FM > 4) { if (nv == 4) MOE_DMA_LOOP(4); }
-    if constexpr (FM > 5) { if (nv == 5) MOE_DMA_LOOP(5); }
+    if constexpr (FM > 6) { if (nv == 6) MOE_DMA_LOOP(6); }
   }
 #undef MOE_DMA_LOOP
   const float* s0p = nullptr;
@@ -794,16 +877,25 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
 #ifndef MOE_CFG0_BM
 #define MOE_CFG0_BM 256
 #endif
+// Depth of the weight-row ring of the 256-row tiles (two activation buffers).
+#ifndef MOE_CFG0_NBB
+#define MOE_CFG0_NBB 2
+#endif
 struct GemmPlan {
   int BM;
   int cfg;   // 0 = large, 1 = medium, 2 = small (decode), 3 = fp32
 };
 
-static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
+// Medium shapes (a few hundred rows per expert or fewer, HBM-bound) take
+// 256-row tiles with the four waves side by side (1 x 4), so an expert's
+// weight slice is streamed once even when it holds more than 128 rows, and
+// 32-row blocks past the expert's rows cost no MFMA time on any wave; FP8
+// weights keep 128-row 2 x 2 tiles.
+static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F, bool q8 = false) {
   if (dtype == MOE_F32) return {64, 3};
   const double avg = (double)max_rows / (double)(G > 0 ? G : 1);
   if (avg >= 192.0) return {MOE_CFG0_BM, 0};
-  if (avg >= 48.0 || F % 256 != 0 || d % 256 != 0) return {128, 1};
+  if (avg >= 48.0 || F % 256 != 0 || d % 256 != 0) return {q8 ? 128 : 256, 1};
   return {32, 2};
 }
 
@@ -828,6 +920,14 @@ static int down_split(const GemmPlan& p, int64_t max_rows, int G, int d, int F) 
   return eff(2 * est) > eff(est) + 0.05 ? 2 : 1;
 }
 
+// One workspace size serves bf16 and FP8 weights: work lists are sized for
+// the smaller tile height of the two plans.
+static int ws_tile_rows(int dtype, int64_t max_rows, int G, int d, int F) {
+  const int a = plan_for(dtype, max_rows, G, d, F, false).BM;
+  const int b = plan_for(dtype, max_rows, G, d, F, true).BM;
+  return a < b ? a : b;
+}
+
 int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype) {
   if (max_rows <= 0 || G <= 0) return 1;
   return down_split(plan_for(dtype, max_rows, G, d, F), max_rows, G, d, F);
@@ -836,9 +936,10 @@ int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype) {
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
+  const int bm = ws_tile_rows(dtype, max_rows, G, d, F);
   const int ks = down_split(p, max_rows, G, d, F);
-  const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d), ks);
+  const int64_t wu = max_work(max_rows, G, bm, F, up_bn(p.cfg));
+  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), ks);
   size_t b = align256((size_t)max_rows * F * es);                       // H
   b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
   b += align256(2 * sizeof(int32_t));                                  // entry counts
@@ -892,13 +993,14 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false>
+template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
+          int NBB = NBUF>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
                      a.B0, a.B1, a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
                      a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
@@ -980,11 +1082,13 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
                               const WeightScales* qs) {
   if (partial2) *partial2 = nullptr;
   if (max_rows <= 0 || G <= 0) return hipSuccess;
-  const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
+  const GemmPlan p = plan_for(dtype, max_rows, G, d, F, qs != nullptr);
   const int ks = down_split(p, max_rows, G, d, F);
   const int es = dtype == MOE_BF16 ? 2 : 4;
-  const int64_t wu = max_work(max_rows, G, p.BM, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, p.BM, d, down_bn(p.cfg, d), ks);
+  // work-list regions laid out as in ffn_ws_bytes
+  const int bm = ws_tile_rows(dtype, max_rows, G, d, F);
+  const int64_t wu = max_work(max_rows, G, bm, F, up_bn(p.cfg));
+  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), ks);
   char* q = (char*)ws;
   void* H = q;               q += align256((size_t)max_rows * F * es);
   int2* work_up = (int2*)q;  q += align256((size_t)wu * sizeof(int2));
@@ -1029,20 +1133,20 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   } else if (dtype == MOE_BF16) {
     using T = uint16_t;
     switch (p.cfg) {
-      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true>(up, s); break;
-      case 1: run_gemm_dma<128, 128, 2, 2, true, 128, 3>(up, s); break;
+      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB>(up, s); break;
+      case 1: run_gemm_dma<256, 128, 1, 4, true, 128, 2, false, 3>(up, s); break;
       default: run_gemm<T, 32, 256, 1, 4, true>(up, s); break;
     }
     timing_mark("ffn_up", s);
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false>(dn, s);
-        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false>(dn, s);
+        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
+        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
         break;
       case 1:
-        if (b256) run_gemm_dma<128, 256, 2, 2, false, 128, 3>(dn, s);
-        else run_gemm_dma<128, 128, 2, 2, false, 128, 3>(dn, s);
+        if (b256) run_gemm_dma<256, 256, 1, 4, false, 128, 2, false, 3>(dn, s);
+        else run_gemm_dma<256, 128, 1, 4, false, 128, 2, false, 3>(dn, s);
         break;
       default: run_gemm<T, 32, 256, 1, 4, false>(dn, s); break;
     }

@@ -68,7 +68,11 @@ def test_fullsize_workload(name):
     assert aux["slot_row"].cpu().numpy().tolist() == d["slot_row"].tolist()
     assert aux["sorted_slot"].cpu().numpy()[:R].tolist() == d["sorted_slot"].tolist()
 
-    # --- G1/G2: sampled experts' rows (up to 8 rows from each of 3 touched experts)
+    # --- G1/G2: every kept row is finite and nonzero (a row whose tile
+    # skipped its main loop would be exactly zero), then sampled experts'
+    # rows (up to 8 rows from each of 3 touched experts) against the oracle
+    yr = aux["Yrows"][:R]
+    assert bool(torch.isfinite(yr).all()) and bool((yr.abs().amax(dim=1) > 0).all())
     touched = np.flatnonzero(d["kept"] > 0)
     for e in rng.choice(touched, size=min(3, touched.size), replace=False):
         a, b = int(d["offsets"][e]), int(d["offsets"][e + 1])
@@ -137,6 +141,8 @@ def test_fullsize_expert_choice(name):
     assert aux["slot_row"].cpu().reshape(-1).tolist() == d["slot_row"].tolist()
     assert aux["sorted_slot"].cpu()[:R].tolist() == d["sorted_slot"].tolist()
 
+    yr = aux["Yrows"][:R]
+    assert bool(torch.isfinite(yr).all()) and bool((yr.abs().amax(dim=1) > 0).all())
     for e in rng.choice(w.E, size=min(3, w.E), replace=False):
         a, b = int(d["offsets"][e]), int(d["offsets"][e + 1])
         rsel = np.sort(rng.choice(np.arange(a, b), size=min(8, b - a), replace=False))

@@ -371,6 +371,8 @@ FFN_SHAPES = {
     "decode": (512, 256, [2, 0, 1, 3, 2, 2, 0, 1, 4, 2, 1, 2, 3, 1, 2, 2], 0),
     # large tiles with a long reduction: the down projection is split along K
     "large_ksplit": (768, 4096, [300, 260, 280, 290], 0),
+    # medium tiles 256 rows tall: every count of 32-row blocks from 1 to 8
+    "tall_tiles": (512, 512, [1, 33, 65, 97, 129, 161, 193, 225, 256, 250, 70], 3),
 }
 
 
