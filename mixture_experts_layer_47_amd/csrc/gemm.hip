@@ -438,9 +438,9 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
 // bf16 activations, bf16 or FP8 (E4M3) weights; tiles with BM, BNT multiples
 // of 32.  A stage covers 64 K-elements (KB = 128) or 32 (KB = 64): KB bytes of
 // every A row and, for bf16 weights, of every B row (KB / 2 bytes for FP8).
-// The A parts of NBA stages and the B parts of NBB >= NBA stages live in two
-// rings of distinct LDS arrays, so weight rows (streamed from HBM) can be
-// fetched further ahead than the activation rows (mostly L2 / MALL hits).  global_load_lds moves
+// The A parts of NBA stages and the B parts of NBB stages live in two rings
+// of distinct LDS arrays, so the operand with the longer memory latency can
+// be fetched further ahead than the other.  global_load_lds moves
 // 16 B per lane from global memory straight into LDS (lane L of one wave
 // instruction fills bytes [16 L, 16 L + 16) of a 1 KB block = 1024 / rowbytes
 // rows), so stages never pass through registers.  LDS row r keeps chunk c
@@ -620,16 +620,23 @@ __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra,
                                           u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave) {
   using G = StageGeo<BM, BNT, KB, Q8>;
   constexpr int BK = KB / 2;                 // K-elements per stage
-  // The last copy stage s needs is its A part when NBB > NBA (its B part was
-  // issued earlier); after it come this iteration's B copies and NBA - 2
-  // more iterations of copies.
-  constexpr int WAITN = (NBB > NBA ? G::CB : 0) + (NBA - 2) * (G::CA + G::CB);
+  // Each iteration copies the part of the shallower ring first (A on
+  // equal depths).  The last copy stage s needs is that part of stage s,
+  // followed by the other part's copies of the same iteration (unless the
+  // depths are equal: then it is the B part, the iteration's last copy) and
+  // by min(NBA, NBB) - 2 more iterations of copies.
+  constexpr int NBS = NBA < NBB ? NBA : NBB;
+  constexpr int WAITN = (NBA < NBB ? G::CB : NBA > NBB ? G::CA : 0) + (NBS - 2) * (G::CA + G::CB);
   wait_vm_lgkm<WAITN>();
   __builtin_amdgcn_s_barrier();
   const int ta = s + NBA - 1, tb = s + NBB - 1;
+  if constexpr (NBA > NBB)
+    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
+                               wave);
   dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa, (ta < nk ? ta : nk - 1) * BK, wave);
-  dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
-                             wave);
+  if constexpr (NBA <= NBB)
+    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
+                               wave);
   if constexpr (NV > 0)
     stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(H % NBA, ra), ring(H % NBB, rb),
                                                     f0, f1, fr, true);
@@ -659,19 +666,25 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
                                               const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
                                               const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
                                               int nk, const FragAddr& fr, int wave) {
-  static_assert(NBA >= 2 && NBB >= NBA, "A ring of >= 2 buffers, B ring at least as deep");
+  static_assert(NBA >= 2 && NBB >= 2, "rings of at least two buffers");
   constexpr int NF = FM + FN;
   constexpr int BK = KB / 2;
   constexpr int P = NBA / gcd_i(NBA, NBB) * NBB;       // ring period
-  // Prologue: virtual iterations i = -(NBB - 1) .. -1 issue what iteration i
-  // would (A part i + NBA - 1, B part i + NBB - 1); a negative A stage is a
-  // stand-in copy of stage 0 into the buffer it would use.
+  // Prologue: virtual iterations i = -(max(NBA, NBB) - 1) .. -1 issue what
+  // iteration i would (A part i + NBA - 1, B part i + NBB - 1); a negative
+  // stage is a stand-in copy of stage 0 into the buffer it would use.
+  constexpr int NBM = NBA > NBB ? NBA : NBB;
 #pragma unroll
-  for (int i = -(NBB - 1); i < 0; ++i) {
+  for (int i = -(NBM - 1); i < 0; ++i) {
     const int sa = i + NBA - 1, sb = i + NBB - 1;
+    if constexpr (NBA > NBB)
+      dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
+                                 (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
     dma_a<BM, BNT, KB, Q8>(ring(((sa % NBA) + NBA) % NBA, ra), pa,
                            (sa < 0 ? 0 : (sa < nk ? sa : nk - 1)) * BK, wave);
-    dma_b<BM, BNT, KB, Q8, TB>(ring(sb % NBB, rb), pb, (sb < nk ? sb : nk - 1) * BK, wave);
+    if constexpr (NBA <= NBB)
+      dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
+                                 (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
   }
   u32x4 f0[NF], f1[NF];
 #pragma unroll
@@ -708,8 +721,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   constexpr int FM = WROWS / 32, FN = WCOLS / 32;
   static_assert(WM * WN == 4 && (KB == 64 || KB == 128 || (Q8 && KB == 256)) && (!Q8 || KB >= 128),
                 "four waves; A rows of 64 or 128 B (256 B with FP8 weights, whose rows are half)");
-  static_assert(NBUF >= 2 && NBUF <= 4 && NBB >= NBUF && NBB <= 6,
-                "A ring of 2..4 buffers, B ring of NBUF..6");
+  static_assert(NBUF >= 2 && NBUF <= 4 && NBB >= 2 && NBB <= 6,
+                "A ring of 2..4 buffers, B ring of 2..6");
   static_assert(G::CA >= 1 && G::CB >= 1 && BM % (4 * G::RPA) == 0 && BNT % (4 * G::RPB) == 0 &&
                 FM >= 1 && FN >= 1 && (!GLU || FN % 2 == 0), "tile shape");
   // GLU: a copy instruction's rows never straddle the W1 / W3 halves
