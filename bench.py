@@ -201,10 +201,21 @@ def main():
     value = w.T * args.steps / elapsed
 
     phases = {}
+    steps_ms, cur = [], None
     for name, ms in marks:
-        if ms is not None:
+        if ms is None:             # a call's first mark: the previous call is complete
+            if cur is not None:
+                steps_ms.append(cur)
+            cur = 0.0
+        else:
             phases.setdefault(name, []).append(ms)
+            cur = (cur or 0.0) + ms
+    if cur is not None:
+        steps_ms.append(cur)
     phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
+    # device time of each forward (first to last phase event), per step
+    step_stats = ({"median": float(np.median(steps_ms)), "min": float(np.min(steps_ms)),
+                   "max": float(np.max(steps_ms)), "n": len(steps_ms)} if steps_ms else None)
     up_ms = phase_ms.get("ffn_up", float("nan"))
     flops, bytes_, touched, rows = up_kernel_work(w, kept, n_kept)
     peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -253,7 +264,7 @@ def main():
                   "mfma_frac": layer_flops / (ms_step * 1e-3) / (peak_flops * 1e12),
                   "hbm_frac": layer_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
                   "kept_rows": n_kept, "balance_stat": balance, "router_health": health,
-                  "phases_ms": phase_ms},
+                  "phases_ms": phase_ms, "device_step_ms": step_stats},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_target_s)

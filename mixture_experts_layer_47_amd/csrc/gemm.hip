@@ -1122,10 +1122,10 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   timing_mark("tile_map", s);
   if (qs) {
     // FP8 weights: 256-row tiles keep 64-K stages (32 KB A + 16 KB B rows,
-    // three buffers); the others use 128-K stages (256-B A rows, 128-B weight
-    // rows: whole cache lines per copy) in two buffers of 64 / 72 KB.
+    // two buffers each); the others use 128-K stages (256-B A rows, 128-B
+    // weight rows: whole cache lines per copy) in two buffers of 64 / 72 KB.
     switch (p.cfg) {
-      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 3, true>(up, s); break;
+      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, true>(up, s); break;
       case 1: run_gemm_dma<128, 128, 2, 2, true, 256, 2, true>(up, s); break;
       default: run_gemm_dma<32, 256, 1, 4, true, 256, 2, true>(up, s); break;
     }
@@ -1133,8 +1133,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 3, true>(dn, s);
-        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 3, true>(dn, s);
+        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 2, true>(dn, s);
+        else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, true>(dn, s);
         break;
       case 1:
         if (b256) run_gemm_dma<128, 256, 2, 2, false, 256, 2, true>(dn, s);
