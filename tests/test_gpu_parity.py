@@ -486,3 +486,41 @@ def test_balance_entry_point_page_example():
     ps = torch.tensor([4.0, 2.0, 2.0, 2.0], device=DEV)
     out = moe.balance(counts, ps, 10, 1)
     assert abs(out.item() - 1.36) < 1e-12
+
+
+# ------------------------------------------------ composition of entry points --
+def test_entry_points_compose_to_forward():
+    """moe_route -> moe_dispatch (with the gather) -> moe_grouped_ffn ->
+    moe_combine gives moe_forward's output bit for bit (same kernels, same
+    summation order), for top-k routing with a capacity limit."""
+    w = SMALL["mixtral_prefill"].with_(cf=1.0)
+    _announce("entry points compose (top-k)")
+    inp = make_inputs(w, DEV)
+    Y_fused = moe.forward(moe.layer_from_inputs(inp), inp["X"])
+    r = moe.route(inp["X"], inp["Wg"], w.k, w.score, w.renorm)
+    C = moe.capacity(w.cf, w.T, w.k, w.E)
+    dsp = moe.dispatch(r["ids"], w.E, C, X=inp["X"])
+    rows = moe.grouped_ffn(dsp["X_sorted"], dsp["offsets"], inp["W1"], inp["W3"], inp["W2"],
+                           w.T * w.k)
+    Y = moe.combine(rows, dsp["slot_row"], r["w"], inp["X"].dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_fused)
+
+
+def test_expert_choice_entry_points_compose_to_forward():
+    """moe_route_expert_choice -> moe_grouped_ffn (row -> token through
+    sorted_slot / E) -> moe_combine with k = E gives moe_forward's output bit
+    for bit."""
+    w = SMALL["mixtral_prefill_ec"]
+    _announce("entry points compose (expert choice)")
+    inp = make_inputs(w, DEV)
+    layer = moe.layer_from_inputs(inp)
+    Y_fused = moe.forward(layer, inp["X"])
+    C = layer.expert_capacity(w.T)
+    r = moe.route_expert_choice(inp["X"], inp["Wg"], C, w.score)
+    row_token = (r["sorted_slot"] // w.E).to(torch.int32)
+    rows = moe.grouped_ffn(inp["X"], r["offsets"], inp["W1"], inp["W3"], inp["W2"], w.E * C,
+                           row_token=row_token)
+    Y = moe.combine(rows, r["slot_row"].reshape(-1), r["gates"], inp["X"].dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_fused)
