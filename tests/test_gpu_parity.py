@@ -199,6 +199,9 @@ EDGE = {
                            n_shared=1, seed=19),
     "E256_k16": Workload("E256_k16", T=20, d=256, E=256, k=16, F=128, score="sigmoid",
                          bias_std=0.01, seed=20),
+    # many tokens through a narrow layer: 131072 slots (128 dispatch chunks),
+    # 65536 combine blocks, thousands of row tiles
+    "T65536": Workload("T65536", T=65536, d=128, E=8, k=2, F=128, cf=1.1, seed=24),
 }
 
 
