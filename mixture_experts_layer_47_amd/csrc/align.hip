@@ -16,7 +16,10 @@
 
 namespace moe {
 
-constexpr int kAlignChunk = 1024;   // slots per wave (16 groups of 64)
+// Slots per wave (chunk): 256 (4 groups of 64) for up to 64 experts, else
+// 1024.  Short chunks give more waves for few experts; with many experts the
+// per-expert scan over chunk histograms would grow instead.
+__host__ __device__ constexpr int align_chunk_for(int E) { return E <= 64 ? 256 : 1024; }
 
 // Mask of active lanes whose expert id equals this lane's.
 __device__ __forceinline__ uint64_t match_id(int e, bool valid, int nbits) {
@@ -34,6 +37,7 @@ __device__ __forceinline__ int nbits_for(int E) {
 }
 
 // Pass 1: chunk histograms hist[c][e].
+template <int CHUNK>
 __global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__ ids,
                                                      int64_t Tk, int E, int nchunks,
                                                      int32_t* __restrict__ hist) {
@@ -46,11 +50,11 @@ __global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   const int nb = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int NG = kAlignChunk / 64;
+  constexpr int NG = CHUNK / 64;
   int ev[NG];                                         // all loads in flight at once
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const int64_t s = (int64_t)c * CHUNK + g * 64 + lane;
     ev[g] = s < Tk ? ids[s] : -1;
   }
 #pragma unroll
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(256) void k_align_scan(int32_t* __restrict__ hist, 
 }
 
 // Pass 3: stable ranks, drop mask and the permutation.
+template <int CHUNK>
 __global__ __launch_bounds__(256) void k_align_scatter(
     const int32_t* __restrict__ ids, int64_t Tk, int k, int E, int nchunks,
     int64_t cap, const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
@@ -115,16 +120,16 @@ __global__ __launch_bounds__(256) void k_align_scatter(
   for (int e = lane; e < E; e += 64) cnt[e] = base[(size_t)c * E + e];
   const int nb = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int NG = kAlignChunk / 64;
+  constexpr int NG = CHUNK / 64;
   int ev[NG];                                         // all loads in flight at once
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const int64_t s = (int64_t)c * CHUNK + g * 64 + lane;
     ev[g] = s < Tk ? ids[s] : -1;
   }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const int64_t s = (int64_t)c * CHUNK + g * 64 + lane;
     const bool v = ev[g] >= 0;
     const int e = v ? ev[g] : 0;
     const uint64_t eq = match_id(e, v, nb);
@@ -214,6 +219,7 @@ __global__ __launch_bounds__(256) void k_rr_scan(int32_t* __restrict__ hist2, in
 // offset change; proposals are ranked in slot order (wave multisplit on
 // the proposed expert, as in k_align_scatter) and placed after the
 // expert's first-pass rows when the rank is below the accepted count.
+template <int CHUNK>
 __global__ __launch_bounds__(256) void k_rr_place(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ props, int64_t Tk, int k,
     int E, int nchunks, const int32_t* __restrict__ base2,
@@ -236,9 +242,9 @@ __global__ __launch_bounds__(256) void k_rr_place(
   for (int e = lane; e < E; e += 64) cnt[e] = base2[(size_t)c * E + e];
   const int nbits = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int NG = kAlignChunk / 64;
+  constexpr int NG = CHUNK / 64;
   for (int g = 0; g < NG; ++g) {
-    const int64_t s = (int64_t)c * kAlignChunk + g * 64 + lane;
+    const int64_t s = (int64_t)c * CHUNK + g * 64 + lane;
     const bool in = s < Tk;
     const int p = in ? props[s] : -1;
     const bool v = p >= 0;
@@ -295,11 +301,11 @@ __global__ void k_zero_words(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // --------------------------------------------------------------- launchers
-int align_nchunks(int64_t Tk) { return (int)MOE_CEIL_DIV(Tk, kAlignChunk); }
+int align_nchunks(int64_t Tk, int E) { return (int)MOE_CEIL_DIV(Tk, align_chunk_for(E)); }
 
 size_t dispatch_ws_bytes(int64_t T, int k, int E) {
   const int64_t Tk = T * (int64_t)k;
-  return align256((size_t)(align_nchunks(Tk) > 0 ? align_nchunks(Tk) : 1) * E * sizeof(int32_t));
+  return align256((size_t)(align_nchunks(Tk, E) > 0 ? align_nchunks(Tk, E) : 1) * E * sizeof(int32_t));
 }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
@@ -314,15 +320,17 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
                            int32_t* sorted_slot, int32_t* slot_row, int32_t* n_kept,
                            int32_t* row_token, void* ws, hipStream_t s) {
   const int64_t Tk = T * (int64_t)k;
-  const int nch = align_nchunks(Tk);
+  const int nch = align_nchunks(Tk, E);
   int32_t* hist = (int32_t*)ws;
   const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
   if (nch > 0)
-    hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(256), 0, s, ids, Tk, E, nch, hist);
+    hipLaunchKernelGGL(E <= 64 ? k_align_count<align_chunk_for(64)> : k_align_count<align_chunk_for(65)>,
+                       dim3(nblk), dim3(256), 0, s, ids, Tk, E, nch, hist);
   hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(256), 0, s, hist, E, nch, cap, tail_rows,
                      counts, offsets, n_kept);
   if (nch > 0)
-    hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(256), 0, s, ids, Tk, k, E, nch, cap,
+    hipLaunchKernelGGL(E <= 64 ? k_align_scatter<align_chunk_for(64)> : k_align_scatter<align_chunk_for(65)>,
+                       dim3(nblk), dim3(256), 0, s, ids, Tk, k, E, nch, cap,
                        hist, offsets, sorted_slot, slot_row, row_token);
   if (row_token && tail_rows > 0)
     hipLaunchKernelGGL(k_tail_tokens, dim3((unsigned)MOE_CEIL_DIV(tail_rows, 256)), dim3(256),
@@ -332,7 +340,7 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
 
 size_t reroute_ws_bytes(int64_t T, int k, int E) {
   const int64_t Tk = T * (int64_t)k;
-  const int nch = align_nchunks(Tk) > 0 ? align_nchunks(Tk) : 1;
+  const int nch = align_nchunks(Tk, E) > 0 ? align_nchunks(Tk, E) : 1;
   return align256((size_t)nch * E * sizeof(int32_t)) + align256((size_t)Tk * sizeof(int32_t) + 4) +
          align256((size_t)3 * E * sizeof(int32_t));
 }
@@ -343,7 +351,7 @@ hipError_t launch_reroute(const int32_t* ids, const int32_t* backup, int nb, int
                           int32_t* n_kept, int32_t* row_token, void* ws, hipStream_t s) {
   const int64_t Tk = T * (int64_t)k;
   if (Tk <= 0 || cap <= 0 || nb <= 0) return hipSuccess;
-  const int nch = align_nchunks(Tk);
+  const int nch = align_nchunks(Tk, E);
   char* p = (char*)ws;
   int32_t* hist2 = (int32_t*)p;  p += align256((size_t)nch * E * sizeof(int32_t));
   int32_t* props = (int32_t*)p;  p += align256((size_t)Tk * sizeof(int32_t) + 4);
@@ -351,10 +359,12 @@ hipError_t launch_reroute(const int32_t* ids, const int32_t* backup, int nb, int
   hipLaunchKernelGGL(k_rr_props, dim3((unsigned)MOE_CEIL_DIV(T, 256)), dim3(256), 0, s, slot_row,
                      backup, T, k, nb, props);
   const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
-  hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(256), 0, s, props, Tk, E, nch, hist2);
+  hipLaunchKernelGGL(E <= 64 ? k_align_count<align_chunk_for(64)> : k_align_count<align_chunk_for(65)>,
+                     dim3(nblk), dim3(256), 0, s, props, Tk, E, nch, hist2);
   hipLaunchKernelGGL(k_rr_scan, dim3(1), dim3(256), 0, s, hist2, E, nch, cap, tail_rows, counts,
                      offsets, n_kept, meta);
-  hipLaunchKernelGGL(k_rr_place, dim3(nblk), dim3(256), 0, s, ids, props, Tk, k, E, nch, hist2,
+  hipLaunchKernelGGL(E <= 64 ? k_rr_place<align_chunk_for(64)> : k_rr_place<align_chunk_for(65)>,
+                     dim3(nblk), dim3(256), 0, s, ids, props, Tk, k, E, nch, hist2,
                      offsets, meta, sorted_slot, slot_row, row_token);
   if (row_token && tail_rows > 0)
     hipLaunchKernelGGL(k_tail_tokens, dim3((unsigned)MOE_CEIL_DIV(tail_rows, 256)), dim3(256),
