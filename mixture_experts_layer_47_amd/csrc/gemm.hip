@@ -834,11 +834,21 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 // Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
 // ceil(rows_g / BM) M-tiles times NN N-tiles times ksplit K-splits, ordered
 // by group, then K-split, then runs of NG neighbouring N-tiles, then M-tile,
-// then N-tile inside the run.
+// then N-tile inside the run.  One block per list: the lists of both
+// projections are built by one launch.
+struct WorkListArgs {
+  int BM, NN, NG, ksplit;
+  int2* work;
+  int32_t* nwork;
+};
+
 __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ offsets, int G,
-                                                    int BM, int max_rows, int NN, int NG,
-                                                    int ksplit, int2* __restrict__ work,
-                                                    int32_t* __restrict__ nwork) {
+                                                    int max_rows, WorkListArgs l0,
+                                                    WorkListArgs l1) {
+  const WorkListArgs& l = blockIdx.x == 0 ? l0 : l1;
+  const int BM = l.BM, NN = l.NN, NG = l.NG, ksplit = l.ksplit;
+  int2* __restrict__ work = l.work;
+  int32_t* __restrict__ nwork = l.nwork;
   __shared__ int32_t sc[1024];
   __shared__ int32_t mts[1024];
   const int g = threadIdx.x;
@@ -988,11 +998,20 @@ struct GemmArgs {
   const float *sc0, *sc1, *sc0l, *sc1l;   // FP8 weights: per-output-channel scales
 };
 
-static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s) {
+static WorkListArgs work_list_args(const GemmArgs& a, int BM, int BN, bool glu) {
   const int NN = a.N / BN;
   const int NG = glu ? 8 : 4;
-  hipLaunchKernelGGL(k_work_list, dim3(1), dim3(1024), 0, s, a.offsets, a.G, BM, a.max_rows, NN,
-                     NG < NN ? NG : NN, a.ksplit, a.work, a.nwork);
+  return WorkListArgs{BM, NN, NG < NN ? NG : NN, a.ksplit, a.work, a.nwork};
+}
+
+// Builds the work list of a (and of b when given: same groups and offsets).
+static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s,
+                          const GemmArgs* b = nullptr, int BMb = 0, int BNb = 0,
+                          bool glub = false) {
+  const WorkListArgs l0 = work_list_args(a, BM, BN, glu);
+  const WorkListArgs l1 = b ? work_list_args(*b, BMb, BNb, glub) : l0;
+  hipLaunchKernelGGL(k_work_list, dim3(b ? 2 : 1), dim3(1024), 0, s, a.offsets, a.G, a.max_rows,
+                     l0, l1);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
@@ -1117,8 +1136,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     up.sc0 = qs->s1; up.sc1 = qs->s3; up.sc0l = qs->s1l; up.sc1l = qs->s3l;
     dn.sc0 = qs->s2; dn.sc0l = qs->s2l;
   }
-  run_work_list(up, p.BM, up_bn(p.cfg), true, s);
-  run_work_list(dn, p.BM, down_bn(p.cfg, d), false, s);
+  run_work_list(up, p.BM, up_bn(p.cfg), true, s, &dn, p.BM, down_bn(p.cfg, d), false);
   timing_mark("tile_map", s);
   if (qs) {
     // FP8 weights: 256-row tiles keep 64-K stages (32 KB A + 16 KB B rows,
