@@ -25,6 +25,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> two bf16 (lo in bits 15:0) with the gfx950 conversion
+// instruction: round to nearest even, the same bits as f32_to_bf16_bits for
+// finite inputs.
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(moe_f32x2{lo, hi}, moe_bf16x2));
+}
+
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> {
   static constexpr int kBytes = 4;

@@ -55,7 +55,11 @@ __device__ __forceinline__ void mma_32x32(f32x16& acc, const u32x4& a, const u32
   }
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
+// silu(x) = x sigmoid(x) in fp32: hardware exp and reciprocal (about 1 ulp
+// each), far below the one rounding of h to bf16 that follows.
+__device__ __forceinline__ float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
 
 
 constexpr int kThreads = 256;   // four waves per block
@@ -251,10 +255,7 @@ __device__ __forceinline__ void store4_h(T* p, float a, float b, float c, float 
 template <>
 __device__ __forceinline__ void store4_h<uint16_t>(uint16_t* p, float a, float b, float c,
                                                    float d) {
-  uint2 v;
-  v.x = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-  v.y = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
-  *(uint2*)p = v;
+  *(uint2*)p = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
 }
 template <>
 __device__ __forceinline__ void store4_h<float>(float* p, float a, float b, float c, float d) {
@@ -325,6 +326,107 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], void* __
                                                          y[4 * q + 2] * c.z, y[4 * q + 3] * c.w);
           }
       }
+    }
+  }
+}
+
+// LDS buffers of one ring (or of the staged epilogue), by position.
+struct Ring {
+  u32x4 *b0, *b1, *b2, *b3, *b4, *b5;
+};
+__device__ __forceinline__ u32x4* ring(int h, const Ring& r) {
+  return h == 0 ? r.b0 : h == 1 ? r.b1 : h == 2 ? r.b2 : h == 3 ? r.b3 : h == 4 ? r.b4 : r.b5;
+}
+
+// Staged tile epilogue (LDS-direct kernel).  The accumulator layout makes a
+// direct store touch 32 rows per instruction, 8 or 16 bytes each; here the
+// outputs pass through LDS so that consecutive threads store consecutive
+// 16-B pieces of one output row and every store instruction covers whole
+// 128-B lines.  Pass i takes the 32-row block i of every wave: each wave
+// writes those rows' finished outputs (same arithmetic as store_tile) into
+// the LDS region of its wave row, the block synchronises, and the 256
+// threads store the rows (rows past the tile's end are skipped).  LDS row r
+// keeps its 16-B chunk c at slot c ^ (r & 7).  With 2 WM regions the passes
+// alternate between two sets and need one barrier each; with WM regions a
+// second barrier ends every pass.  The regions are ring buffers: a first
+// barrier makes sure no wave still reads the last stage.
+template <int BM, int BN, int BNT, int WM, int WN, bool GLU>
+struct StagedEpi {
+  static constexpr int ES = GLU ? 2 : 4;                  // bf16 h or fp32 y
+  static constexpr int OC = GLU ? BN : BNT;               // output columns per tile
+  static constexpr int RB = OC * ES;                      // bytes per output row
+  static constexpr int NC = RB / 16;                      // 16-B chunks per row
+  static constexpr int PASS = 32 * RB;                    // bytes per region and pass
+};
+
+template <int BM, int BN, int BNT, int WM, int WN, int FM, int FN, bool GLU, bool SC, bool DB>
+__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
+                                                  void* __restrict__ out,
+                                                  float* __restrict__ out2, int ks, int max_rows,
+                                                  int N, int rbeg, int rows, int n0, int wm,
+                                                  int wn, int lane, int tid,
+                                                  const float* __restrict__ sc0,
+                                                  const float* __restrict__ sc1,
+                                                  const Ring& reg) {
+  using E = StagedEpi<BM, BN, BNT, WM, WN, GLU>;
+  constexpr int FNO = GLU ? FN / 2 : FN;                  // 32-column output blocks per wave
+  constexpr int WOC = E::OC / WN;                         // output columns per wave
+  constexpr int WROWS = BM / WM;
+  static_assert(E::NC >= 8 && E::NC % 8 == 0 && WOC == 32 * FNO, "staged epilogue shape");
+  const int r = lane & 31;
+  const int cq = 4 * (lane >> 5);
+  float4 sa[FNO][4], sb[FNO][4];
+#pragma unroll
+  for (int j = 0; j < FNO; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = n0 + wn * WOC + 32 * j + 8 * q + cq;
+      sa[j][q] = SC ? *(const float4*)(sc0 + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+      sb[j][q] = (SC && GLU) ? *(const float4*)(sc1 + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+  char* obase = GLU ? (char*)out
+                    : (char*)(ks == 0 ? (float*)out : out2 + (size_t)(ks - 1) * max_rows * N);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    char* R = (char*)ring((DB ? (i & 1) * WM : 0) + wm, reg);
+#pragma unroll
+    for (int j = 0; j < FNO; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int byte = (wn * WOC + 32 * j + 8 * q + cq) * E::ES;
+        char* p = R + r * E::RB + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+        const float4 a = sa[j][q], b = sb[j][q];
+        if constexpr (GLU) {
+          const f32x16& g = acc[i][j];
+          const f32x16& u = acc[i][j + FNO];
+          *(uint2*)p = make_uint2(bf16x2_bits(silu_f(g[4 * q] * a.x) * (u[4 * q] * b.x),
+                                              silu_f(g[4 * q + 1] * a.y) * (u[4 * q + 1] * b.y)),
+                                  bf16x2_bits(silu_f(g[4 * q + 2] * a.z) * (u[4 * q + 2] * b.z),
+                                              silu_f(g[4 * q + 3] * a.w) * (u[4 * q + 3] * b.w)));
+        } else {
+          const f32x16& y = acc[i][j];
+          *(float4*)p = make_float4(y[4 * q] * a.x, y[4 * q + 1] * a.y, y[4 * q + 2] * a.z,
+                                    y[4 * q + 3] * a.w);
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WM; ++w) {
+      const char* R2 = (const char*)ring((DB ? (i & 1) * WM : 0) + w, reg);
+#pragma unroll
+      for (int e0 = 0; e0 < 32 * E::NC; e0 += kThreads) {
+        const int e = e0 + tid;
+        const int rr = e / E::NC, cc = e % E::NC;
+        const int row = w * WROWS + 32 * i + rr;
+        if (row < rows) {
+          const u32x4 v = *(const u32x4*)(R2 + rr * E::RB + ((cc ^ (rr & 7)) << 4));
+          *(u32x4*)(obase + ((size_t)(rbeg + row) * N + n0) * E::ES + cc * 16) = v;
+        }
+      }
+    }
+    if constexpr (!DB) {
+      if (i + 1 < FM) __syncthreads();
     }
   }
 }
@@ -547,12 +649,6 @@ __device__ __forceinline__ void load_frags_dma(u32x4* f, const u32x4* pa, const 
   }
 }
 
-struct Ring {
-  u32x4 *b0, *b1, *b2, *b3, *b4, *b5;
-};
-__device__ __forceinline__ u32x4* ring(int h, const Ring& r) {
-  return h == 0 ? r.b0 : h == 1 ? r.b1 : h == 2 ? r.b2 : h == 3 ? r.b3 : h == 4 ? r.b4 : r.b5;
-}
 
 // Per-lane fragment addressing: A rows fa + 32 i, B rows fb + rr (both in
 // slots of their region), swizzled chunk per substep.
@@ -827,8 +923,21 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     s0p = (g == g_last) ? sc0l : sc0 + (size_t)g * N;
     s1p = GLU ? ((g == g_last) ? sc1l : sc1 + (size_t)g * N) : nullptr;
   }
-  store_tile<T, BN, BNT, WN, FM, FN, GLU, Q8>(acc, out, out2, ks, max_rows, N, rbeg, rows, arow0,
-                                              n0, wn, lane, s0p, s1p);
+  // The down projection's fp32 rows go through the staged epilogue (ring
+  // buffers that hold a whole pass); the gate/up tile's bf16 h is stored
+  // directly, which measured as fast.
+  using E = StagedEpi<BM, BN, BNT, WM, WN, GLU>;
+  constexpr bool FA = SZA * 16 >= E::PASS, FB = SZB * 16 >= E::PASS;
+  constexpr int NR = (FA ? 2 : 0) + (FB ? 2 : 0);
+  if constexpr (!GLU && NR >= WM) {
+    const Ring reg{FA ? LA0 : LB0, FA ? LA1 : LB1, FA && FB ? LB0 : LA0, FA && FB ? LB1 : LA1,
+                   LA0, LA0};
+    store_tile_staged<BM, BN, BNT, WM, WN, FM, FN, GLU, Q8, (NR >= 2 * WM)>(
+        acc, out, out2, ks, max_rows, N, rbeg, rows, n0, wm, wn, lane, tid, s0p, s1p, reg);
+  } else {
+    store_tile<T, BN, BNT, WN, FM, FN, GLU, Q8>(acc, out, out2, ks, max_rows, N, rbeg, rows,
+                                                arow0, n0, wn, lane, s0p, s1p);
+  }
 }
 
 // Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
