@@ -597,13 +597,14 @@ struct StageGeo {
 template <int BM, int BNT, int KB, bool Q8>
 __device__ __forceinline__ void dma_a(u32x4* buf,
                                       const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                      int koff, int wave) {
+                                      int koff, int wave, uint32_t alive) {
   using G = StageGeo<BM, BNT, KB, Q8>;
 #pragma unroll
   for (int i = 0; i < G::CA; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
-                                     (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA), 16,
-                                     0, 0);
+    if (alive & (1u << i))
+      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
+                                       (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA), 16,
+                                       0, 0);
 }
 template <int BM, int BNT, int KB, bool Q8, typename TB>
 __device__ __forceinline__ void dma_b(u32x4* buf,
@@ -713,7 +714,8 @@ __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra,
                                           const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
                                           const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
                                           int s, int nk, u32x4 (&f0)[FM + FN],
-                                          u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave) {
+                                          u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave,
+                                          uint32_t alive) {
   using G = StageGeo<BM, BNT, KB, Q8>;
   constexpr int BK = KB / 2;                 // K-elements per stage
   // Each iteration copies the part of the shallower ring first (A on
@@ -729,7 +731,8 @@ __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra,
   if constexpr (NBA > NBB)
     dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
                                wave);
-  dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa, (ta < nk ? ta : nk - 1) * BK, wave);
+  dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa, (ta < nk ? ta : nk - 1) * BK, wave,
+                         alive);
   if constexpr (NBA <= NBB)
     dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
                                wave);
@@ -746,11 +749,11 @@ __device__ __forceinline__ void ring_period(f32x16 (&acc)[FM][FN], const Ring& r
                                             const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
                                             int s0, int nk, int limit, u32x4 (&f0)[FM + FN],
                                             u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave,
-                                            std::integer_sequence<int, Hs...>) {
+                                            uint32_t alive, std::integer_sequence<int, Hs...>) {
   // limit: stages of this period to run (the whole period in the loop, the
   // remainder in the tail); uniform across the block
   ((Hs < limit ? ring_step<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB, Hs>(
-                     acc, ra, rb, pa, pb, s0 + Hs, nk, f0, f1, fr, wave)
+                     acc, ra, rb, pa, pb, s0 + Hs, nk, f0, f1, fr, wave, alive)
                : (void)0),
    ...);
 }
@@ -761,7 +764,8 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
                                               const Ring& rb,
                                               const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
                                               const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
-                                              int nk, const FragAddr& fr, int wave) {
+                                              int nk, const FragAddr& fr, int wave,
+                                              uint32_t alive) {
   static_assert(NBA >= 2 && NBB >= 2, "rings of at least two buffers");
   constexpr int NF = FM + FN;
   constexpr int BK = KB / 2;
@@ -777,7 +781,7 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
       dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
                                  (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
     dma_a<BM, BNT, KB, Q8>(ring(((sa % NBA) + NBA) % NBA, ra), pa,
-                           (sa < 0 ? 0 : (sa < nk ? sa : nk - 1)) * BK, wave);
+                           (sa < 0 ? 0 : (sa < nk ? sa : nk - 1)) * BK, wave, alive);
     if constexpr (NBA <= NBB)
       dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
                                  (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
@@ -788,10 +792,11 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
   const int nfull = nk - nk % P;
   for (int s0 = 0; s0 < nfull; s0 += P)
     ring_period<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB>(
-        acc, ra, rb, pa, pb, s0, nk, P, f0, f1, fr, wave, std::make_integer_sequence<int, P>{});
+        acc, ra, rb, pa, pb, s0, nk, P, f0, f1, fr, wave, alive,
+        std::make_integer_sequence<int, P>{});
   if (nfull < nk)
     ring_period<NV, BM, BN, BNT, FM, FN, GLU, KB, NBA, NBB, Q8, TB>(
-        acc, ra, rb, pa, pb, nfull, nk, nk - nfull, f0, f1, fr, wave,
+        acc, ra, rb, pa, pb, nfull, nk, nk - nfull, f0, f1, fr, wave, alive,
         std::make_integer_sequence<int, P>{});
   if constexpr (NV > 0) mma_substep<uint16_t, NV, FM, FN>(acc, f1);
   wait_vm_lgkm<0>();   // no copy may still be landing when the block ends
@@ -874,6 +879,18 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     if (row_token) src = row_token[src];
     pa[i] = A + (size_t)src * K + kbeg + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
   }
+  // A copies whose rows all lie past the tile's end are not issued (their
+  // LDS rows feed only outputs that are never stored).  The wait counts stay
+  // right as long as no A copy is among the copies a wait leaves in flight:
+  // two A buffers, issued before the B part of the same iteration.
+  static_assert(G::CA <= 32, "one mask bit per A copy");
+  uint32_t alive = (1u << G::CA) - 1;
+  if constexpr (NBUF == 2 && NBUF <= NBB) {
+#pragma unroll
+    for (int i = 0; i < G::CA; ++i)
+      if ((wave * G::CA + i) * G::RPA >= rows) alive &= ~(1u << i);
+  }
+  alive = __builtin_amdgcn_readfirstlane(alive);
   constexpr int EPC_B = 16 / sizeof(TB);             // B elements per 16-B chunk
   const TB* pb[G::CB];
 #pragma unroll
@@ -902,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   static_assert(FM <= 8, "at most eight 32-row blocks per wave");
 #define MOE_DMA_LOOP(NV_)                                                                     \
   main_loop_dma<NV_, BM, BN, BNT, FM, FN, GLU, KB, NBUF, NBB, Q8, TB>(acc, ra, rb, pa, pb, nk, fr, \
-                                                                     wave)
+                                                                     wave, alive)
   if (nv >= FM) {
     MOE_DMA_LOOP(FM);
   } else if (nv == 0) {
