@@ -349,7 +349,8 @@ __device__ __forceinline__ u32x4* ring(int h, const Ring& r) {
 // keeps its 16-B chunk c at slot c ^ (r & 7).  With 2 WM regions the passes
 // alternate between two sets and need one barrier each; with WM regions a
 // second barrier ends every pass.  The regions are ring buffers: a first
-// barrier makes sure no wave still reads the last stage.
+// barrier makes sure no wave still reads the last stage.  Passes past the
+// tile's last row (the same for every wave) are skipped.
 template <int BM, int BN, int BNT, int WM, int WN, bool GLU>
 struct StagedEpi {
   static constexpr int ES = GLU ? 2 : 4;                  // bf16 h or fp32 y
@@ -389,6 +390,7 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    if (32 * i >= rows) break;   // no wave holds a live row in this or a later pass
     char* R = (char*)ring((DB ? (i & 1) * WM : 0) + wm, reg);
 #pragma unroll
     for (int j = 0; j < FNO; ++j)
