@@ -127,6 +127,49 @@ __device__ __forceinline__ void limit_groups(double (&key)[NE], const double (&a
   }
 }
 
+// Logits of token t for experts lane + 64 i: the split-K partials summed
+// in split order z = 0, 1, ... (then the offset), -inf for experts past E or
+// a token past T.  Four splits' loads are in flight at once.
+template <int NE>
+__device__ __forceinline__ void gather_logits(float (&l)[NE], const float* __restrict__ part,
+                                              int nsplit, int T_, int E, int t, bool tok_ok,
+                                              int lane, const float* __restrict__ offset,
+                                              float* __restrict__ logits) {
+  bool ok[NE];
+  float v[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    ok[i] = tok_ok && lane + 64 * i < E;
+    v[i] = 0.f;
+  }
+  const size_t zs = (size_t)T_ * E;
+  const float* base = part + (size_t)t * E + lane;
+  int z = 0;
+  for (; z + 4 <= nsplit; z += 4) {
+    float q[4][NE];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) q[u][i] = ok[i] ? base[(size_t)(z + u) * zs + 64 * i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) v[i] += q[u][i];
+  }
+  for (; z < nsplit; ++z)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) v[i] += ok[i] ? base[(size_t)z * zs + 64 * i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    if (ok[i]) {
+      if (offset) v[i] += offset[e];
+      if (logits) logits[(size_t)t * E + e] = v[i];
+    }
+    l[i] = ok[i] ? v[i] : -INFINITY;
+  }
+}
+
 template <int NE>
 __global__ __launch_bounds__(256) void k_router_select(
     const float* __restrict__ part, int nsplit, int T_, int E,
@@ -140,18 +183,7 @@ __global__ __launch_bounds__(256) void k_router_select(
   const bool tok_ok = t < T_;
   float l[NE], p[NE];
   double key[NE], s64[NE];
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int e = lane + 64 * i;
-    float v = -INFINITY;
-    if (tok_ok && e < E) {
-      v = 0.f;
-      for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T_ + t) * E + e];
-      if (offset) v += offset[e];
-      if (logits) logits[(size_t)t * E + e] = v;
-    }
-    l[i] = v;
-  }
+  gather_logits<NE>(l, part, nsplit, T_, E, t, tok_ok, lane, offset, logits);
   double aff[NE];                        // group scores' affinities (fp64)
   if (score == MOE_SOFTMAX) {
     float m = -INFINITY;
@@ -350,18 +382,7 @@ __global__ __launch_bounds__(256) void k_ec_scores(const float* __restrict__ par
     const int t = t0 + tl;
     const bool tok_ok = t < T_;
     float l[NE];
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = lane + 64 * i;
-      float v = -INFINITY;
-      if (tok_ok && e < E) {
-        v = 0.f;
-        for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T_ + t) * E + e];
-        if (offset) v += offset[e];
-        if (logits) logits[(size_t)t * E + e] = v;
-      }
-      l[i] = v;
-    }
+    gather_logits<NE>(l, part, nsplit, T_, E, t, tok_ok, lane, offset, logits);
     double lse = 0.0;
     if (score == MOE_SOFTMAX) {
       float m = -INFINITY;
@@ -517,6 +538,9 @@ __global__ __launch_bounds__(1024) void k_ec_select(
 // path it is doubled while that leaves fewer tiles than CUs, slices stay
 // multiples of 128 elements and the partial logits the select pass reads
 // stay small (<= 16 MB).
+// Waves per 16-token group of the skinny logits kernel (divides 4).
+static int router_wpt(int E) { return E > 48 ? 4 : E > 16 ? 2 : 1; }
+
 int router_split(int64_t T, int d, int E, int dtype) {
   int s = d / 1024;
   s = s < 1 ? 1 : (s > 8 ? 8 : s);
@@ -524,6 +548,12 @@ int router_split(int64_t T, int d, int E, int dtype) {
     while ((int64_t)router_gemm_tiles(T, E) * s < 256 && s * 2 <= 16 && d % (2 * s) == 0 &&
            (d / (2 * s)) % 128 == 0 && 2 * s * T * (int64_t)E * 4 <= ((int64_t)16 << 20))
       s *= 2;
+  } else {
+    // skinny kernel: with few tokens, split K further until the grid has
+    // about two blocks per CU (each split keeps >= 256 elements of K)
+    const int wpt = router_wpt(E);
+    const int64_t blocks = MOE_CEIL_DIV(T, 16 * (4 / wpt)) * MOE_CEIL_DIV(E, 16 * wpt);
+    while (blocks * s < 512 && d / (2 * s) >= 256 && 2 * s <= 32) s *= 2;
   }
   return s;
 }
@@ -556,7 +586,7 @@ static hipError_t launch_logit_partials(const void* X, int dtype, int64_t T, int
     // many experts: the LDS-tiled GEMM reads X once and W_g once per M-tile
     return launch_router_gemm(X, Wg, T, d, E, split, part, p, s);
   }
-  const int wpt = E > 48 ? 4 : E > 16 ? 2 : 1;   // waves per token group (divides 4)
+  const int wpt = router_wpt(E);
   dim3 g1((unsigned)MOE_CEIL_DIV(T, 16 * (4 / wpt)), (unsigned)MOE_CEIL_DIV(E, 16 * wpt),
           (unsigned)split);
   if (dtype == MOE_BF16)
