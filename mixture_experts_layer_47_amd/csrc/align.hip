@@ -274,6 +274,117 @@ __global__ __launch_bounds__(256) void k_rr_place(
   }
 }
 
+// Few slots (at most 4096): the three passes in one block of 16 waves, with
+// the chunk histograms, bases and offsets in LDS instead of global memory,
+// and chunks of NG x 64 slots so that every wave has a chunk.  A stable rank
+// does not depend on the chunking, so the ranks, drops and permutation are
+// the same bits as the three-kernel path's; only launches and global round
+// trips go away (decode batches).
+constexpr int kSmallWaves = 16;
+constexpr int64_t kSmallSlots = kSmallWaves * 4 * 64;
+template <int NG>
+__global__ __launch_bounds__(1024) void k_align_small(
+    const int32_t* __restrict__ ids, int64_t Tk, int k, int E, int nchunks, int64_t cap,
+    int tail_rows, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_kept, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token) {
+  __shared__ int32_t hist[kSmallWaves][256];
+  __shared__ int32_t off[257];
+  const int lane = threadIdx.x & 63, c = threadIdx.x >> 6;
+  const int nb = nbits_for(E);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int CHUNK = NG * 64;
+  int ev[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int64_t sl = (int64_t)c * CHUNK + g * 64 + lane;
+    ev[g] = (c < nchunks && sl < Tk) ? ids[sl] : -1;
+  }
+  // pass 1: chunk histograms
+  volatile int32_t* cnt = hist[c];
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  if (c < nchunks) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const bool v = ev[g] >= 0;
+      const int e = v ? ev[g] : 0;
+      const uint64_t eq = match_id(e, v, nb);
+      if (v && (eq & lt) == 0) cnt[e] = cnt[e] + __popcll(eq);
+    }
+  }
+  __syncthreads();
+  // pass 2: per-expert chunk bases, counts, kept rows; offsets by a wave scan
+  int kept = 0;
+  if (threadIdx.x < (unsigned)E) {
+    const int e = threadIdx.x;
+    int run = 0;
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int h = hist[cc][e];
+      hist[cc][e] = run;
+      run += h;
+    }
+    counts[e] = run;
+    kept = (cap > 0 && run > cap) ? (int)cap : run;
+    off[e] = kept;
+  }
+  __syncthreads();
+  if (c == 0) {                      // exclusive scan of off[0..E) by wave 0, 4 per lane
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      v[i] = e < E ? off[e] : 0;
+      sum += v[i];
+    }
+    int inc = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    int acc = inc - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < E) { off[e] = acc; offsets[e] = acc; }
+      acc += v[i];
+    }
+    if (lane == 63) {
+      offsets[E] = acc;
+      if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
+      n_kept[0] = acc;
+      off[256] = acc;
+    }
+  }
+  __syncthreads();
+  // pass 3: stable ranks, drops and the permutation
+  if (c < nchunks) {
+    volatile int32_t* base = hist[c];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int64_t sl = (int64_t)c * CHUNK + g * 64 + lane;
+      const bool v = ev[g] >= 0;
+      const int e = v ? ev[g] : 0;
+      const uint64_t eq = match_id(e, v, nb);
+      int rank = 0;
+      if (v) rank = base[e] + __popcll(eq & lt);
+      __builtin_amdgcn_wave_barrier();
+      if (v && (eq & lt) == 0) base[e] = rank + __popcll(eq);
+      if (v) {
+        const bool keep = cap <= 0 || rank < cap;
+        const int row = keep ? off[e] + rank : -1;
+        slot_row[sl] = row;
+        if (keep) {
+          sorted_slot[row] = (int32_t)sl;
+          if (row_token) row_token[row] = (int32_t)(sl / k);
+        }
+      }
+    }
+  }
+  // shared-expert rows after the kept rows
+  if (row_token)
+    for (int t = threadIdx.x; t < tail_rows; t += 1024) row_token[off[256] + t] = t;
+}
+
 // Rows of the shared expert: row_token[R + t] = t, R read on the device.
 __global__ __launch_bounds__(256) void k_tail_tokens(const int32_t* __restrict__ n_kept,
                                                      int T_, int32_t* __restrict__ row_token) {
@@ -321,6 +432,14 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
                            int32_t* row_token, void* ws, hipStream_t s) {
   const int64_t Tk = T * (int64_t)k;
   const int nch = align_nchunks(Tk, E);
+  if (Tk <= kSmallSlots) {
+    const int ng = Tk <= kSmallSlots / 4 ? 1 : Tk <= kSmallSlots / 2 ? 2 : 4;
+    const int nc = (int)MOE_CEIL_DIV(Tk, ng * 64);
+    auto kern = ng == 1 ? k_align_small<1> : ng == 2 ? k_align_small<2> : k_align_small<4>;
+    hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, ids, Tk, k, E, nc, cap, tail_rows,
+                       counts, offsets, n_kept, sorted_slot, slot_row, row_token);
+    return hipGetLastError();
+  }
   int32_t* hist = (int32_t*)ws;
   const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
   if (nch > 0)
