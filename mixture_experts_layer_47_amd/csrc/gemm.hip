@@ -989,10 +989,14 @@ struct WorkListArgs {
   int32_t* nwork;
 };
 
+// blockIdx.y picks the list; the kWorkSlices blocks of a list each rebuild
+// the group scan (cheap, G <= 1024) and write every kWorkSlices-th run of
+// 1024 entries.
+constexpr int kWorkSlices = 8;
 __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ offsets, int G,
                                                     int max_rows, WorkListArgs l0,
                                                     WorkListArgs l1) {
-  const WorkListArgs& l = blockIdx.x == 0 ? l0 : l1;
+  const WorkListArgs& l = blockIdx.y == 0 ? l0 : l1;
   const int BM = l.BM, NN = l.NN, NG = l.NG, ksplit = l.ksplit;
   int2* __restrict__ work = l.work;
   int32_t* __restrict__ nwork = l.nwork;
@@ -1006,17 +1010,24 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
     mt = MOE_CEIL_DIV(b - a, BM);
   }
   mts[g] = mt;
-  sc[g] = mt * NN * ksplit;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {       // inclusive Hillis-Steele scan
-    const int v = (g >= o) ? sc[g - o] : 0;
-    __syncthreads();
-    sc[g] += v;
-    __syncthreads();
+  // inclusive scan of the entry counts: in each wave by shuffles, then over
+  // the 16 wave totals
+  __shared__ int32_t wsum[16];
+  const int lane = g & 63, wv = g >> 6;
+  int v = mt * NN * ksplit;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
   }
+  if (lane == 63) wsum[wv] = v;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += wsum[i];
+  sc[g] = v + before;
+  __syncthreads();
   const int total = sc[1023];
   const int nfull = NN / NG;
-  for (int e = g; e < total; e += 1024) {
+  for (int e = blockIdx.x * 1024 + g; e < total; e += kWorkSlices * 1024) {
     int lo = 0, hi = G - 1;                     // first group with inclusive sum > e
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -1040,7 +1051,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
     }
     work[e] = make_int2(gg | (ni << 10) | (ks << 24), mi * BM);
   }
-  if (g == 0) nwork[0] = total;
+  if (blockIdx.x == 0 && g == 0) nwork[0] = total;
 }
 
 // ------------------------------------------------------------------ launch
@@ -1157,8 +1168,8 @@ static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream
                           bool glub = false) {
   const WorkListArgs l0 = work_list_args(a, BM, BN, glu);
   const WorkListArgs l1 = b ? work_list_args(*b, BMb, BNb, glub) : l0;
-  hipLaunchKernelGGL(k_work_list, dim3(b ? 2 : 1), dim3(1024), 0, s, a.offsets, a.G, a.max_rows,
-                     l0, l1);
+  hipLaunchKernelGGL(k_work_list, dim3(kWorkSlices, b ? 2 : 1), dim3(1024), 0, s, a.offsets, a.G,
+                     a.max_rows, l0, l1);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
