@@ -274,14 +274,14 @@ __global__ __launch_bounds__(256) void k_rr_place(
   }
 }
 
-// Few slots (at most 4096): the three passes in one block of 16 waves, with
+// Few slots (at most 8192): the three passes in one block of 16 waves, with
 // the chunk histograms, bases and offsets in LDS instead of global memory,
 // and chunks of NG x 64 slots so that every wave has a chunk.  A stable rank
 // does not depend on the chunking, so the ranks, drops and permutation are
 // the same bits as the three-kernel path's; only launches and global round
 // trips go away (decode batches).
 constexpr int kSmallWaves = 16;
-constexpr int64_t kSmallSlots = kSmallWaves * 4 * 64;
+constexpr int64_t kSmallSlots = kSmallWaves * 8 * 64;
 template <int NG>
 __global__ __launch_bounds__(1024) void k_align_small(
     const int32_t* __restrict__ ids, int64_t Tk, int k, int E, int nchunks, int64_t cap,
@@ -433,9 +433,10 @@ hipError_t launch_dispatch(const int32_t* ids, int64_t T, int k, int E, int64_t 
   const int64_t Tk = T * (int64_t)k;
   const int nch = align_nchunks(Tk, E);
   if (Tk <= kSmallSlots) {
-    const int ng = Tk <= kSmallSlots / 4 ? 1 : Tk <= kSmallSlots / 2 ? 2 : 4;
+    const int ng = Tk <= kSmallSlots / 8 ? 1 : Tk <= kSmallSlots / 4 ? 2 : Tk <= kSmallSlots / 2 ? 4 : 8;
     const int nc = (int)MOE_CEIL_DIV(Tk, ng * 64);
-    auto kern = ng == 1 ? k_align_small<1> : ng == 2 ? k_align_small<2> : k_align_small<4>;
+    auto kern = ng == 1 ? k_align_small<1> : ng == 2 ? k_align_small<2>
+              : ng == 4 ? k_align_small<4> : k_align_small<8>;
     hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, ids, Tk, k, E, nc, cap, tail_rows,
                        counts, offsets, n_kept, sorted_slot, slot_row, row_token);
     return hipGetLastError();
