@@ -36,6 +36,67 @@ __device__ __forceinline__ int nbits_for(int E) {
   return E <= 1 ? 0 : 32 - __clz(E - 1);
 }
 
+// Expert e's column of the chunk histograms hist[c][e] becomes exclusive
+// per-chunk bases (chunk order); returns the expert's total.  Eight chunks'
+// loads are in flight at once.
+__device__ __forceinline__ int chunk_bases(int32_t* __restrict__ hist, int E, int nchunks, int e) {
+  int run = 0, c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    int h[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) h[u] = hist[(size_t)(c + u) * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      hist[(size_t)(c + u) * E + e] = run;
+      run += h[u];
+    }
+  }
+  for (; c < nchunks; ++c) {
+    const int h = hist[(size_t)c * E + e];
+    hist[(size_t)c * E + e] = run;
+    run += h;
+  }
+  return run;
+}
+
+// Exclusive scan of the per-expert row counts in[0..E) (E <= 256, LDS) by
+// one wave, four experts per lane: offsets[0..E], offsets[E + 1] = total +
+// tail_rows when there is a tail, n_kept = total; out (LDS, may be in)
+// receives the offsets and out[256] the total when given.
+__device__ __forceinline__ void wave_offsets(const int32_t* in, int E, int tail_rows,
+                                             int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ n_kept, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  int v[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane * 4 + i;
+    v[i] = e < E ? in[e] : 0;
+    sum += v[i];
+  }
+  int inc = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  int acc = inc - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane * 4 + i;
+    if (e < E) {
+      offsets[e] = acc;
+      if (out) out[e] = acc;
+    }
+    acc += v[i];
+  }
+  if (lane == 63) {
+    offsets[E] = acc;
+    if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
+    n_kept[0] = acc;
+    if (out) out[256] = acc;
+  }
+}
+
 // Pass 1: chunk histograms hist[c][e].
 template <int CHUNK>
 __global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__ ids,
@@ -80,26 +141,12 @@ __global__ __launch_bounds__(256) void k_align_scan(int32_t* __restrict__ hist, 
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {          // hist becomes exclusive bases
-      const int h = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;
-      run += h;
-    }
+    run = chunk_bases(hist, E, nchunks, e);       // hist becomes exclusive bases
     counts[e] = run;
   }
   kept[e] = (e < E) ? (cap > 0 && run > cap ? (int)cap : run) : 0;
   __syncthreads();
-  if (e == 0) {                                   // E <= 256: serial scan is cheap
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      const int v = kept[i];
-      offsets[i] = acc;
-      acc += v;
-    }
-    offsets[E] = acc;
-    if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
-    n_kept[0] = acc;
-  }
+  if (threadIdx.x < 64) wave_offsets(kept, E, tail_rows, offsets, n_kept, nullptr);
 }
 
 // Pass 3: stable ranks, drop mask and the permutation.
@@ -188,12 +235,7 @@ __global__ __launch_bounds__(256) void k_rr_scan(int32_t* __restrict__ hist2, in
   __shared__ int32_t tot[256];
   const int e = threadIdx.x;
   if (e < E) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist2[(size_t)c * E + e];
-      hist2[(size_t)c * E + e] = run;
-      run += h;
-    }
+    const int run = chunk_bases(hist2, E, nchunks, e);
     const int kept1 = counts[e] < cap ? counts[e] : (int)cap;
     const int room = (int)cap - kept1;
     const int acc = run < room ? run : room;
@@ -203,16 +245,7 @@ __global__ __launch_bounds__(256) void k_rr_scan(int32_t* __restrict__ hist2, in
     tot[e] = kept1 + acc;
   }
   __syncthreads();                                // old offsets read before the rewrite
-  if (e == 0) {
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      offsets[i] = acc;
-      acc += tot[i];
-    }
-    offsets[E] = acc;
-    if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
-    n_kept[0] = acc;
-  }
+  if (threadIdx.x < 64) wave_offsets(tot, E, tail_rows, offsets, n_kept, nullptr);
 }
 
 // Final placement of every slot: first-pass rows move by their expert's
@@ -328,33 +361,7 @@ __global__ __launch_bounds__(1024) void k_align_small(
     off[e] = kept;
   }
   __syncthreads();
-  if (c == 0) {                      // exclusive scan of off[0..E) by wave 0, 4 per lane
-    int v[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      v[i] = e < E ? off[e] : 0;
-      sum += v[i];
-    }
-    int inc = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    int acc = inc - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      if (e < E) { off[e] = acc; offsets[e] = acc; }
-      acc += v[i];
-    }
-    if (lane == 63) {
-      offsets[E] = acc;
-      if (tail_rows > 0) offsets[E + 1] = acc + tail_rows;
-      n_kept[0] = acc;
-      off[256] = acc;
-    }
-  }
+  if (c == 0) wave_offsets(off, E, tail_rows, offsets, n_kept, off);
   __syncthreads();
   // pass 3: stable ranks, drops and the permutation
   if (c < nchunks) {
