@@ -16,10 +16,11 @@
 
 namespace moe {
 
-// Slots per wave (chunk): 256 (4 groups of 64) for up to 64 experts, else
-// 1024.  Short chunks give more waves for few experts; with many experts the
-// per-expert scan over chunk histograms would grow instead.
-__host__ __device__ constexpr int align_chunk_for(int E) { return E <= 64 ? 256 : 1024; }
+// Slots per wave (chunk): 256, four groups of 64.  Short chunks give more
+// waves; the per-expert walk over chunk histograms that grows with them
+// keeps eight chunks' loads in flight (with 256 experts and 32768 slots,
+// chunks of 256 measured 27 us against 31 us for 512 and 40 us for 1024).
+__host__ __device__ constexpr int align_chunk_for(int) { return 256; }
 
 // Mask of active lanes whose expert id equals this lane's.
 __device__ __forceinline__ uint64_t match_id(int e, bool valid, int nbits) {
