@@ -336,7 +336,10 @@ def test_route_expert_choice_entry_point(score, T, E, C):
 
 @pytest.mark.parametrize("T,k,E,C", [(1, 1, 1, 0), (100, 2, 8, 0), (1000, 8, 256, 0),
                                      (1000, 8, 256, 20), (3000, 1, 64, 40), (777, 3, 5, 1),
-                                     (5000, 4, 17, 900)])
+                                     (5000, 4, 17, 900),
+                                     # the one-block path ends at 8192 slots
+                                     (8192, 1, 8, 0), (8193, 1, 8, 0), (1024, 8, 256, 40),
+                                     (2049, 4, 256, 30)])
 @pytest.mark.parametrize("reroute", [False, True])
 def test_dispatch_entry_point(T, k, E, C, reroute):
     _announce(f"moe_dispatch T={T} k={k} E={E} C={C} reroute={reroute}")
