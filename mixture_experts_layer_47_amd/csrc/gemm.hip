@@ -6,22 +6,25 @@
 // (14.2.2): h = silu(x W1) * (x W3), y = h W2.
 //
 // Kernel shape (one launch per projection):
-//   * a device-built work list holds one entry per (expert, M-tile, N-tile);
-//     it is ordered expert by expert, and inside an expert in runs of NG
-//     neighbouring N-tiles with the M-tiles fastest, so the tiles that run
-//     at the same time on one XCD share both their weight slices and their
-//     activation rows in that XCD's L2;
+//   * a device-built work list holds one entry per (expert, M-tile, N-tile
+//     [, K-split]); it is ordered expert by expert, and inside an expert in
+//     runs of NG neighbouring N-tiles with the M-tiles fastest, so the tiles
+//     that run at the same time on one XCD share both their weight slices
+//     and their activation rows in that XCD's L2;
 //   * one block per list entry, one block per CU at a time; blocks are
 //     mapped to entries so that in each round of (CUs) blocks every XCD
 //     works on a contiguous run of the list;
 //   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
 //     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
 //     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
-//   * BK = 128 bytes of K per stage (64 bf16 / 32 fp32), two LDS stages
-//     and two register staging sets: a software pipeline over k16 substeps
-//     reads each substep's fragments while the previous substep's MFMAs
-//     run, and fetches stage k+2 from global memory while stage k+1 is
-//     stored to LDS, so loads have ~1.6 stages to arrive; scheduling groups
+//   * two kernels share the tile logic.  k_moe_gemm_dma (bf16 and FP8
+//     prefill, FP8 decode) copies each stage from global memory straight
+//     into LDS rings (global_load_lds), described at the kernel.
+//     k_moe_gemm (bf16 decode, fp32) stages through registers: BK = 128
+//     bytes of K per stage, two LDS stages and two register staging sets,
+//     stage k+2 fetched while stage k+1 is stored to LDS;
+//   * in both, a software pipeline over k16 substeps reads each substep's
+//     fragments while the previous substep's MFMAs run; scheduling groups
 //     pin the interleave;
 //   * LDS rows are 8 chunks of 16 B, chunk c of row r at slot
 //     c ^ ((r ^ (r/8 mod 4)) mod 8): the 16-B stores and the fragment reads
@@ -32,7 +35,10 @@
 //     per operand; fp32: four v_mfma_f32_32x32x2f32 per 16-B fragment;
 //   * gate/up fusion: the B tile holds BN rows of W1 then BN rows of W3, a
 //     wave owns matching gate and up columns, and SwiGLU runs on the fp32
-//     accumulators before one rounding of h to the storage type.
+//     accumulators before one rounding of h to the storage type;
+//   * epilogues: bf16 h is stored from the accumulators (8 bytes per lane);
+//     the down projection's fp32 rows pass through LDS so that each store
+//     instruction writes whole lines (store_tile_staged).
 #include <cmath>
 #include <type_traits>
 #include <utility>
