@@ -443,7 +443,9 @@ def test_forward_ksplit_paths_agree():
 
 
 @pytest.mark.parametrize("T,k,d,keep", [(257, 3, 384, 0.5), (64, 256, 256, 0.05),
-                                        (40, 64, 128, 0.3), (9, 16, 128, 0.0)])
+                                        (40, 64, 128, 0.3), (9, 16, 128, 0.0),
+                                        # all kept: rows summed in groups of 4, then 2, then 1
+                                        (33, 7, 256, 1.0), (20, 5, 128, 1.0), (16, 8, 1024, 1.0)])
 def test_combine_entry_point(T, k, d, keep):
     _announce(f"moe_combine T={T} k={k} d={d}")
     g = torch.Generator().manual_seed(9)
