@@ -151,7 +151,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library runs on one GPU; the multi-GPU design is written up, not built).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
