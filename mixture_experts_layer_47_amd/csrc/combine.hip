@@ -13,7 +13,7 @@ namespace moe {
 
 // KS: a second fp32 slab (the down projection's second K-split) is present.
 template <typename OutT, bool KS>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows,
+__global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows,
                                                  const float* __restrict__ Yrows2,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ w, int k, int d,
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ int32_t rows[256];
   __shared__ float gw[256];
-  __shared__ int nw[4];
+  __shared__ int nw[8];
   int32_t r = -1;
   float g = 0.f;
   if (threadIdx.x < (unsigned)k) {
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
   __syncthreads();
   int at = 0;
   for (int i = 0; i < wave; ++i) at += nw[i];
-  const int n = (nw[0] + nw[1]) + (nw[2] + nw[3]);
+  const int n = ((nw[0] + nw[1]) + (nw[2] + nw[3])) + ((nw[4] + nw[5]) + (nw[6] + nw[7]));
   if (r >= 0) {
     const uint64_t below = lane ? (kept & (~0ull >> (64 - lane))) : 0ull;
     at += __popcll(below);
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Yrows
     }
     return y;
   };
-  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+  for (int c = threadIdx.x * 4; c < d; c += 512 * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int j = 0;
     // four rows' loads in flight at once; the sum still runs j = 0, 1, ...
@@ -119,7 +119,7 @@ hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t
                           const float* w, int64_t T, int k, int d, const float* shared,
                           const int32_t* shared_row0, void* Y, int dtype, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)T), block(256);
+  const dim3 grid((unsigned)T), block(512);
   if (dtype == MOE_BF16) {
     if (Yrows2)
       hipLaunchKernelGGL((k_combine<uint16_t, true>), grid, block, 0, s, Yrows, Yrows2, slot_row, w,
