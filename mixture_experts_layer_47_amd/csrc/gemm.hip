@@ -812,7 +812,9 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
 
 // TB = uint16_t (bf16 weights) or uint8_t (E4M3 weights, Q8, with scales
 // sc0/sc1 [G][N] and sc0l/sc1l [N] for group g_last).
-template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8, int NBB>
+// DENSE: one group of max_rows rows and no work list (the router logits).
+template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8, int NBB,
+          bool DENSE>
 __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
@@ -860,17 +862,29 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   const int cx = round >> 3;
   const int xi = blockIdx.x >> 3;
   const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
-  if (t >= nwork[0]) return;
+  // A dense product (no list: one group of max_rows rows, the router
+  // logits) takes entry t as M-tile t % mt of N-tile (t / mt) % NN and
+  // K-split t / (mt NN).
+  int2 wi;
+  if constexpr (DENSE) {
+    const int mt = (max_rows + BM - 1) / BM, nn = N / BN;
+    if (t >= mt * nn * ksplit) return;
+    const int kt = t / (mt * nn), r = t - kt * (mt * nn);
+    wi = make_int2(((r / mt) << 10) | (kt << 24), (r % mt) * BM);
+  } else {
+    if (t >= nwork[0]) return;
+    wi = work[t];
+  }
   const int Kc = K / ksplit;
   const int nk = Kc / (KB / 2);
-  const int2 wi = work[t];
   const int g = wi.x & 1023;
   const int n0 = ((wi.x >> 10) & 16383) * BN;
   const int ks = (int)((uint32_t)wi.x >> 24);
   const int kbeg = ks * Kc;
-  const int gbeg = min(max(offsets[g], 0), max_rows);
+  const int gbeg = DENSE ? 0 : min(max(offsets[g], 0), max_rows);
   const int rbeg = gbeg + wi.y;
-  const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
+  const int gend = DENSE ? max_rows : min(max(offsets[g + 1], gbeg), max_rows);
+  const int rows = min(BM, gend - rbeg);
   const TB* B0 = (const TB*)B0v;
   const TB* B1 = (const TB*)B1v;
   const TB* w0 = ((g == g_last) ? (const TB*)B0lv : B0 + (size_t)g * N * K) + kbeg;
@@ -1194,13 +1208,13 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
-          int NBB = NBUF>
+          int NBB = NBUF, bool DENSE = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB, DENSE>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
                      a.B0, a.B1, a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
                      a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
@@ -1227,13 +1241,9 @@ __global__ __launch_bounds__(256) void k_reduce_split(float* __restrict__ Y,
 }
 
 // ---------------------------------------------------------------- router
-// Router logits through the same tiled kernel: one group of T rows,
-// part[z][t][e] = sum over K-split z of X[t] . Wg[e].  Used when E is a
-// multiple of 64; the select kernel sums the splits in order.
-__global__ void k_set_range(int32_t* __restrict__ off, int n) {
-  off[0] = 0;
-  off[1] = n;
-}
+// Router logits through the same tiled kernel, as a dense product (no work
+// list, no group offsets): part[z][t][e] = sum over K-split z of X[t] . Wg[e].
+// Used when E is a multiple of 64; the select kernel sums the splits in order.
 
 static int router_bn(int E) { return E % 256 == 0 ? 256 : E % 128 == 0 ? 128 : 64; }
 
@@ -1245,28 +1255,18 @@ bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split) {
 
 int router_gemm_tiles(int64_t T, int E) { return (int)MOE_CEIL_DIV(T, 128) * (E / router_bn(E)); }
 
-size_t router_gemm_ws_bytes(int64_t T, int d, int E, int split) {
-  const int bn = router_bn(E);
-  return align256(2 * sizeof(int32_t)) +
-         align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2)) +
-         align256(sizeof(int32_t));
-}
+size_t router_gemm_ws_bytes(int64_t, int, int, int) { return 0; }   // nothing beyond the partials
 
 hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, int E, int split,
                               float* part, void* ws, hipStream_t s) {
-  char* q = (char*)ws;
-  int32_t* off = (int32_t*)q;  q += align256(2 * sizeof(int32_t));
+  (void)ws;                    // a dense product: the kernel derives its tiles, no list
   const int bn = router_bn(E);
-  int2* work = (int2*)q;       q += align256((size_t)max_work(T, 1, 128, E, bn, split) * sizeof(int2));
-  int32_t* nwork = (int32_t*)q;
-  hipLaunchKernelGGL(k_set_range, dim3(1), dim3(1), 0, s, off, (int)T);
   const int mr = (int)T;
-  GemmArgs a{X, nullptr, off, 1, Wg, nullptr, nullptr, nullptr, -1, d, E, mr, part, work, nwork,
-             split, part + (size_t)T * E};
-  run_work_list(a, 128, bn, false, s);
-  if (bn == 256) run_gemm_dma<128, 256, 2, 2, false, 128, 3>(a, s);
-  else if (bn == 128) run_gemm_dma<128, 128, 2, 2, false, 128, 3>(a, s);
-  else run_gemm_dma<128, 64, 2, 2, false, 128, 3>(a, s);
+  GemmArgs a{X, nullptr, nullptr, 1, Wg, nullptr, nullptr, nullptr, -1, d, E, mr, part, nullptr,
+             nullptr, split, part + (size_t)T * E};
+  if (bn == 256) run_gemm_dma<128, 256, 2, 2, false, 128, 3, false, 3, true>(a, s);
+  else if (bn == 128) run_gemm_dma<128, 128, 2, 2, false, 128, 3, false, 3, true>(a, s);
+  else run_gemm_dma<128, 64, 2, 2, false, 128, 3, false, 3, true>(a, s);
   return hipGetLastError();
 }
 
