@@ -267,6 +267,52 @@ def test_deterministic_bitwise(name):
             assert torch.equal(a1[k], f.aux[k]), k
 
 
+@pytest.mark.parametrize("name", ["mixtral_prefill", "dsv3_prefill", "dsv3_prefill_fp8",
+                                  "mixtral_prefill_ec", "switch_capacity_reroute"])
+def test_forward_graph_replay(name):
+    """moe_forward launches kernels only (no allocation, no host
+    synchronisation, no memset nodes), so a HIP graph can record it. Every
+    replay, with eager work on the stream between replays, matches the eager
+    call bit for bit, also after new tokens are copied into the captured
+    input (routing, counts and tile lists are rebuilt on the device)."""
+    import dataclasses
+    w = SMALL[name]
+    _announce(f"graph replay {w.name}")
+    inp = make_inputs(w, DEV)
+    layer = moe.layer_from_inputs(inp)
+    X2 = make_inputs(dataclasses.replace(w, x_seed=w.seed + 101), DEV)["X"]
+    want = []
+    for X in (inp["X"], X2):
+        e = moe.Forward(layer, X.clone(), aux=True)
+        for t in e.aux.values():
+            t.fill_(-7)  # rows the layer leaves unwritten (dropped slots) hold -7 on both sides
+        want.append((e().clone(), {k: v.clone() for k, v in e.aux.items()}))
+    f = moe.Forward(layer, inp["X"].clone(), aux=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f()
+    torch.cuda.synchronize()
+    for rep, which in enumerate((0, 1, 0, 1)):
+        f.X.copy_(inp["X"] if which == 0 else X2)
+        f.Y.fill_(float("nan"))
+        for t in f.aux.values():
+            t.fill_(-7)
+        junk = torch.randn(4096, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk).all()
+        Y_ref, aux_ref = want[which]
+        assert torch.equal(f.Y, Y_ref), f"replay {rep}"
+        for k in aux_ref:
+            assert torch.equal(f.aux[k], aux_ref[k]), (rep, k)
+
+
 # ---------------------------------------------------------- entry points --
 @pytest.mark.parametrize("score,ng,tg", [("sigmoid", 1, 1), ("sigmoid", 8, 4), ("sigmoid", 4, 1),
                                          ("softmax", 8, 2), ("softmax", 32, 32)])
