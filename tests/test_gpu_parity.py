@@ -428,6 +428,9 @@ FFN_SHAPES = {
     "large_ksplit": (768, 4096, [300, 260, 280, 290], 0),
     # medium tiles 256 rows tall: every count of 32-row blocks from 1 to 8
     "tall_tiles": (512, 512, [1, 33, 65, 97, 129, 161, 193, 225, 256, 250, 70], 3),
+    # large tiles, nine groups (one short): 264 down tiles, more than one
+    # dispatch round
+    "large_tail": (2048, 256, [1024, 1000, 900, 800, 1024, 1024, 1024, 1024, 100], 0),
 }
 
 
