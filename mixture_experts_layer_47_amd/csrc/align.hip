@@ -324,6 +324,10 @@ __global__ __launch_bounds__(1024) void k_align_small(
     int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token) {
   __shared__ int32_t hist[kSmallWaves][256];
   __shared__ int32_t off[257];
+  // The permutation (row -> slot) is built here and written out in row order
+  // at the end: one CU storing it scattered, 4 B at a time, was the slowest
+  // part of this kernel.
+  __shared__ int32_t s_slot[kSmallSlots];
   const int lane = threadIdx.x & 63, c = threadIdx.x >> 6;
   const int nb = nbits_for(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -381,16 +385,20 @@ __global__ __launch_bounds__(1024) void k_align_small(
         const bool keep = cap <= 0 || rank < cap;
         const int row = keep ? off[e] + rank : -1;
         slot_row[sl] = row;
-        if (keep) {
-          sorted_slot[row] = (int32_t)sl;
-          if (row_token) row_token[row] = (int32_t)(sl / k);
-        }
+        if (keep) s_slot[row] = (int32_t)sl;
       }
     }
   }
+  __syncthreads();
+  const int nk = off[256];               // kept rows (<= Tk <= kSmallSlots)
+  for (int r = threadIdx.x; r < nk; r += 1024) {
+    const int32_t sl = s_slot[r];
+    sorted_slot[r] = sl;
+    if (row_token) row_token[r] = sl / k;
+  }
   // shared-expert rows after the kept rows
   if (row_token)
-    for (int t = threadIdx.x; t < tail_rows; t += 1024) row_token[off[256] + t] = t;
+    for (int t = threadIdx.x; t < tail_rows; t += 1024) row_token[nk + t] = t;
 }
 
 // Rows of the shared expert: row_token[R + t] = t, R read on the device.
