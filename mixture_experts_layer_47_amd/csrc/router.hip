@@ -129,7 +129,7 @@ __device__ __forceinline__ void limit_groups(double (&key)[NE], const double (&a
 
 // Logits of token t for experts lane + 64 i: the split-K partials summed
 // in split order z = 0, 1, ... (then the offset), -inf for experts past E or
-// a token past T.  Four splits' loads are in flight at once.
+// a token past T.  Up to 32 partial logits per lane are loaded at once.
 template <int NE>
 __device__ __forceinline__ void gather_logits(float (&l)[NE], const float* __restrict__ part,
                                               int nsplit, int T_, int E, int t, bool tok_ok,
@@ -144,21 +144,23 @@ __device__ __forceinline__ void gather_logits(float (&l)[NE], const float* __res
   }
   const size_t zs = (size_t)T_ * E;
   const float* base = part + (size_t)t * E + lane;
-  int z = 0;
-  for (; z + 4 <= nsplit; z += 4) {
-    float q[4][NE];
+  // U splits' loads in flight at once (U * NE <= 32 registers), summed in
+  // split order; the last batch is predicated, so a split count that is
+  // not a multiple of U costs no extra round trips
+  constexpr int U = NE >= 4 ? 8 : 16;
+  for (int z = 0; z < nsplit; z += U) {
+    float q[U][NE];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < NE; ++i) q[u][i] = ok[i] ? base[(size_t)(z + u) * zs + 64 * i] : 0.f;
+      for (int i = 0; i < NE; ++i)
+        q[u][i] = (ok[i] && z + u < nsplit) ? base[(size_t)(z + u) * zs + 64 * i] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
+      if (z + u < nsplit)
 #pragma unroll
-      for (int i = 0; i < NE; ++i) v[i] += q[u][i];
+        for (int i = 0; i < NE; ++i) v[i] += q[u][i];
   }
-  for (; z < nsplit; ++z)
-#pragma unroll
-    for (int i = 0; i < NE; ++i) v[i] += ok[i] ? base[(size_t)z * zs + 64 * i] : 0.f;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     const int e = lane + 64 * i;
