@@ -131,6 +131,58 @@ def _full_check_ec(inp):
     return Y, aux, mask
 
 
+def _random_layer(seed):
+    """A seeded random layer inside the library's limits: d and F multiples
+    of 128, k <= min(8, E), one shared expert or none, FP8 weights only on a
+    bf16 layer, expert choice without renorm, bias or groups, re-route only
+    with a capacity factor, groups only where they divide E and can hold k."""
+    r = np.random.default_rng(1000 + seed)
+    E = int(r.choice([2, 4, 8, 12, 16, 32, 64, 96, 256]))
+    k = int(r.integers(1, min(8, E) + 1))
+    dtype = "f32" if r.random() < 0.2 else "bf16"
+    score = str(r.choice(["softmax", "sigmoid"]))
+    kw = dict(name=f"random{seed}", T=int(r.choice([1, 3, 17, 64, 129, 300, 513, 700])),
+              d=int(r.choice([128, 256, 384, 512])), E=E, k=k,
+              F=int(r.choice([128, 256, 384, 640])), dtype=dtype, score=score,
+              n_shared=int(r.random() < 0.4), seed=5000 + seed)
+    if dtype == "bf16" and r.random() < 0.3:
+        kw["wdtype"] = "fp8"
+    if r.random() < 0.3:
+        kw["zipf_s"] = 1.1
+    if r.random() < 0.2:
+        kw.update(routing="expert", renorm=False)
+        if r.random() < 0.5:
+            kw["cf"] = float(r.choice([0.5, 1.0, 1.5]))
+        return Workload(**kw)
+    kw["renorm"] = bool(r.random() < 0.6)
+    if score == "sigmoid" and r.random() < 0.6:
+        kw["bias_std"] = 0.01
+    if r.random() < 0.5:
+        kw["cf"] = float(r.choice([0.5, 1.0, 1.25, 2.0]))
+        kw["reroute"] = bool(r.random() < 0.5)
+    divs = [g for g in (2, 4, 8) if E % g == 0]
+    if divs and r.random() < 0.3:
+        ng = int(r.choice(divs))
+        tg = int(r.integers(1, ng + 1))
+        if k <= tg * (E // ng):
+            kw.update(n_group=ng, topk_group=tg)
+    return Workload(**kw)
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_forward_random_layers(seed):
+    """Seeded random layer configurations (shapes, router, renorm, capacity,
+    re-route, groups, shared expert, expert choice, fp32 / bf16 / FP8), each
+    checked step by step against the oracle like the named workloads."""
+    w = _random_layer(seed)
+    _announce(f"random layer {seed}: {w}")
+    inp = make_inputs(w, DEV)
+    if w.routing == "expert":
+        _full_check_ec(inp)
+    else:
+        _full_check(inp)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small_workloads(name):
     w = SMALL[name]
