@@ -493,8 +493,34 @@ def test_grouped_ffn_entry_point(dtype, use_row_token, shape):
     """bf16 / fp32 layers, and bf16 activations with E4M3 weights ("fp8")."""
     _announce(f"moe_grouped_ffn {shape} {dtype} row_token={use_row_token}")
     d, F, counts, slack = FFN_SHAPES[shape]
+    _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, 5)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_grouped_ffn_random(seed):
+    """Seeded random groups: empty, decode-sized, medium and above-256-row
+    counts, so the tile plan (large, medium or decode tiles) changes across
+    the draws; random d, F, dtype, row gathering and slack rows."""
+    r = np.random.default_rng(2000 + seed)
+    G = int(r.integers(1, 13))
+    kind = r.choice(["decode", "medium", "large", "mixed"])
+    lo, hi = {"decode": (0, 6), "medium": (20, 200), "large": (180, 700), "mixed": (0, 700)}[kind]
+    counts = [int(c) for c in r.integers(lo, hi + 1, G)]
+    if r.random() < 0.3:
+        counts[int(r.integers(0, G))] = 0
+    d = int(r.choice([128, 256, 384, 512, 768, 1024]))
+    F = int(r.choice([128, 256, 384, 512, 1024, 4096 if kind == "decode" else 640]))
+    dtype = str(r.choice(["bf16", "bf16", "f32", "fp8"]))
+    use_row_token = bool(r.random() < 0.5)
+    slack = int(r.choice([0, 0, 3, 64]))
+    _announce(f"moe_grouped_ffn random {seed}: d={d} F={F} {dtype} row_token={use_row_token} "
+              f"counts={counts} slack={slack}")
+    _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, 7000 + seed)
+
+
+def _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, seed):
     G = len(counts)
-    g = torch.Generator().manual_seed(5)
+    g = torch.Generator().manual_seed(seed)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     T = 400
     X = torch.randn((T, d), generator=g).to(tdt)
