@@ -275,7 +275,8 @@ def dispatch(ids, n_experts: int, cap=None, backups=None):
             expert[s] = e
     n_rerouted = 0
     if backups is not None and C is not None:
-        bk = np.asarray(backups, dtype=np.int64).reshape(flat.size // k, -1).tolist()
+        bk = (np.asarray(backups, dtype=np.int64).reshape(flat.size // k, -1).tolist()
+              if flat.size else [])
         room = [C - len(members[e]) for e in range(E)]
         for t in range(flat.size // k):
             m = 0                                  # dropped slots of token t so far

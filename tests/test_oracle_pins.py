@@ -730,6 +730,13 @@ def test_reroute_to_a_full_expert_stays_dropped():
     assert d["slot_row"][6] == -1 and d["expert"][8] == 2 and d["n_kept"] == 11
 
 
+def test_reroute_of_an_empty_batch():
+    """T = 0 with a backup table: nothing to place, nothing kept."""
+    d = O.dispatch(np.zeros((0, 3), np.int64), 8, 1, np.zeros((0, 3), np.int64))
+    assert d["n_kept"] == 0 and d["n_rerouted"] == 0
+    assert d["offsets"].tolist() == [0] * 9 and d["sorted_slot"].size == 0
+
+
 def test_backup_experts_follow_the_key_order():
     lg = np.array([[0.1, 3.0, 2.0, -1.0, 1.0]])
     assert O.backup_experts(lg, 2, "softmax").tolist() == [[4, 0]]
