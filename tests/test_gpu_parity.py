@@ -441,9 +441,30 @@ def test_route_expert_choice_entry_point(score, T, E, C):
 @pytest.mark.parametrize("reroute", [False, True])
 def test_dispatch_entry_point(T, k, E, C, reroute):
     _announce(f"moe_dispatch T={T} k={k} E={E} C={C} reroute={reroute}")
-    g = torch.Generator().manual_seed(T * 31 + E)
+    _check_dispatch(T, k, E, C, reroute, T * 31 + E, 2.0)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_dispatch_random(seed):
+    """Seeded random (T, k, E, capacity, re-route, skew): slot counts on
+    both sides of the one-block limit (8192), capacities from 1 to none;
+    integer outputs bit-exact against the oracle."""
+    r = np.random.default_rng(3000 + seed)
+    E = int(r.choice([1, 2, 7, 16, 64, 100, 256]))
+    k = int(r.integers(1, min(8, E) + 1))
+    T = int(r.choice([0, 1, 5, 100, 1000, 1023, 1025, 3000, 8192 // k, 8192 // k + 1, 20000]))
+    C = int(r.choice([0, 0, 1, max(1, T * k // E), max(1, (5 * T * k) // (4 * E)), 10 ** 6]))
+    reroute = bool(k < E and C > 0 and r.random() < 0.5)
+    skew = float(r.choice([0.0, 2.0, 20.0]))
+    _announce(f"moe_dispatch random {seed}: T={T} k={k} E={E} C={C} reroute={reroute} "
+              f"skew={skew}")
+    _check_dispatch(T, k, E, C, reroute, 9000 + seed, skew)
+
+
+def _check_dispatch(T, k, E, C, reroute, seed, skew):
+    g = torch.Generator().manual_seed(seed)
     # skewed distinct ids per token; the next choices are the backups
-    pri = torch.rand((T, E), generator=g) * torch.linspace(1.0, 3.0, E)
+    pri = torch.rand((T, E), generator=g) * torch.linspace(1.0, 1.0 + skew, E)
     nb = min(k, E - k) if reroute else 0
     order = torch.topk(pri, k + nb, dim=1).indices.to(torch.int32)
     ids = order[:, :k].contiguous()
