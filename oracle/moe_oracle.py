@@ -102,7 +102,9 @@ R22 Bias update (the load rule of DeepSeek-V3's auxiliary-loss-free
 Parity status: every function here is pinned by the CPU tests (worked examples
 printed on the pages, closed forms, brute force and cross-tier agreement).  The
 bf16 rounding of h (R9) is a reading, pinned only by its own RNE unit test; the
-E4M3 decode (R12) is pinned by closed-form codes and by a library decoder.
+E4M3 decode (R12) is pinned by closed-form codes and by a library decoder, and
+the per-output-channel scale of dequantize_rows by a round trip through the
+library encoder (error within half an E4M3 ulp times the row's scale).
 """
 from __future__ import annotations
 
