@@ -24,6 +24,15 @@
  *     contiguous.  Router Wg[E][d] (logical W_g[d,E] transposed); gate/up
  *     W1,W3[G][F][d] (logical [G,d,F] transposed); down W2[G][d][F] (logical
  *     [G,F,d] transposed).  Activations X[T][d], H[rows][F], Y[T][d].
+ *     A caller that holds the weights in the logical layout of LLM Internals
+ *     14.2.1 step 5 (x[m_i, d] times W_i[d, F], i.e. W1/W3 as [G][d][F], W2
+ *     as [G][F][d], W_g as [d][E]) must transpose each matrix once, when
+ *     the weights are loaded: W1[g].T, W3[g].T, W2[g].T and W_g.T, made
+ *     contiguous.  The reason is the matrix-core operand format: both MFMA
+ *     operands take 8 consecutive K-elements per lane, so with K contiguous
+ *     in memory one 16-byte load per lane feeds a fragment straight from
+ *     global memory through LDS, for the token rows and the weight rows
+ *     alike; the library performs no transposition per call.
  *   - dtype: MOE_BF16 (bf16 storage, fp32 accumulation, fp32 router scores)
  *     or MOE_F32.  Integers are int32.
  *   - Supported shapes: d and F multiples of 128, 1 <= E <= 256, 1 <= k <= E,

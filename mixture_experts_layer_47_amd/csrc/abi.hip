@@ -198,6 +198,10 @@ int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E, int64_t capac
   MOE_REQUIRE(counts && offsets && n_kept, MOE_EINVAL, "NULL counts, offsets or n_kept");
   MOE_REQUIRE(T == 0 || (topk_ids && sorted_slot && slot_row), MOE_EINVAL,
               "NULL topk_ids, sorted_slot or slot_row");
+  // A capacity of T*k or more never drops a slot; clamping it there keeps
+  // every per-expert room and row count inside int32 in the kernels.
+  const int64_t Tk = T * (int64_t)k;
+  if (capacity > Tk) capacity = Tk > 0 ? Tk : 1;
   const bool gather = X_sorted != nullptr;
   if (gather) {
     int rc;
@@ -215,8 +219,7 @@ int moe_dispatch(const int32_t* topk_ids, int64_t T, int k, int E, int64_t capac
     e = launch_reroute(topk_ids, backup_ids, n_backup, T, k, E, capacity, 0, counts, offsets,
                        sorted_slot, slot_row, n_kept, nullptr, (char*)ws + dws, s);
   if (e == hipSuccess && gather)
-    e = launch_gather(X, sorted_slot, n_kept, T * (int64_t)k, k, d, dtype == MOE_BF16 ? 2 : 4,
-                      X_sorted, s);
+    e = launch_gather(X, sorted_slot, n_kept, Tk, k, d, dtype == MOE_BF16 ? 2 : 4, X_sorted, s);
   return hip_status(e, "moe_dispatch");
 }
 
@@ -471,6 +474,10 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
   if (L->capacity_factor > 0) {
     cap = moe_capacity(L->capacity_factor, T, L->k, L->E);
     if (cap < 0) return (int)cap;
+    // C >= T*k never drops a slot: clamped there, the kernels' per-expert
+    // room and row counts stay inside int32
+    const int64_t tk = T * (int64_t)L->k;
+    if (cap > tk) cap = tk > 0 ? tk : 1;
   }
   moe_aux none;
   memset(&none, 0, sizeof(none));

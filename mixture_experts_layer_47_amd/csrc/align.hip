@@ -33,6 +33,11 @@ __device__ __forceinline__ uint64_t match_id(int e, bool valid, int nbits) {
   return valid ? eq : 0ull;
 }
 
+// Only ids in [0, E) take part in a dispatch; a slot holding any other value
+// is left out of the counts and gets row -1 (it contributes nothing), so no
+// index outside the per-expert tables is ever formed.
+__device__ __forceinline__ bool id_ok(int e, int E) { return (unsigned)e < (unsigned)E; }
+
 __device__ __forceinline__ int nbits_for(int E) {
   return E <= 1 ? 0 : 32 - __clz(E - 1);
 }
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void k_align_count(const int32_t* __restrict__
   }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const bool v = ev[g] >= 0;
+    const bool v = id_ok(ev[g], E);
     const int e = v ? ev[g] : 0;
     const uint64_t eq = match_id(e, v, nb);
     if (v && (eq & lt) == 0)                          // lowest lane of its id
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256) void k_align_scatter(
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int64_t s = (int64_t)c * CHUNK + g * 64 + lane;
-    const bool v = ev[g] >= 0;
+    const bool v = id_ok(ev[g], E);
     const int e = v ? ev[g] : 0;
     const uint64_t eq = match_id(e, v, nb);
     int rank = 0;
@@ -194,6 +199,8 @@ __global__ __launch_bounds__(256) void k_align_scatter(
         sorted_slot[row] = (int32_t)s;
         if (row_token) row_token[row] = (int32_t)(s / k);
       }
+    } else if (s < Tk) {
+      slot_row[s] = -1;                               // id outside [0, E)
     }
   }
 }
@@ -206,9 +213,12 @@ __global__ __launch_bounds__(256) void k_align_scatter(
 // placed after the expert's first-pass rows.
 
 // props[s]: the backup expert dropped slot s proposes, or -1.
-__global__ __launch_bounds__(256) void k_rr_props(const int32_t* __restrict__ slot_row,
+// Slots whose own id lies outside [0, E) were never dispatched and propose
+// nothing; a backup outside [0, E) is no proposal.
+__global__ __launch_bounds__(256) void k_rr_props(const int32_t* __restrict__ ids,
+                                                  const int32_t* __restrict__ slot_row,
                                                   const int32_t* __restrict__ backup,
-                                                  int64_t T_, int k, int nb,
+                                                  int64_t T_, int k, int E, int nb,
                                                   int32_t* __restrict__ props) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= T_) return;
@@ -216,8 +226,9 @@ __global__ __launch_bounds__(256) void k_rr_props(const int32_t* __restrict__ sl
   for (int j = 0; j < k; ++j) {
     const int64_t s = t * k + j;
     int p = -1;
-    if (slot_row[s] < 0) {
+    if (slot_row[s] < 0 && id_ok(ids[s], E)) {
       if (m < nb) p = backup[t * nb + m];
+      if (!id_ok(p, E)) p = -1;
       ++m;
     }
     props[s] = p;
@@ -237,13 +248,13 @@ __global__ __launch_bounds__(256) void k_rr_scan(int32_t* __restrict__ hist2, in
   const int e = threadIdx.x;
   if (e < E) {
     const int run = chunk_bases(hist2, E, nchunks, e);
-    const int kept1 = counts[e] < cap ? counts[e] : (int)cap;
-    const int room = (int)cap - kept1;
-    const int acc = run < room ? run : room;
+    const int64_t kept1 = counts[e] < cap ? counts[e] : cap;
+    const int64_t room = cap - kept1;
+    const int acc = run < room ? run : (int)room;
     meta[e] = offsets[e];
-    meta[E + e] = kept1;
+    meta[E + e] = (int)kept1;
     meta[2 * E + e] = acc;
-    tot[e] = kept1 + acc;
+    tot[e] = (int)kept1 + acc;
   }
   __syncthreads();                                // old offsets read before the rewrite
   if (threadIdx.x < 64) wave_offsets(tot, E, tail_rows, offsets, n_kept, nullptr);
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(1024) void k_align_small(
   if (c < nchunks) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const bool v = ev[g] >= 0;
+      const bool v = id_ok(ev[g], E);
       const int e = v ? ev[g] : 0;
       const uint64_t eq = match_id(e, v, nb);
       if (v && (eq & lt) == 0) cnt[e] = cnt[e] + __popcll(eq);
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(1024) void k_align_small(
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int64_t sl = (int64_t)c * CHUNK + g * 64 + lane;
-      const bool v = ev[g] >= 0;
+      const bool v = id_ok(ev[g], E);
       const int e = v ? ev[g] : 0;
       const uint64_t eq = match_id(e, v, nb);
       int rank = 0;
@@ -386,6 +397,8 @@ __global__ __launch_bounds__(1024) void k_align_small(
         const int row = keep ? off[e] + rank : -1;
         slot_row[sl] = row;
         if (keep) s_slot[row] = (int32_t)sl;
+      } else if (sl < Tk) {
+        slot_row[sl] = -1;                            // id outside [0, E)
       }
     }
   }
@@ -492,8 +505,8 @@ hipError_t launch_reroute(const int32_t* ids, const int32_t* backup, int nb, int
   int32_t* hist2 = (int32_t*)p;  p += align256((size_t)nch * E * sizeof(int32_t));
   int32_t* props = (int32_t*)p;  p += align256((size_t)Tk * sizeof(int32_t) + 4);
   int32_t* meta = (int32_t*)p;
-  hipLaunchKernelGGL(k_rr_props, dim3((unsigned)MOE_CEIL_DIV(T, 256)), dim3(256), 0, s, slot_row,
-                     backup, T, k, nb, props);
+  hipLaunchKernelGGL(k_rr_props, dim3((unsigned)MOE_CEIL_DIV(T, 256)), dim3(256), 0, s, ids,
+                     slot_row, backup, T, k, E, nb, props);
   const unsigned nblk = (unsigned)MOE_CEIL_DIV(nch, 4);
   hipLaunchKernelGGL(E <= 64 ? k_align_count<align_chunk_for(64)> : k_align_count<align_chunk_for(65)>,
                      dim3(nblk), dim3(256), 0, s, props, Tk, E, nch, hist2);

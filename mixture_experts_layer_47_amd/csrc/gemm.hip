@@ -73,11 +73,11 @@ constexpr int kThreads = 256;   // four waves per block
 // One K stage, global -> registers.  Thread t owns the 16-B chunk t%8 of
 // rows t/8, t/8 + 32, ... of the A tile and of the B tile.
 template <typename T, int CA, int CB, bool GLU, int BN>
-__device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB], const T* A,
-                                           const uint32_t (&oa)[CA], const T* pb0,
+__device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB],
+                                           const T* const (&pa)[CA], const T* pb0,
                                            const T* pb1, size_t bstep, int k0) {
 #pragma unroll
-  for (int i = 0; i < CA; ++i) ra[i] = *(const u32x4*)(A + oa[i] + k0);
+  for (int i = 0; i < CA; ++i) ra[i] = *(const u32x4*)(pa[i] + k0);
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     constexpr int kSplit = BN / (kThreads / 8);   // first thread-row index in the W3 half
@@ -193,8 +193,8 @@ __device__ __forceinline__ void sched_substep() {
 // multiple of 128 elements), so the loop advances two stages at a time and
 // the staging sets keep fixed names.
 template <typename T, int NV, int BM, int BN, int CA, int CB, int FM, int FN, bool GLU>
-__device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1], const T* Ak,
-                                          const uint32_t (&oa)[CA], const T* pb0, const T* pb1,
+__device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1],
+                                          const T* const (&oa)[CA], const T* pb0, const T* pb1,
                                           size_t bstep, int nk, int fa, int fb,
                                           const int (&cs)[4], int tid) {
   constexpr int NF = FM + FN;
@@ -203,8 +203,8 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
   u32x4* sm0 = smem[0];
   u32x4* sm1 = sm0 + (BM + (GLU ? 2 * BN : BN)) * 8;
   u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
-  gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, Ak, oa, pb0, pb1, bstep, 0);
-  gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, Ak, oa, pb0, pb1, bstep, (nk > 1 ? 1 : 0) * BK);
+  gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, oa, pb0, pb1, bstep, 0);
+  gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, oa, pb0, pb1, bstep, (nk > 1 ? 1 : 0) * BK);
   lstore_tile<BM, CA, CB>(sm0, ra1, rb1, tid);
   __syncthreads();
   u32x4 f0[NF], f1[NF];
@@ -216,8 +216,8 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
       const int k = kt + h;
       const u32x4* sm = h ? sm1 : sm0;
       const int kn = (k + 2 < nk ? k + 2 : nk - 1) * BK;
-      if (h == 0) gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, Ak, oa, pb0, pb1, bstep, kn);
-      else        gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, Ak, oa, pb0, pb1, bstep, kn);
+      if (h == 0) gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, oa, pb0, pb1, bstep, kn);
+      else        gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, oa, pb0, pb1, bstep, kn);
       if constexpr (NV > 0) {
         load_frags<NV, FM, FN, BN, GLU>(f0, sm + fa, sm + fb, cs[0]);
         mma_substep<T, NV, FM, FN>(acc, f1);
@@ -497,19 +497,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
     const T* w0 = ((g == g_last) ? B0_last : B0 + (size_t)g * N * K) + kbeg;
     const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) + kbeg : nullptr;
-    const T* Ak = A + kbeg;
-
-    // per-thread source rows as 32-bit element offsets (operands hold < 2^31
-    // elements).  Rows past the tile's end re-read its first row: their
-    // outputs are never stored, and each output row depends only on its own
-    // A row.
-    uint32_t oa[CA];
+    // per-thread source rows (64-bit addresses: an operand may hold 2^31
+    // elements or more).  Rows past the tile's end re-read its first row:
+    // their outputs are never stored, and each output row depends only on
+    // its own A row.
+    const T* oa[CA];
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int r = (tid >> 3) + i * (NT / 8);
       int src = rbeg + (r < rows ? r : 0);
       if (row_token) src = row_token[src];
-      oa[i] = (uint32_t)src * (uint32_t)K + c16 * EPC;
+      oa[i] = A + (size_t)src * K + kbeg + c16 * EPC;
     }
     const T* pb0 = w0 + (size_t)(n0 + (tid >> 3)) * K + c16 * EPC;
     const T* pb1 = GLU ? w1 + (size_t)(n0 + (tid >> 3)) * K + c16 * EPC : nullptr;
@@ -526,8 +524,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const int nv = min(FM, max(0, (rows - arow0 + 31) >> 5));
     auto* sm2 = reinterpret_cast<u32x4 (*)[1]>(&smem[0][0]);
 #define MOE_MAIN_LOOP(NV_)                                                                   \
-  main_loop<T, NV_, BM, BN, CA, CB, FM, FN, GLU>(acc, sm2, Ak, oa, pb0, pb1, bstep, nk, fa, fb, \
-                                                 cs, tid)
+  main_loop<T, NV_, BM, BN, CA, CB, FM, FN, GLU>(acc, sm2, oa, pb0, pb1, bstep, nk, fa, fb, cs, \
+                                                 tid)
     if (nv >= FM) {
       MOE_MAIN_LOOP(FM);
     } else if (nv == 0) {
@@ -998,11 +996,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   }
 }
 
-// Work list: for each group g (rows clamped to [0, max_rows)), mt_g =
-// ceil(rows_g / BM) M-tiles times NN N-tiles times ksplit K-splits, ordered
-// by group, then K-split, then runs of NG neighbouring N-tiles, then M-tile,
-// then N-tile inside the run.  One block per list: the lists of both
-// projections are built by one launch.
+// Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles times NN
+// N-tiles times ksplit K-splits, ordered by group, then K-split, then runs
+// of NG neighbouring N-tiles, then M-tile, then N-tile inside the run.  One
+// launch builds the lists of both projections.
+//
+// Group g's rows are [a_g, b_g) with the caller's offsets clamped to
+// [0, max_rows] and made non-decreasing by a running maximum (b_g = the
+// largest clamped end up to g, a_g = b_{g-1}), so the groups never overlap
+// and the list never holds more than ceil(max_rows / BM) + G M-tiles per
+// N-tile, whatever the offsets hold.  Block (0, 0) stores these bounds in
+// `clean` [G+1]; the GEMMs read their rows from there.
 struct WorkListArgs {
   int BM, NN, NG, ksplit;
   int2* work;
@@ -1015,25 +1019,44 @@ struct WorkListArgs {
 constexpr int kWorkSlices = 8;
 __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ offsets, int G,
                                                     int max_rows, WorkListArgs l0,
-                                                    WorkListArgs l1) {
+                                                    WorkListArgs l1,
+                                                    int32_t* __restrict__ clean) {
   const WorkListArgs& l = blockIdx.y == 0 ? l0 : l1;
   const int BM = l.BM, NN = l.NN, NG = l.NG, ksplit = l.ksplit;
   int2* __restrict__ work = l.work;
   int32_t* __restrict__ nwork = l.nwork;
   __shared__ int32_t sc[1024];
   __shared__ int32_t mts[1024];
+  __shared__ int32_t bend[1024];
+  __shared__ int32_t wsum[16];
   const int g = threadIdx.x;
+  const int lane = g & 63, wv = g >> 6;
+  // running maximum of the clamped group ends (inclusive max-scan)
+  const int a0 = min(max(offsets[0], 0), max_rows);
+  int be = a0;
+  if (g < G) be = max(a0, min(max(offsets[g + 1], 0), max_rows));
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(be, o);
+    if (lane >= o) be = max(be, y);
+  }
+  if (lane == 63) wsum[wv] = be;
+  __syncthreads();
+  for (int i = 0; i < wv; ++i) be = max(be, wsum[i]);
+  bend[g] = be;
+  __syncthreads();
   int mt = 0;
   if (g < G) {
-    const int a = min(max(offsets[g], 0), max_rows);
-    const int b = min(max(offsets[g + 1], a), max_rows);
-    mt = MOE_CEIL_DIV(b - a, BM);
+    const int a = g == 0 ? a0 : bend[g - 1];
+    mt = MOE_CEIL_DIV(be - a, BM);
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      clean[g] = a;
+      if (g == G - 1) clean[G] = be;
+    }
   }
   mts[g] = mt;
+  __syncthreads();                       // wsum is reused below
   // inclusive scan of the entry counts: in each wave by shuffles, then over
   // the 16 wave totals
-  __shared__ int32_t wsum[16];
-  const int lane = g & 63, wv = g >> 6;
   int v = mt * NN * ksplit;
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(v, o);
@@ -1148,6 +1171,7 @@ size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   size_t b = align256((size_t)max_rows * F * es);                       // H
   b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
   b += align256(2 * sizeof(int32_t));                                  // entry counts
+  b += align256((size_t)(G + 1) * sizeof(int32_t));                    // group bounds
   b += align256((size_t)(ks - 1) * max_rows * d * sizeof(float));       // extra K-split partials
   return b;
 }
@@ -1187,13 +1211,14 @@ static WorkListArgs work_list_args(const GemmArgs& a, int BM, int BN, bool glu) 
 }
 
 // Builds the work list of a (and of b when given: same groups and offsets).
-static void run_work_list(const GemmArgs& a, int BM, int BN, bool glu, hipStream_t s,
-                          const GemmArgs* b = nullptr, int BMb = 0, int BNb = 0,
-                          bool glub = false) {
+// `clean` receives the non-decreasing group bounds both GEMMs then read.
+static void run_work_list(const GemmArgs& a, const int32_t* offsets, int32_t* clean, int BM,
+                          int BN, bool glu, hipStream_t s, const GemmArgs* b = nullptr,
+                          int BMb = 0, int BNb = 0, bool glub = false) {
   const WorkListArgs l0 = work_list_args(a, BM, BN, glu);
   const WorkListArgs l1 = b ? work_list_args(*b, BMb, BNb, glub) : l0;
-  hipLaunchKernelGGL(k_work_list, dim3(kWorkSlices, b ? 2 : 1), dim3(1024), 0, s, a.offsets, a.G,
-                     a.max_rows, l0, l1);
+  hipLaunchKernelGGL(k_work_list, dim3(kWorkSlices, b ? 2 : 1), dim3(1024), 0, s, offsets, a.G,
+                     a.max_rows, l0, l1, clean);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
@@ -1294,17 +1319,19 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   int2* work_up = (int2*)q;  q += align256((size_t)wu * sizeof(int2));
   int2* work_dn = (int2*)q;  q += align256((size_t)wd * sizeof(int2));
   int32_t* nwork = (int32_t*)q; q += align256(2 * sizeof(int32_t));
+  int32_t* bounds = (int32_t*)q; q += align256((size_t)(G + 1) * sizeof(int32_t));
   float* slabs = (float*)q;  // (ks - 1) extra partial slabs of [max_rows][d]
   const int mr = (int)max_rows;
-  GemmArgs up{A,  row_token, offsets, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork,
+  GemmArgs up{A,  row_token, bounds, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork,
               1,  nullptr};
-  GemmArgs dn{H,  nullptr, offsets, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
+  GemmArgs dn{H,  nullptr, bounds, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
               nwork + 1, ks, slabs};
   if (qs) {
     up.sc0 = qs->s1; up.sc1 = qs->s3; up.sc0l = qs->s1l; up.sc1l = qs->s3l;
     dn.sc0 = qs->s2; dn.sc0l = qs->s2l;
   }
-  run_work_list(up, p.BM, up_bn(p.cfg), true, s, &dn, p.BM, down_bn(p.cfg, d), false);
+  run_work_list(up, offsets, bounds, p.BM, up_bn(p.cfg), true, s, &dn, p.BM, down_bn(p.cfg, d),
+                false);
   timing_mark("tile_map", s);
   if (qs) {
     // FP8 weights: the large and medium tiles keep 64-K stages (32 KB of A
@@ -1360,7 +1387,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   if (ks > 1) {
     if (reduce)
       hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)max_rows), dim3(256), 0, s, Yrows, slabs,
-                         offsets, G, mr, d, ks);
+                         bounds, G, mr, d, ks);
     else if (partial2)
       *partial2 = slabs;
   }

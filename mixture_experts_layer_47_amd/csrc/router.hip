@@ -65,9 +65,17 @@ __global__ __launch_bounds__(256) void k_router_logits(
 
 // --------------------------------------------------------------------------
 // Select: one wave per token.  Lane L holds experts L, L+64, L+128, L+192.
+// Key descending, lower id on ties; a NaN key ranks below every number,
+// -inf included (the order of a stable ascending sort of -key).  kNoKey, a
+// NaN, with id kNoId starts every arg-max: any candidate beats it, so a
+// round always ends on a real expert while one is left.
 __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);   // key descending, lower id wins ties
+  const bool na = ka != ka, nb = kb != kb;
+  if (na || nb) return na == nb ? ia < ib : nb;
+  return ka > kb || (ka == kb && ia < ib);
 }
+#define kNoKey __builtin_nan("")
+constexpr int kNoId = 0x7fffffff;
 
 // Wave arg-max of (key, id) over this lane's candidates (already reduced to
 // one per lane): the best key, lower id on ties.
@@ -96,8 +104,8 @@ __device__ __forceinline__ void limit_groups(double (&key)[NE], const double (&a
     uint32_t taken = 0;
     double acc = 0.0;
     for (int r = 0; r < gk; ++r) {
-      double bk = -INFINITY;
-      int bi = 0x7fffffff;
+      double bk = kNoKey;
+      int bi = kNoId;
 #pragma unroll
       for (int i = 0; i < NE; ++i) {
         const int e = lane + 64 * i;
@@ -115,8 +123,8 @@ __device__ __forceinline__ void limit_groups(double (&key)[NE], const double (&a
   uint64_t chosen = 0;
   for (int r = 0; r < topk_group; ++r) {
     const bool cand = lane < n_group && !((chosen >> lane) & 1ull);
-    double bk = cand ? gscore : -INFINITY;
-    int bi = cand ? lane : 0x7fffffff;
+    double bk = cand ? gscore : kNoKey;
+    int bi = cand ? lane : kNoId;
     wave_best(bk, bi);
     chosen |= 1ull << bi;
   }
@@ -230,8 +238,8 @@ __global__ __launch_bounds__(256) void k_router_select(
   int my_id = 0;
   double my_val = 0.0, tot = 0.0;
   for (int j = 0; j < k + nb; ++j) {
-    double bk = -INFINITY;
-    int bi = 0x7fffffff;
+    double bk = kNoKey;
+    int bi = kNoId;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
       const int e = lane + 64 * i;
@@ -245,7 +253,10 @@ __global__ __launch_bounds__(256) void k_router_select(
     for (int i = 0; i < NE; ++i) if (i == oi) mine = s64[i];
     const double val = __shfl(mine, ol);
     if (lane == ol) taken |= 1u << oi;
-    if (lane == j) { my_id = (bk == -INFINITY) ? -1 : bi; my_val = val; }
+    // a top-k pick is always the expert found (k <= E untaken experts
+    // exist), even when its key is -inf or NaN; a backup is -1 unless its
+    // key is above -inf (an expert outside the chosen groups is not one)
+    if (lane == j) { my_id = (j < k || bk > -INFINITY) ? bi : -1; my_val = val; }
     if (j < k) tot += val;                       // fixed order j = 0..k-1
   }
   if (tok_ok && lane < k) {
