@@ -17,12 +17,14 @@
 //   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
 //     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
 //     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
-//   * two kernels share the tile logic.  k_moe_gemm_dma (bf16 and FP8
+//   * three kernels share the tile logic.  k_moe_gemm_dma (bf16 and FP8
 //     prefill, FP8 decode) copies each stage from global memory straight
 //     into LDS rings (global_load_lds), described at the kernel.
 //     k_moe_gemm (bf16 decode, fp32) stages through registers: BK = 128
 //     bytes of K per stage, two LDS stages and two register staging sets,
-//     stage k+2 fetched while stage k+1 is stored to LDS;
+//     stage k+2 fetched while stage k+1 is stored to LDS.  k_moe_down_pp
+//     (the bf16 down projection of large tiles) runs eight waves as two
+//     groups that alternate memory and compute phases (ping-pong);
 //   * in both, a software pipeline over k16 substeps reads each substep's
 //     fragments while the previous substep's MFMAs run; scheduling groups
 //     pin the interleave;
@@ -996,6 +998,178 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   }
 }
 
+// ------------------------------------------------------- ping-pong variant
+// Down projection of the large tiles (experts with hundreds of rows, bf16
+// weights): 256 rows x 256 output columns per block, eight waves in two
+// groups of four (one wave of each group per SIMD).  Group gp owns rows
+// [128 gp, +128), wave wi the columns [64 wi, +64): 4 x 2 accumulator blocks
+// of 32x32 (128 registers), so two waves share a SIMD.
+//
+// The two groups alternate between a memory phase (read the next 32 K of
+// fragments from LDS into registers, issue global->LDS copies, wait) and a
+// compute phase (16 MFMAs from registers only), offset by one phase and
+// separated by block barriers: while one wave of a SIMD feeds the matrix
+// core the other does its loads, so the matrix core never waits on an LDS
+// read.
+//
+// Copies move whole 128-B lines (a stage is 64 K-elements: the address unit
+// spends the same time on a half line as on a full one).  The A and B parts
+// of a stage live in separate rings of 32 KB buffers, 2 for A and 3 for B
+// (160 KB): A(S + 1) is issued in the first memory phase of stage S, B(S + 2)
+// in the second, so the address unit sees an even load and the weight rows
+// get two stages of lead.  Every wave copies 32 A rows and 32 B rows of each
+// stage.  (The same loop with a gate/up epilogue was 16 % faster than the
+// 4-wave kernel on one dense product, but on Mixtral-shaped grouped layers,
+// whose ragged last M-tiles stream a full weight slice for a few rows, it
+// was 7 % slower, so the gate/up projection keeps the 4-wave kernel.)
+struct PPRing {
+  static constexpr int BM = 256, BN = 256;    // token rows, output columns per tile
+  static constexpr int NA = 2, NB = 3;        // ring depths (64-K stages)
+  static constexpr int HS = 256 * 8;          // 16-B slots per 32 KB buffer
+};
+
+// A barrier that no instruction is scheduled across (the compiler may
+// otherwise hoist it past the MFMAs of a compute phase).
+__device__ __forceinline__ void fenced_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// out = Y (fp32), y = A W2^T, N = d; K-split entries write slab ks - 1 of out2.
+__global__ __launch_bounds__(512) void k_moe_down_pp(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const int2* __restrict__ work, const int32_t* __restrict__ nwork,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B0l, int g_last, int K, int N,
+    int max_rows, int ksplit, int round, float* __restrict__ out, float* __restrict__ out2) {
+  using R = PPRing;
+  __shared__ u32x4 la[R::NA * R::HS];
+  __shared__ u32x4 lb[R::NB * R::HS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gp = wave >> 2, wi = wave & 3;
+  // Blocks are dispatched round-robin over the 8 XCDs: in every round of
+  // `round` blocks each XCD takes a contiguous run of the list.
+  const int cx = round >> 3;
+  const int xi = blockIdx.x >> 3;
+  const int t = (xi / cx) * round + (blockIdx.x & 7) * cx + (xi % cx);
+  if (t >= nwork[0]) return;
+  const int2 wk = work[t];
+  const int g = wk.x & 1023;
+  const int n0 = ((wk.x >> 10) & 16383) * R::BN;
+  const int ks = (int)((uint32_t)wk.x >> 24);
+  const int Kc = K / ksplit;
+  const int kbeg = ks * Kc;
+  const int nk = Kc / 64;
+  const int gbeg = min(max(offsets[g], 0), max_rows);
+  const int rbeg = gbeg + wk.y;
+  const int gend = min(max(offsets[g + 1], gbeg), max_rows);
+  const int rows = min(R::BM, gend - rbeg);
+  const uint16_t* w0 = ((g == g_last) ? B0l : B0 + (size_t)g * N * K) + kbeg;
+
+  // This wave's copies: A and B rows wave * 32 + 8 i + lane / 8, chunk
+  // (lane % 8) ^ swz(row) of each 128-B row.  A rows past the tile's end
+  // re-read its first row (their outputs are never stored).
+  const uint16_t *sa[4], *sb[4];
+  int dslot[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + lane / 8;
+    const int c = ((lane % 8) ^ swz(r & 31)) * 8;
+    sa[i] = A + (size_t)(rbeg + (r < rows ? r : 0)) * K + kbeg + c;
+    sb[i] = w0 + (size_t)(n0 + r) * K + c;
+    dslot[i] = (wave * 32 + i * 8) * 8;
+  }
+  auto copy_a = [&](int S) {
+    u32x4* buf = la + (S % R::NA) * R::HS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(sa[i] + S * 64), (void*)(buf + dslot[i]),
+                                       16, 0, 0);
+  };
+  auto copy_b = [&](int S) {
+    u32x4* buf = lb + (S % R::NB) * R::HS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(sb[i] + S * 64), (void*)(buf + dslot[i]),
+                                       16, 0, 0);
+  };
+  // fragments: A rows 128 gp + 32 i + lane % 32, B rows 64 wi + 32 j + lane
+  // % 32; chunk 2 q + lane / 32 of k16 substep q, swizzled
+  const int ra = 128 * gp + (lane & 31);
+  const int rb = 64 * wi + (lane & 31);
+  int csw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) csw[q] = (2 * q + (lane >> 5)) ^ swz(lane & 31);
+  // live 32-row blocks of this wave's 128 rows: the rest skip their MFMAs
+  const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * gp + 31) >> 5)));
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  u32x4 fa[2][4], fb[2][2];
+
+  // prologue: A stage 0, B stages 0 and 1 landed in every wave; then group
+  // 1 falls one phase behind group 0
+  copy_a(0);
+  copy_b(0);
+  if (nk > 1) copy_b(1);
+  wait_vm_lgkm<0>();
+  fenced_barrier();
+  if (gp == 1) fenced_barrier();
+  for (int S = 0; S < nk; ++S) {
+    const u32x4* ba = la + (S % R::NA) * R::HS;
+    const u32x4* bb = lb + (S % R::NB) * R::HS;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // ---- memory phase: fragments of k16 substeps 2 hh, 2 hh + 1
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int cs = csw[2 * hh + q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[q][i] = ba[(ra + 32 * i) * 8 + cs];
+        fb[q][0] = bb[rb * 8 + cs];
+        fb[q][1] = bb[(rb + 32) * 8 + cs];
+      }
+      // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
+      // the B buffer of stage S - 1: both were last read in the previous
+      // phase of the other group, before the barrier that ended it.
+      if (hh == 0) {
+        if (S + 1 < nk) copy_a(S + 1);
+        wait_vm_lgkm<8>();                    // LDS reads done; copies fly on
+      } else if (S + 2 < nk) {
+        copy_b(S + 2);
+        wait_vm_lgkm<4>();                    // all but B(S + 2): stage S + 1 landed
+      } else {
+        wait_vm_lgkm<0>();
+      }
+      fenced_barrier();
+      // ---- compute phase
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nv) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, fb[q][j]), __builtin_bit_cast(bf16x8, fa[q][i]),
+                  acc[i][j], 0, 0, 0);
+          }
+      __builtin_amdgcn_s_setprio(0);
+      fenced_barrier();
+    }
+  }
+  if (gp == 0) fenced_barrier();              // both groups end on the same barrier count
+  store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false>(acc, out, out2, ks, max_rows, N, rbeg, rows,
+                                                     128 * gp, n0, wi, lane);
+}
+
 // Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles times NN
 // N-tiles times ksplit K-splits, ordered by group, then K-split, then runs
 // of NG neighbouring N-tiles, then M-tile, then N-tile inside the run.  One
@@ -1232,6 +1406,15 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
+static void run_down_pp(const GemmArgs& a, hipStream_t s) {
+  const int64_t ub = max_work(a.max_rows, a.G, PPRing::BM, a.N, PPRing::BN, a.ksplit);
+  const int round = num_cus() & ~7;
+  const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
+  hipLaunchKernelGGL(k_moe_down_pp, dim3((unsigned)nb), dim3(512), 0, s, (const uint16_t*)a.A,
+                     a.offsets, a.work, a.nwork, (const uint16_t*)a.B0, (const uint16_t*)a.B0l,
+                     a.g_last, a.K, a.N, a.max_rows, a.ksplit, round, (float*)a.out, a.out2);
+}
+
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
           int NBB = NBUF, bool DENSE = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
@@ -1368,7 +1551,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
+        if (b256) run_down_pp(dn, s);
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
         break;
       case 1:
