@@ -318,6 +318,26 @@ size_t moe_forward_workspace_size(const moe_layer* L, int64_t T);
 int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y,
                 const moe_aux* aux, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ forward, no allocation --
+ * For callers that cannot allocate device memory or call hipMalloc (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * moe_forward with its workspace taken from a fixed array of
+ * moe_forward_noalloc_max_bytes() = 64 MiB that the library holds in device
+ * memory, one per GPU, until the process ends.  The caller still passes X,
+ * Y and the optional moe_aux outputs.  A layer and batch whose
+ * moe_forward_workspace_size() exceeds that size is rejected with
+ * MOE_EWORKSPACE before anything is launched (decode-sized batches fit;
+ * large prefill batches use moe_forward with a workspace).  Nothing is
+ * allocated or freed; the array's device address is looked up once per
+ * device.  All calls on one GPU share the array and it keeps the last
+ * call's contents (every buffer the forward reads is written by the same
+ * call first), so calls that overlap on one GPU, on different streams or
+ * threads, race: serialise them.  Results are bit-identical to
+ * moe_forward's. */
+size_t moe_forward_noalloc_max_bytes(void);
+int moe_forward_noalloc(const moe_layer* L, const void* X, int64_t T, void* Y,
+                        const moe_aux* aux, void* stream);
+
 /* ------------------------------------------------------------- timing --
  * Optional event timing of moe_forward's phases, for benchmarks.
  * moe_timing_enable(n): n > 0 creates a pool of n HIP events (runtime

@@ -29,7 +29,7 @@ EXPORTS = ("moe_last_error", "moe_capacity", "moe_route_workspace_size", "moe_ro
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_fp8",
            "moe_combine", "moe_bias_update",
            "moe_balance", "moe_forward_workspace_size", "moe_forward", "moe_timing_enable",
-           "moe_timing_read")
+           "moe_timing_read", "moe_forward_noalloc_max_bytes", "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +85,9 @@ def _declare(L):
         "moe_forward_workspace_size": (SZ, [ctypes.POINTER(MoeLayerC), I64]),
         "moe_forward": (I, [ctypes.POINTER(MoeLayerC), P, I64, P, ctypes.POINTER(MoeAuxC), P,
                             SZ, P]),
+        "moe_forward_noalloc_max_bytes": (SZ, []),
+        "moe_forward_noalloc": (I, [ctypes.POINTER(MoeLayerC), P, I64, P, ctypes.POINTER(MoeAuxC),
+                                    P]),
         "moe_timing_enable": (I, [I]),
         "moe_timing_read": (I, [ctypes.c_char_p, I, ctypes.POINTER(ctypes.c_float), I]),
     }
@@ -381,6 +384,14 @@ class Forward:
         _check(lib().moe_forward(ctypes.byref(self.cl), _ptr(self.X), self.T, _ptr(self.Y),
                                  ctypes.byref(self.caux), _ptr(self.ws), self.ws.numel(),
                                  _stream(self.X.device)))
+        return self.Y
+
+    def noalloc(self):
+        """The same forward through moe_forward_noalloc: the library's own
+        static scratch array instead of this object's workspace."""
+        _check(lib().moe_forward_noalloc(ctypes.byref(self.cl), _ptr(self.X), self.T,
+                                         _ptr(self.Y), ctypes.byref(self.caux),
+                                         _stream(self.X.device)))
         return self.Y
 
 

@@ -1,6 +1,7 @@
 // C-ABI entry points: host-side validation, workspace carving, launches.
 // Nothing here allocates, frees or synchronises device memory.
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -536,6 +537,61 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
     e = launch_router_health(counts, nkept, ent, T, L->k, L->E, a.health, s);
   timing_mark("aux", s);
   return hip_status(e, "moe_forward");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- forward without allocation
+// moe_forward's workspace taken from a fixed device array instead of the
+// caller: for callers that cannot allocate.  Every GPU the library runs on
+// holds its own copy of `scratch` until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// symbol): the device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch.
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on
+// each device); MOE_OK or a negative status with the message set.
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_EUNSUPPORTED,
+              "device %d beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    MOE_REQUIRE(p != nullptr, MOE_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t moe_forward_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int moe_forward_noalloc(const moe_layer* L, const void* X, int64_t T, void* Y,
+                        const moe_aux* aux, void* stream) {
+  int rc;
+  if ((rc = check_layer(L, T))) return rc;
+  const size_t need = fwd_layout(L, T).total;
+  MOE_REQUIRE(need <= kScratchBytes, MOE_EWORKSPACE,
+              "this layer and batch need %zu bytes of scratch, more than the %zu bytes "
+              "moe_forward_noalloc holds; call moe_forward with a caller workspace",
+              need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws))) return rc;
+  return moe_forward(L, X, T, Y, aux, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

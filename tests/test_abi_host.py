@@ -57,6 +57,22 @@ def test_workspace_sizes_positive(L):
     assert L.moe_forward_workspace_size(ctypes.byref(lay), 4096) > (32768 + 4096) * 7168 * 4
 
 
+def test_forward_noalloc_rejects_oversize_on_host(L):
+    """moe_forward_noalloc checks the workspace need against its fixed array
+    on the host: a batch that does not fit is rejected with MOE_EWORKSPACE
+    before any device call (the pointers here are never dereferenced)."""
+    cap = L.moe_forward_noalloc_max_bytes()
+    assert cap == 64 << 20
+    lay = _lib.MoeLayerC(1, 0, 1, 4096, 8, 2, 14336, 0, 0.0, 1, None, None, 1, 1, 1)
+    T = 4096
+    assert L.moe_forward_workspace_size(ctypes.byref(lay), T) > cap
+    rc = L.moe_forward_noalloc(ctypes.byref(lay), 1, T, 1, None, None)
+    assert rc == -3 and "moe_forward_noalloc" in _lib.last_error()
+    # invalid layers are rejected by the same checks as moe_forward
+    bad = _lib.MoeLayerC(1, 0, 1, 4096, 8, 9, 14336, 0, 0.0, 1, None, None, 1, 1, 1)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), 1, 4, 1, None, None) == -1
+
+
 def test_down_projection_split_decision(L):
     """Long-reduction, few-tile shapes split the down projection along K; the
     workspace then carries one extra fp32 partial slab of [max_rows][d]."""
