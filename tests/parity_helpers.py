@@ -19,11 +19,22 @@ def np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def e4m3_table():
+    """The oracle's value of each of the 256 E4M3 codes."""
+    return O.decode_e4m3(np.arange(256))
+
+
 def weights64(t, scale=None):
-    """Storage-layout weights as float64; E4M3 codes (uint8) are decoded by
-    the oracle and multiplied by their per-row scales."""
+    """Storage-layout weights as float64.  E4M3 codes (uint8) become
+    O.dequantize_rows(codes, scale) = value(code) * scale of their row,
+    evaluated as a lookup in the oracle's table of the 256 code values
+    followed by one fp64 multiply (the same numbers; pinned against
+    O.dequantize_rows in the CPU tests).  The lookup runs where the codes
+    live, so full-size expert matrices decode in milliseconds."""
     if t.dtype == torch.uint8:
-        return O.dequantize_rows(t.cpu().numpy(), scale.detach().cpu().numpy())
+        lut = torch.as_tensor(e4m3_table(), dtype=torch.float64, device=t.device)
+        w = lut[t.long()] * scale.detach().to(torch.float64).unsqueeze(-1)
+        return w.cpu().numpy()
     return np64(t)
 
 

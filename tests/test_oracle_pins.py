@@ -858,3 +858,19 @@ def test_reroute_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_backup_experts_follow_the_key_order()
     monkeypatch.setattr(O, "backup_experts", bko)
+
+
+def test_table_dequantization_equals_oracle():
+    """The parity helpers decode E4M3 weights through a table of the
+    oracle's 256 code values; that must equal O.dequantize_rows exactly,
+    NaN codes included."""
+    import torch
+    from tests import parity_helpers as H
+    rng = np.random.default_rng(17)
+    codes = rng.integers(0, 256, size=(3, 40, 96)).astype(np.uint8)
+    scale = rng.uniform(1e-3, 10.0, size=(3, 40))
+    ref = O.dequantize_rows(codes, scale)
+    got = H.weights64(torch.from_numpy(codes), torch.from_numpy(scale))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
