@@ -12,31 +12,46 @@
 namespace moe {
 
 // KS: a second fp32 slab (the down projection's second K-split) is present.
-template <typename OutT, bool KS>
+// A block of 512 threads serves 512 / TPT tokens, TPT threads each (TPT a
+// multiple of 64 and at least k): narrow rows pack several tokens into a
+// block, so blocks stay large enough that their launch cost does not
+// dominate (8192 tokens of 2048 columns: 2048 blocks instead of 8192).
+template <typename OutT, bool KS, int TPT>
 __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows,
                                                  const float* __restrict__ Yrows2,
                                                  const int32_t* __restrict__ slot_row,
-                                                 const float* __restrict__ w, int k, int d,
-                                                 const float* __restrict__ shared,
+                                                 const float* __restrict__ w, int64_t T_, int k,
+                                                 int d, const float* __restrict__ shared,
                                                  const int32_t* __restrict__ shared_row0,
                                                  OutT* __restrict__ Y) {
-  const int t = blockIdx.x;
+  static_assert(TPT % 64 == 0 && TPT <= 512, "whole waves per token");
+  constexpr int NTB = 512 / TPT;              // tokens per block
+  constexpr int WPT = TPT / 64;               // waves per token
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ int32_t rows[256];
-  __shared__ float gw[256];
+  const int grp = threadIdx.x / TPT, lt = threadIdx.x % TPT;
+  const int64_t t = (int64_t)blockIdx.x * NTB + grp;
+  const bool tok = t < T_;
+  __shared__ int32_t rows_[NTB][TPT];
+  __shared__ float gw_[NTB][TPT];
   __shared__ int nw[8];
+  int32_t* rows = rows_[grp];
+  float* gw = gw_[grp];
+  // compact this token's kept slots in slot order (k <= TPT: one slot per thread)
   int32_t r = -1;
   float g = 0.f;
-  if (threadIdx.x < (unsigned)k) {
-    r = slot_row[(size_t)t * k + threadIdx.x];
-    g = w[(size_t)t * k + threadIdx.x];
+  if (tok && lt < k) {
+    r = slot_row[t * k + lt];
+    g = w[t * k + lt];
   }
   const uint64_t kept = __ballot(r >= 0);
   if (lane == 0) nw[wave] = __popcll(kept);
   __syncthreads();
-  int at = 0;
-  for (int i = 0; i < wave; ++i) at += nw[i];
-  const int n = ((nw[0] + nw[1]) + (nw[2] + nw[3])) + ((nw[4] + nw[5]) + (nw[6] + nw[7]));
+  const int w0 = grp * WPT;
+  int at = 0, n = 0;
+  for (int i = 0; i < WPT; ++i) {
+    if (w0 + i < wave) at += nw[w0 + i];
+    n += nw[w0 + i];
+  }
   if (r >= 0) {
     const uint64_t below = lane ? (kept & (~0ull >> (64 - lane))) : 0ull;
     at += __popcll(below);
@@ -44,6 +59,7 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
     gw[at] = g;
   }
   __syncthreads();
+  if (!tok) return;                           // no block barrier below
   const float* sh = nullptr;
   const float* sh2 = nullptr;
   if (shared) {
@@ -55,15 +71,15 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
   // Expert row j of this column chunk (K-split partials summed first, in
   // split order).
   auto row_val = [&](int j, int c) {
-    const int r = rows[j];
-    float4 y = *(const float4*)(Yrows + (size_t)r * d + c);
+    const int rr = rows[j];
+    float4 y = *(const float4*)(Yrows + (size_t)rr * d + c);
     if constexpr (KS) {
-      const float4 y2 = *(const float4*)(Yrows2 + (size_t)r * d + c);
+      const float4 y2 = *(const float4*)(Yrows2 + (size_t)rr * d + c);
       y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
     }
     return y;
   };
-  for (int c = threadIdx.x * 4; c < d; c += 512 * 4) {
+  for (int c = lt * 4; c < d; c += TPT * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int j = 0;
     // four rows' loads in flight at once; the sum still runs j = 0, 1, ...
@@ -115,25 +131,52 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
   }
 }
 
+// Threads per token: about 16 columns per thread (four 16-B row loads in
+// flight per pass), rounded up to a power of two in [64, 512], and at
+// least k rounded up to whole waves.
+static int combine_tpt(int64_t k, int d) {
+  int tpt = 64;
+  while (tpt < 512 && tpt * 16 < d) tpt *= 2;
+  while (tpt < 512 && tpt < k) tpt *= 2;
+  return tpt;
+}
+
+template <typename OutT, bool KS>
+static void run_combine(int tpt, const float* Yrows, const float* Yrows2, const int32_t* slot_row,
+                        const float* w, int64_t T, int k, int d, const float* shared,
+                        const int32_t* shared_row0, OutT* Y, hipStream_t s) {
+  const unsigned nb = (unsigned)MOE_CEIL_DIV(T, 512 / tpt);
+#define MOE_COMBINE(TPT_)                                                                      \
+  hipLaunchKernelGGL((k_combine<OutT, KS, TPT_>), dim3(nb), dim3(512), 0, s, Yrows, Yrows2,  \
+                     slot_row, w, T, k, d, shared, shared_row0, Y)
+  switch (tpt) {
+    case 64: MOE_COMBINE(64); break;
+    case 128: MOE_COMBINE(128); break;
+    case 256: MOE_COMBINE(256); break;
+    default: MOE_COMBINE(512); break;
+  }
+#undef MOE_COMBINE
+}
+
 hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t* slot_row,
                           const float* w, int64_t T, int k, int d, const float* shared,
                           const int32_t* shared_row0, void* Y, int dtype, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)T), block(512);
+  const int tpt = combine_tpt(k, d);
   if (dtype == MOE_BF16) {
     if (Yrows2)
-      hipLaunchKernelGGL((k_combine<uint16_t, true>), grid, block, 0, s, Yrows, Yrows2, slot_row, w,
-                         k, d, shared, shared_row0, (uint16_t*)Y);
+      run_combine<uint16_t, true>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
+                                  (uint16_t*)Y, s);
     else
-      hipLaunchKernelGGL((k_combine<uint16_t, false>), grid, block, 0, s, Yrows, Yrows2, slot_row,
-                         w, k, d, shared, shared_row0, (uint16_t*)Y);
+      run_combine<uint16_t, false>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
+                                   (uint16_t*)Y, s);
   } else {
     if (Yrows2)
-      hipLaunchKernelGGL((k_combine<float, true>), grid, block, 0, s, Yrows, Yrows2, slot_row, w, k,
-                         d, shared, shared_row0, (float*)Y);
+      run_combine<float, true>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
+                               (float*)Y, s);
     else
-      hipLaunchKernelGGL((k_combine<float, false>), grid, block, 0, s, Yrows, Yrows2, slot_row, w,
-                         k, d, shared, shared_row0, (float*)Y);
+      run_combine<float, false>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
+                                (float*)Y, s);
   }
   return hipGetLastError();
 }

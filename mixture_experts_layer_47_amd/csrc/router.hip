@@ -180,20 +180,18 @@ __device__ __forceinline__ void gather_logits(float (&l)[NE], const float* __res
   }
 }
 
+// One token's scores, top-k and gates, by one wave (lane L holds experts
+// L, L + 64, ...): l are the logits (-inf past E or past T), p receives the
+// full-row probability (softmax p, or the sigmoid s) for the balance and
+// entropy statistics; ids, gates and backups are written for a real token.
 template <int NE>
-__global__ __launch_bounds__(256) void k_router_select(
-    const float* __restrict__ part, int nsplit, int T_, int E,
-    const float* __restrict__ offset, const float* __restrict__ bias, int score,
-    int k, int renorm, int n_group, int topk_group, float* __restrict__ logits,
-    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part,
-    float* __restrict__ ent_part, int nb, int32_t* __restrict__ backup) {
-  __shared__ float sp[4][NE * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  const bool tok_ok = t < T_;
-  float l[NE], p[NE];
+__device__ __forceinline__ void route_token(const float (&l)[NE], float (&p)[NE], int t,
+                                            bool tok_ok, int lane, int E,
+                                            const float* __restrict__ bias, int score, int k,
+                                            int renorm, int n_group, int topk_group,
+                                            int32_t* __restrict__ ids, float* __restrict__ wts,
+                                            int nb, int32_t* __restrict__ backup) {
   double key[NE], s64[NE];
-  gather_logits<NE>(l, part, nsplit, T_, E, t, tok_ok, lane, offset, logits);
   double aff[NE];                        // group scores' affinities (fp64)
   if (score == MOE_SOFTMAX) {
     float m = -INFINITY;
@@ -264,21 +262,48 @@ __global__ __launch_bounds__(256) void k_router_select(
     wts[(size_t)t * k + lane] = (float)(renorm ? my_val / tot : my_val);
   }
   if (tok_ok && lane >= k && lane < k + nb) backup[(size_t)t * nb + lane - k] = my_id;
+}
+
+// Routing entropy of one token, -sum q ln q in fp32 with q = p (softmax) or
+// s / sum(s) (sigmoid); wave-reduced, every lane holds it.
+template <int NE>
+__device__ __forceinline__ float token_entropy(const float (&p)[NE], int score) {
+  float zs = 0.f;
+  if (score != MOE_SOFTMAX) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) zs += p[i];
+    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
+  }
+  float h = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const float q = score == MOE_SOFTMAX ? p[i] : (zs > 0.f ? p[i] / zs : 0.f);
+    if (q > 0.f) h -= q * logf(q);
+  }
+  for (int o = 32; o > 0; o >>= 1) h += __shfl_xor(h, o);
+  return h;
+}
+
+// Select from split-K logit partials: one wave per token, four tokens per
+// block; per-block partials of the entropy and of sum_t p[t][e] in a fixed
+// order (token 0 + 1, + 2, + 3).
+template <int NE>
+__global__ __launch_bounds__(256) void k_router_select(
+    const float* __restrict__ part, int nsplit, int T_, int E,
+    const float* __restrict__ offset, const float* __restrict__ bias, int score,
+    int k, int renorm, int n_group, int topk_group, float* __restrict__ logits,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part,
+    float* __restrict__ ent_part, int nb, int32_t* __restrict__ backup) {
+  __shared__ float sp[4][NE * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool tok_ok = t < T_;
+  float l[NE], p[NE];
+  gather_logits<NE>(l, part, nsplit, T_, E, t, tok_ok, lane, offset, logits);
+  route_token<NE>(l, p, t, tok_ok, lane, E, bias, score, k, renorm, n_group, topk_group, ids,
+                  wts, nb, backup);
   if (ent_part) {  // per-block partial of the tokens' routing entropies
-    // q = p, or s / sum(s) for a sigmoid router; -sum q ln q in fp32
-    float zs = 0.f;
-    if (score != MOE_SOFTMAX) {
-#pragma unroll
-      for (int i = 0; i < NE; ++i) zs += p[i];
-      for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
-    }
-    float h = 0.f;
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const float q = score == MOE_SOFTMAX ? p[i] : (zs > 0.f ? p[i] / zs : 0.f);
-      if (q > 0.f) h -= q * logf(q);
-    }
-    for (int o = 32; o > 0; o >>= 1) h += __shfl_xor(h, o);
+    const float h = token_entropy<NE>(p, score);
     __shared__ float eh[4];
     if (lane == 0) eh[wave] = tok_ok ? h : 0.f;
     __syncthreads();
@@ -291,6 +316,101 @@ __global__ __launch_bounds__(256) void k_router_select(
     for (int e = threadIdx.x; e < E; e += 256)
       ps_part[(size_t)blockIdx.x * E + e] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
   }
+}
+
+// Fused router for up to 32 experts and many tokens: a block of 16 waves
+// computes the logits of 16 tokens over the whole of d into LDS (16x16
+// MFMA blocks; the waves split over the 16-expert blocks, then over K, and
+// the K parts are added in K order), then every wave routes one token
+// exactly as k_router_select does.  The per-four-token partials (entropy,
+// sum of p) have k_router_select's layout and summation order, so the
+// statistics kernels read them unchanged.  No split-K partials go through
+// global memory and one launch is saved.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_router_fused(
+    const T* __restrict__ X, const T* __restrict__ Wg, int T_, int d, int E,
+    const float* __restrict__ offset, const float* __restrict__ bias, int score, int k,
+    int renorm, int n_group, int topk_group, float* __restrict__ logits,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ ps_part,
+    float* __restrict__ ent_part, int nb, int32_t* __restrict__ backup) {
+  __shared__ float part[16][16][65];        // [K part][token][expert]
+  __shared__ float sp[16][64];              // p of each wave's token
+  __shared__ float eh[16];                  // entropy of each wave's token
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16;
+  const int nexb = (E + 15) / 16;           // 16-expert blocks (1..4)
+  const int wpb = 16 / nexb;                // waves per expert block: K parts
+  const int eb = wave % nexb, kq = wave / nexb;
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int KSTEP = EPL * 4;
+  if (kq < wpb) {
+    const int dq = MOE_CEIL_DIV(MOE_CEIL_DIV(d, wpb), KSTEP) * KSTEP;
+    const int kb = min(kq * dq, d), ke = min(kb + dq, d);
+    const int row = lane & 15, grp = lane >> 4;
+    const int tok = t0 + row, ex = eb * 16 + row;
+    const bool tv = tok < T_, ev = ex < E;
+    const T* xa = X + (size_t)(tv ? tok : 0) * d;
+    const T* wb = Wg + (size_t)(ev ? ex : 0) * d;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+    for (int kk0 = kb; kk0 < ke; kk0 += KSTEP) {
+      const int kk = kk0 + grp * EPL;
+      u32x4 a = tv ? *(const u32x4*)(xa + kk) : zero;
+      u32x4 b = ev ? *(const u32x4*)(wb + kk) : zero;
+      if constexpr (sizeof(T) == 2) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0,
+                                                       0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]),
+                                                     acc, 0, 0, 0);
+      }
+    }
+    // C layout: lane holds expert column lane & 15, tokens 4 (lane >> 4) + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[kq][grp * 4 + r][eb * 16 + (lane & 15)] = acc[r];
+  }
+  __syncthreads();
+  const int t = t0 + wave;                  // this wave's token
+  const bool tok_ok = t < T_;
+  const bool ok = tok_ok && lane < E;
+  float v = 0.f;
+  if (ok) {
+    for (int q = 0; q < wpb; ++q) v += part[q][wave][lane];   // K order
+    if (offset) v += offset[lane];
+    if (logits) logits[(size_t)t * E + lane] = v;
+  }
+  float l[1] = {ok ? v : -INFINITY}, p[1];
+  route_token<1>(l, p, t, tok_ok, lane, E, bias, score, k, renorm, n_group, topk_group, ids, wts,
+                 nb, backup);
+  float h = 0.f;
+  if (ent_part) h = token_entropy<1>(p, score);
+  if (lane == 0) eh[wave] = tok_ok ? h : 0.f;
+  sp[wave][lane] = tok_ok ? p[0] : 0.f;
+  __syncthreads();
+  // wave g < 4 writes the partials of tokens 4 g .. 4 g + 3 of the block
+  if (wave < 4) {
+    const int blk4 = blockIdx.x * 4 + wave;
+    if ((int64_t)blk4 * 4 < T_) {
+      const int w4 = wave * 4;
+      if (ent_part && lane == 0)
+        ent_part[blk4] = ((eh[w4] + eh[w4 + 1]) + eh[w4 + 2]) + eh[w4 + 3];
+      if (ps_part && lane < E)
+        ps_part[(size_t)blk4 * E + lane] =
+            ((sp[w4][lane] + sp[w4 + 1][lane]) + sp[w4 + 2][lane]) + sp[w4 + 3][lane];
+    }
+  }
+}
+
+// Up to 32 experts: each block then re-reads at most 32 rows of W_g (from
+// L2).  With 64 experts the per-block W_g traffic was the larger cost
+// (Switch-shaped router 22 -> 39 us), and the tiled router GEMM, which
+// shares W_g across 128-token tiles, stays faster.
+bool router_fused_ok(int64_t T, int d, int E) {
+  return E <= 32 && T >= 2048 && d % 128 == 0 && T <= INT32_MAX;
 }
 
 // Final prob_sum: one block per expert, fixed-order tree over block partials.
@@ -620,13 +740,32 @@ hipError_t launch_route(const void* X, int dtype, int64_t T, int d, const void* 
     if (prob_sum) return launch_zero_f32(prob_sum, E, s);
     return hipSuccess;
   }
+  const int nblk = (int)MOE_CEIL_DIV(T, 4);
+  if (router_fused_ok(T, d, E)) {
+    // logits and selection in one launch; the per-four-token partials go to
+    // the same workspace region as on the split-K path
+    const int split = router_split(T, d, E, dtype);
+    float* ps_part = (float*)((char*)ws + align256((size_t)split * T * E * sizeof(float)));
+    float* psp = prob_sum ? ps_part : nullptr;
+    const dim3 grid((unsigned)MOE_CEIL_DIV(T, 16));
+    if (dtype == MOE_BF16)
+      hipLaunchKernelGGL(k_router_fused<uint16_t>, grid, dim3(1024), 0, s, (const uint16_t*)X,
+                         (const uint16_t*)Wg, (int)T, d, E, offset, bias, score, k, renorm,
+                         n_group, topk_group, logits, ids, w, psp, ent_part, n_backup, backup);
+    else
+      hipLaunchKernelGGL(k_router_fused<float>, grid, dim3(1024), 0, s, (const float*)X,
+                         (const float*)Wg, (int)T, d, E, offset, bias, score, k, renorm,
+                         n_group, topk_group, logits, ids, w, psp, ent_part, n_backup, backup);
+    if (prob_sum)
+      hipLaunchKernelGGL(k_prob_sum, dim3(E), dim3(256), 0, s, ps_part, nblk, E, prob_sum);
+    return hipGetLastError();
+  }
   float* part;
   int split;
   char* rest;
   hipError_t err = launch_logit_partials(X, dtype, T, d, Wg, E, ws, s, &part, &split, &rest);
   if (err != hipSuccess) return err;
   float* ps_part = (float*)rest;
-  const int nblk = (int)MOE_CEIL_DIV(T, 4);
   float* psp = prob_sum ? ps_part : nullptr;
   const int ne = MOE_CEIL_DIV(E, 64);
 #define MOE_SEL(NE_)                                                                 \

@@ -401,6 +401,58 @@ def test_route_entry_point(score, ng, tg):
             assert np.allclose(kg, kr, atol=H.SIGMOID_TIE, rtol=0), t
 
 
+@pytest.mark.parametrize("score,E,ng,tg,dtype", [("softmax", 8, 1, 1, "bf16"),
+                                                  ("softmax", 32, 1, 1, "bf16"),
+                                                  ("sigmoid", 32, 8, 4, "bf16"),
+                                                  ("sigmoid", 20, 1, 1, "bf16"),
+                                                  ("softmax", 64, 1, 1, "bf16"),
+                                                  ("softmax", 16, 4, 2, "f32"),
+                                                  ("sigmoid", 24, 1, 1, "f32")])
+def test_route_many_tokens_entry_point(score, E, ng, tg, dtype):
+    """moe_route with 2000+ tokens (up to 32 experts: logits and selection
+    in one fused launch; 64: the split-K path): logits, ids, gates,
+    backups and the probability sums against the oracle."""
+    T, k = 2345, min(4, E // 2)
+    w = Workload("route_many", T=T, d=512, E=E, k=k, F=128, score=score, dtype=dtype,
+                 bias_std=0.01 if score == "sigmoid" else None, zipf_s=1.2, seed=E + T)
+    _announce(f"moe_route T={T} E={E} {score} n_group={ng} topk_group={tg} {dtype}")
+    inp = make_inputs(w, DEV)
+    nb = min(k, E - k)
+    r = moe.route(inp["X"], inp["Wg"], k, score, True, bias=inp["bias"], offset=inp["offset"],
+                  n_group=ng, topk_group=tg, n_backup=nb)
+    torch.cuda.synchronize()
+    L = H.logical(inp)
+    lg = H.np64(r["logits"])
+    H.check_logits(lg, O.router_logits(L["X"], L["Wg"], L["offset"]))
+    ids, g, p = O.route(lg, k, score, True, L["bias"], ng, tg)
+    _, keys = O.select_topk(lg, k, score, L["bias"], ng, tg)
+    H.check_ids(H.np64(r["ids"]).astype(np.int64), ids, keys if score == "sigmoid" else None)
+    H.check_gates(H.np64(r["w"]), O.gates(lg, H.np64(r["ids"]).astype(np.int64), score, True))
+    assert np.allclose(H.np64(r["prob_sum"]), p.sum(axis=0), rtol=1e-5, atol=1e-4)
+    bk_ref = O.backup_experts(lg, k, score, L["bias"], ng, tg)
+    bk = H.np64(r["backup"]).astype(np.int64)
+    bad = np.flatnonzero((bk != bk_ref).any(axis=1))
+    for t in bad:        # only near-ties may order differently
+        kg = np.where(bk[t] >= 0, keys[t, np.maximum(bk[t], 0)], -np.inf)
+        kr = np.where(bk_ref[t] >= 0, keys[t, np.maximum(bk_ref[t], 0)], -np.inf)
+        assert np.allclose(kg, kr, atol=H.SIGMOID_TIE, rtol=0), t
+    if score == "softmax":
+        assert bad.size == 0
+
+
+@pytest.mark.parametrize("score,E,k,cf,reroute", [("softmax", 16, 2, 1.25, True),
+                                                   ("sigmoid", 32, 6, None, False)])
+def test_forward_many_tokens(score, E, k, cf, reroute):
+    """A whole layer with 2100 tokens and at most 32 experts, so the router
+    runs its fused launch: every step, the balance statistic and the router
+    health against the oracle."""
+    w = Workload("fwd_many", T=2100, d=256, E=E, k=k, F=256, score=score, cf=cf,
+                 reroute=reroute, bias_std=0.01 if score == "sigmoid" else None,
+                 n_shared=1 if score == "sigmoid" else 0, zipf_s=1.2 if cf else None, seed=E)
+    _announce(f"forward many tokens {score} E={E} k={k} cf={cf} reroute={reroute}")
+    _full_check(make_inputs(w, DEV))
+
+
 @pytest.mark.parametrize("score,T,E,C", [("softmax", 333, 32, 40), ("sigmoid", 333, 32, 40),
                                          ("softmax", 100, 8, 100), ("softmax", 100, 8, 150),
                                          ("sigmoid", 50, 256, 3), ("softmax", 1, 4, 1),
