@@ -97,6 +97,19 @@ __device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB],
 // distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
+// Height of the M-tiles of a group of n rows: ceil(n / BM) tiles of equal
+// height rounded up to whole 32-row blocks (the last tile takes the rest).
+// A group slightly larger than a multiple of BM then gets a few slightly
+// shorter tiles instead of full tiles plus one of a handful of rows, which
+// would cost nearly a full tile's copies.  Every tile holds at least one
+// row: n > (ceil(n / BM) - 1) BM >= (ceil(n / BM) - 1) height.
+__host__ __device__ __forceinline__ int tile_height(int n, int BM) {
+  if (n <= BM) return BM;
+  const int mt = (n + BM - 1) / BM;
+  const int h = ((n + mt - 1) / mt + 31) & ~31;
+  return h < BM ? h : BM;
+}
+
 // Registers -> one LDS stage.  Rows r and r + 32 i share swz(r).
 template <int BM, int CA, int CB>
 __device__ __forceinline__ void lstore_tile(u32x4* sm, const u32x4 (&ra)[CA],
@@ -496,7 +509,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const int kbeg = ks * Kc;
     const int gbeg = min(max(offsets[g], 0), max_rows);
     const int rbeg = gbeg + wi.y;
-    const int rows = min(BM, min(max(offsets[g + 1], gbeg), max_rows) - rbeg);
+    const int gend = min(max(offsets[g + 1], gbeg), max_rows);
+    const int rows = min(tile_height(gend - gbeg, BM), gend - rbeg);
     const T* w0 = ((g == g_last) ? B0_last : B0 + (size_t)g * N * K) + kbeg;
     const T* w1 = GLU ? ((g == g_last) ? B1_last : B1 + (size_t)g * N * K) + kbeg : nullptr;
     // per-thread source rows (64-bit addresses: an operand may hold 2^31
@@ -884,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   const int gbeg = DENSE ? 0 : min(max(offsets[g], 0), max_rows);
   const int rbeg = gbeg + wi.y;
   const int gend = DENSE ? max_rows : min(max(offsets[g + 1], gbeg), max_rows);
-  const int rows = min(BM, gend - rbeg);
+  const int rows = min(DENSE ? BM : tile_height(gend - gbeg, BM), gend - rbeg);
   const TB* B0 = (const TB*)B0v;
   const TB* B1 = (const TB*)B1v;
   const TB* w0 = ((g == g_last) ? (const TB*)B0lv : B0 + (size_t)g * N * K) + kbeg;
@@ -1064,7 +1078,7 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   const int gbeg = min(max(offsets[g], 0), max_rows);
   const int rbeg = gbeg + wk.y;
   const int gend = min(max(offsets[g + 1], gbeg), max_rows);
-  const int rows = min(R::BM, gend - rbeg);
+  const int rows = min(tile_height(gend - gbeg, R::BM), gend - rbeg);
   const uint16_t* w0 = ((g == g_last) ? B0l : B0 + (size_t)g * N * K) + kbeg;
 
   // This wave's copies: A and B rows wave * 32 + 8 i + lane / 8, chunk
@@ -1170,7 +1184,8 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
                                                      128 * gp, n0, wi, lane);
 }
 
-// Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles times NN
+// Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles (of
+// tile_height(rows_g, BM) rows, the last one taking the rest) times NN
 // N-tiles times ksplit K-splits, ordered by group, then K-split, then runs
 // of NG neighbouring N-tiles, then M-tile, then N-tile inside the run.  One
 // launch builds the lists of both projections.
@@ -1203,6 +1218,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
   __shared__ int32_t mts[1024];
   __shared__ int32_t bend[1024];
   __shared__ int32_t wsum[16];
+  __shared__ int32_t hts[1024];
   const int g = threadIdx.x;
   const int lane = g & 63, wv = g >> 6;
   // running maximum of the clamped group ends (inclusive max-scan)
@@ -1222,6 +1238,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
   if (g < G) {
     const int a = g == 0 ? a0 : bend[g - 1];
     mt = MOE_CEIL_DIV(be - a, BM);
+    hts[g] = tile_height(be - a, BM);
     if (blockIdx.x == 0 && blockIdx.y == 0) {
       clean[g] = a;
       if (g == G - 1) clean[G] = be;
@@ -1266,7 +1283,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
       mi = r / last;
       ni = nfull * NG + (r - mi * last);
     }
-    work[e] = make_int2(gg | (ni << 10) | (ks << 24), mi * BM);
+    work[e] = make_int2(gg | (ni << 10) | (ks << 24), mi * hts[gg]);
   }
   if (blockIdx.x == 0 && g == 0) nwork[0] = total;
 }
