@@ -556,6 +556,9 @@ FFN_SHAPES = {
     # large tiles, nine groups (one short): 264 down tiles, more than one
     # dispatch round
     "large_tail": (2048, 256, [1024, 1000, 900, 800, 1024, 1024, 1024, 1024, 100], 0),
+    # large tiles, groups just above a multiple of 256 rows: their M-tiles are
+    # of equal height (1045 rows: five tiles of 224 rows, the last 149)
+    "large_uneven": (512, 512, [1045, 1069, 513, 289, 257, 33], 2),
 }
 
 
