@@ -244,9 +244,12 @@ int moe_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offs
   MOE_REQUIRE(max_rows == 0 || (A && W1 && W3 && W2 && Yrows), MOE_EINVAL,
               "NULL A, W1, W3, W2 or Yrows");
   if ((rc = check_ws(ws, ws_bytes, ffn_ws_bytes(max_rows, G, d, F, dtype)))) return rc;
+  // A holds max_rows rows when read directly; through row_token its row
+  // count is not known here
   return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
                                        nullptr, -1, dtype, d, F, max_rows, Yrows, ws,
-                                       (hipStream_t)stream, true, nullptr),
+                                       (hipStream_t)stream, true, nullptr, nullptr,
+                                       row_token ? -1 : max_rows),
                     "moe_grouped_ffn");
 }
 
@@ -446,7 +449,7 @@ int forward_expert_choice(const moe_layer* L, const void* X, int64_t T, void* Y,
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, L->E * C + ns * T,
                            yrows, w + o.ffn, s, a.Yrows != nullptr, &part2,
-                           L->wtype == MOE_W_FP8 ? &q : nullptr);
+                           L->wtype == MOE_W_FP8 ? &q : nullptr, T);
   if (e == hipSuccess)
     e = launch_combine(yrows, part2, slotrow, gw, T, L->E, L->d, nullptr, ns ? nkept : nullptr,
                        Y, L->dtype, s);
@@ -525,7 +528,7 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
                            w + o.ffn, s, a.Yrows != nullptr, &part2,
-                           L->wtype == MOE_W_FP8 ? &q : nullptr);
+                           L->wtype == MOE_W_FP8 ? &q : nullptr, T);
   if (e == hipSuccess)
     e = launch_combine(yrows, part2, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
                        L->dtype, s);

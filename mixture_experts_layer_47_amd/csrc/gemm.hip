@@ -612,32 +612,80 @@ struct StageGeo {
   static constexpr int SZ = BM * CPA + BNT * CPB;                // 16-B slots per stage
 };
 
+// Copies through buffer loads: a wave-uniform base (a buffer descriptor in
+// SGPRs) plus a 32-bit per-lane byte offset that stays fixed for the whole
+// K loop; the stage's K position is the descriptor's scalar offset.  The
+// loop then spends no VALU work on addresses (the 64-bit per-lane form adds
+// one 64-bit add per copy, and register pressure makes the compiler reuse
+// one address register pair, so every copy waits for the previous one to
+// read its address).  Valid when every offset of the operand stays below
+// 2^32 bytes from its base; the launcher checks that on the host.
+__device__ __forceinline__ void buf_lds16(const void* base, uint32_t off, uint32_t soff,
+                                          void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff,
+                                        0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           off, soff, 0, 0);
+}
+// Copy sources of a stage part: per copy a per-lane pointer (PtrSrc), or a
+// wave-uniform base and a per-lane byte offset (BufSrc, bf16 operands).
+template <typename T, int N>
+struct PtrSrc {
+  const T* p[N];
+};
+template <int N>
+struct BufSrc {
+  const void* base[N];
+  uint32_t off[N];
+};
+
 // Copies of one stage's A or B part: instruction i of wave w fills A rows
 // (w CA + i) RPA .. + RPA of an A buffer, or B rows (w CB + i) RPB .. + RPB
 // of a B buffer.  pa[i], pb[i]: this lane's source of copy i at stage 0;
 // koff is the stage's first K element.
-template <int BM, int BNT, int KB, bool Q8, typename AL>
-__device__ __forceinline__ void dma_a(u32x4* buf,
-                                      const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                      int koff, int wave, AL alive) {
+template <int BM, int BNT, int KB, bool Q8, typename AL, int N>
+__device__ __forceinline__ void dma_a(u32x4* buf, const PtrSrc<uint16_t, N>& pa, int koff,
+                                      int wave, AL alive) {
   using G = StageGeo<BM, BNT, KB, Q8>;
+  static_assert(N == G::CA, "A copies");
 #pragma unroll
   for (int i = 0; i < G::CA; ++i)
     if ((uint32_t)alive & (1u << i))
-      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + koff),
+      __builtin_amdgcn_global_load_lds((const void*)(pa.p[i] + koff),
                                        (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA), 16,
                                        0, 0);
 }
-template <int BM, int BNT, int KB, bool Q8, typename TB>
-__device__ __forceinline__ void dma_b(u32x4* buf,
-                                      const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
-                                      int koff, int wave) {
+template <int BM, int BNT, int KB, bool Q8, typename TB, int N>
+__device__ __forceinline__ void dma_b(u32x4* buf, const PtrSrc<TB, N>& pb, int koff, int wave) {
   using G = StageGeo<BM, BNT, KB, Q8>;
+  static_assert(N == G::CB, "B copies");
 #pragma unroll
   for (int i = 0; i < G::CB; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(pb[i] + koff),
+    __builtin_amdgcn_global_load_lds((const void*)(pb.p[i] + koff),
                                      (void*)(buf + ((wave * G::CB + i) * G::RPB) * G::CPB), 16,
                                      0, 0);
+}
+// The same copies from buffer-form sources (bf16 operands).
+template <int BM, int BNT, int KB, bool Q8, typename AL, int N>
+__device__ __forceinline__ void dma_a(u32x4* buf, const BufSrc<N>& pa, int koff, int wave,
+                                      AL alive) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
+  static_assert(N == G::CA && !Q8, "bf16 A copies");
+#pragma unroll
+  for (int i = 0; i < G::CA; ++i)
+    if ((uint32_t)alive & (1u << i))
+      buf_lds16(pa.base[i], pa.off[i], (uint32_t)koff * 2u,
+                (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA));
+}
+template <int BM, int BNT, int KB, bool Q8, typename TB, int N>
+__device__ __forceinline__ void dma_b(u32x4* buf, const BufSrc<N>& pb, int koff, int wave) {
+  using G = StageGeo<BM, BNT, KB, Q8>;
+  static_assert(N == G::CB && !Q8, "bf16 B copies");
+#pragma unroll
+  for (int i = 0; i < G::CB; ++i)
+    buf_lds16(pb.base[i], pb.off[i], (uint32_t)koff * 2u,
+              (void*)(buf + ((wave * G::CB + i) * G::RPB) * G::CPB));
 }
 
 // Eight E4M3 bytes -> eight bf16 in MFMA operand order (byte i is element i),
@@ -731,10 +779,10 @@ constexpr int gcd_i(int a, int b) { return b ? gcd_i(b, a % b) : a; }
 // One iteration of the ring (see above) for stage s = s0 + h, h a
 // compile-time position in the ring period.
 template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
-          bool Q8, typename TB, int H, typename AL>
+          bool Q8, typename TB, int H, typename PA, typename PB, typename AL>
 __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra, const Ring& rb,
-                                          const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                          const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                          const PA& pa,
+                                          const PB& pb,
                                           int s, int nk, u32x4 (&f0)[FM + FN],
                                           u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave,
                                           AL alive) {
@@ -764,11 +812,11 @@ __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra,
 }
 
 template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
-          bool Q8, typename TB, typename AL, int... Hs>
+          bool Q8, typename TB, typename PA, typename PB, typename AL, int... Hs>
 __device__ __forceinline__ void ring_period(f32x16 (&acc)[FM][FN], const Ring& ra,
                                             const Ring& rb,
-                                            const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                            const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                            const PA& pa,
+                                            const PB& pb,
                                             int s0, int nk, int limit, u32x4 (&f0)[FM + FN],
                                             u32x4 (&f1)[FM + FN], const FragAddr& fr, int wave,
                                             AL alive, std::integer_sequence<int, Hs...>) {
@@ -781,11 +829,11 @@ __device__ __forceinline__ void ring_period(f32x16 (&acc)[FM][FN], const Ring& r
 }
 
 template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
-          bool Q8, typename TB, typename AL>
+          bool Q8, typename TB, typename PA, typename PB, typename AL>
 __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring& ra,
                                               const Ring& rb,
-                                              const uint16_t* const (&pa)[StageGeo<BM, BNT, KB, Q8>::CA],
-                                              const TB* const (&pb)[StageGeo<BM, BNT, KB, Q8>::CB],
+                                              const PA& pa,
+                                              const PB& pb,
                                               int nk, const FragAddr& fr, int wave,
                                               AL alive) {
   static_assert(NBA >= 2 && NBB >= 2, "rings of at least two buffers");
@@ -828,7 +876,7 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
 // sc0/sc1 [G][N] and sc0l/sc1l [N] for group g_last).
 // DENSE: one group of max_rows rows and no work list (the router logits).
 template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8, int NBB,
-          bool DENSE>
+          bool DENSE, bool BUF = false>
 __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
@@ -907,13 +955,22 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   // This lane's source of each copy: row (w C + i) RP + lane / CP of the
   // tile, chunk (lane % CP) ^ swz(row).  Rows past the tile's end re-read its
   // first row: their outputs are never stored.
-  const T* pa[G::CA];
+  // BUF: byte offsets from A + kbeg and from the weight matrix (+ kbeg),
+  // below 2^32 (checked by the launcher)
+  static_assert(!BUF || !Q8, "buffer-form copies for bf16 operands");
+  std::conditional_t<BUF, BufSrc<G::CA>, PtrSrc<T, G::CA>> pa;
 #pragma unroll
   for (int i = 0; i < G::CA; ++i) {
     const int r = (wave * G::CA + i) * G::RPA + lane / G::CPA;
     int src = rbeg + (r < rows ? r : 0);
     if (row_token) src = row_token[src];
-    pa[i] = A + (size_t)src * K + kbeg + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
+    const size_t e = (size_t)src * K + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
+    if constexpr (BUF) {
+      pa.base[i] = A + kbeg;
+      pa.off[i] = (uint32_t)(e * sizeof(T));
+    } else {
+      pa.p[i] = A + kbeg + e;
+    }
   }
   // A copies whose rows all lie past the tile's end are not issued (their
   // LDS rows feed only outputs that are never stored).  The wait counts stay
@@ -935,15 +992,22 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   }
   alive = __builtin_amdgcn_readfirstlane(alive);
   constexpr int EPC_B = 16 / sizeof(TB);             // B elements per 16-B chunk
-  const TB* pb[G::CB];
+  std::conditional_t<BUF, BufSrc<G::CB>, PtrSrc<TB, G::CB>> pb;
 #pragma unroll
   for (int i = 0; i < G::CB; ++i) {
-    const int r = (wave * G::CB + i) * G::RPB + lane / G::CPB;
+    // a copy's rows lie in one half (W1 or W3) of a gate/up tile
+    const int r0 = (wave * G::CB + i) * G::RPB;
+    const int r = r0 + lane / G::CPB;
     const int c = ((lane % G::CPB) ^ swz_rb<G::RBB>(r & 31)) * EPC_B;
-    if constexpr (GLU)
-      pb[i] = (r < BN ? w0 + (size_t)(n0 + r) * K : w1 + (size_t)(n0 + r - BN) * K) + c;
-    else
-      pb[i] = w0 + (size_t)(n0 + r) * K + c;
+    const bool lo = !GLU || r0 < BN;
+    const TB* wb = lo ? w0 : w1;
+    const size_t e = (size_t)(n0 + (lo ? r : r - BN)) * K + c;
+    if constexpr (BUF) {
+      pb.base[i] = wb;
+      pb.off[i] = (uint32_t)(e * sizeof(TB));
+    } else {
+      pb.p[i] = wb + e;
+    }
   }
 
   f32x16 acc[FM][FN];
@@ -1051,6 +1115,8 @@ __device__ __forceinline__ void fenced_barrier() {
 }
 
 // out = Y (fp32), y = A W2^T, N = d; K-split entries write slab ks - 1 of out2.
+// BUF: copies in buffer form (byte offsets below 2^32, checked by the launcher).
+template <bool BUF>
 __global__ __launch_bounds__(512) void k_moe_down_pp(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const int2* __restrict__ work, const int32_t* __restrict__ nwork,
@@ -1084,30 +1150,44 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   // This wave's copies: A and B rows wave * 32 + 8 i + lane / 8, chunk
   // (lane % 8) ^ swz(row) of each 128-B row.  A rows past the tile's end
   // re-read its first row (their outputs are never stored).
-  const uint16_t *sa[4], *sb[4];
+  // element offsets of this lane's copies from A + kbeg and from w0
+  size_t ea[4], eb[4];
   int dslot[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + lane / 8;
     const int c = ((lane % 8) ^ swz(r & 31)) * 8;
-    sa[i] = A + (size_t)(rbeg + (r < rows ? r : 0)) * K + kbeg + c;
-    sb[i] = w0 + (size_t)(n0 + r) * K + c;
+    ea[i] = (size_t)(rbeg + (r < rows ? r : 0)) * K + c;
+    eb[i] = (size_t)(n0 + r) * K + c;
     dslot[i] = (wave * 32 + i * 8) * 8;
   }
-  auto copy_a = [&](int S) {
-    u32x4* buf = la + (S % R::NA) * R::HS;
+  const uint16_t* abase = A + kbeg;
+  std::conditional_t<BUF, BufSrc<4>, PtrSrc<uint16_t, 4>> sa, sb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(sa[i] + S * 64), (void*)(buf + dslot[i]),
-                                       16, 0, 0);
-  };
-  auto copy_b = [&](int S) {
-    u32x4* buf = lb + (S % R::NB) * R::HS;
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BUF) {
+      sa.base[i] = abase;
+      sa.off[i] = (uint32_t)(ea[i] * 2);
+      sb.base[i] = w0;
+      sb.off[i] = (uint32_t)(eb[i] * 2);
+    } else {
+      sa.p[i] = abase + ea[i];
+      sb.p[i] = w0 + eb[i];
+    }
+  }
+  // stage S: K elements [64 S, 64 S + 64) of the split
+  auto copy = [&](const auto& src, u32x4* buf, int S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(sb[i] + S * 64), (void*)(buf + dslot[i]),
-                                       16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BUF)
+        buf_lds16(src.base[i], src.off[i], (uint32_t)S * 128u, (void*)(buf + dslot[i]));
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(src.p[i] + S * 64),
+                                         (void*)(buf + dslot[i]), 16, 0, 0);
+    }
   };
+  auto copy_a = [&](int S) { copy(sa, la + (S % R::NA) * R::HS, S); };
+  auto copy_b = [&](int S) { copy(sb, lb + (S % R::NB) * R::HS, S); };
   // fragments: A rows 128 gp + 32 i + lane % 32, B rows 64 wi + 32 j + lane
   // % 32; chunk 2 q + lane / 32 of k16 substep q, swizzled
   const int ra = 128 * gp + (lane & 31);
@@ -1423,23 +1503,24 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
+template <bool BUF>
 static void run_down_pp(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, PPRing::BM, a.N, PPRing::BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
-  hipLaunchKernelGGL(k_moe_down_pp, dim3((unsigned)nb), dim3(512), 0, s, (const uint16_t*)a.A,
+  hipLaunchKernelGGL(k_moe_down_pp<BUF>, dim3((unsigned)nb), dim3(512), 0, s, (const uint16_t*)a.A,
                      a.offsets, a.work, a.nwork, (const uint16_t*)a.B0, (const uint16_t*)a.B0l,
                      a.g_last, a.K, a.N, a.max_rows, a.ksplit, round, (float*)a.out, a.out2);
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
-          int NBB = NBUF, bool DENSE = false>
+          int NBB = NBUF, bool DENSE = false, bool BUF = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB, DENSE>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB, DENSE, BUF>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
                      a.B0, a.B1, a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
                      a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
@@ -1495,6 +1576,12 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
   return hipGetLastError();
 }
 
+// rows x K elements of es bytes lie within 2^32 bytes of their base, so the
+// buffer-form copies reach every one of them (rows < 0: not known).
+static bool buf_fits(int64_t rows, int64_t K, int es) {
+  return rows >= 0 && rows * K * es < ((int64_t)1 << 32);
+}
+
 // Yrows receives the down projection.  If the down GEMM is split along K,
 // the partial slabs are Yrows and the workspace slab(s) after it; with
 // reduce = true they are summed into Yrows here, otherwise *partial2 tells
@@ -1504,7 +1591,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
                               hipStream_t s, bool reduce, const float** partial2,
-                              const WeightScales* qs) {
+                              const WeightScales* qs, int64_t a_rows) {
   if (partial2) *partial2 = nullptr;
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
@@ -1560,7 +1647,12 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   } else if (dtype == MOE_BF16) {
     using T = uint16_t;
     switch (p.cfg) {
-      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB>(up, s); break;
+      case 0:
+        if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 2))
+          run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB, false, true>(up, s);
+        else
+          run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB>(up, s);
+        break;
       case 1: run_gemm_dma<256, 128, 1, 4, true, 128, 2, false, 3>(up, s); break;
       default: run_gemm<T, 32, 128, 1, 4, true>(up, s); break;
     }
@@ -1568,7 +1660,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_down_pp(dn, s);
+        if (b256 && buf_fits(max_rows, F, 2) && buf_fits(d, F, 2)) run_down_pp<true>(dn, s);
+        else if (b256) run_down_pp<false>(dn, s);
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
         break;
       case 1:

@@ -76,12 +76,14 @@ struct WeightScales {
 // partial sums are summed into Yrows if `reduce`, else *partial2 receives the
 // second partial slab ([max_rows][d], to be added to Yrows by the caller).
 // q != NULL: W1/W3/W2 (and the g_last matrices) hold E4M3 codes, A is bf16.
+// a_rows: rows A holds (row_token indexes them), or -1 if not known; with a
+// bound the large bf16 tiles may address A through 32-bit offsets.
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
                               hipStream_t s, bool reduce, const float** partial2,
-                              const WeightScales* q = nullptr);
+                              const WeightScales* q = nullptr, int64_t a_rows = -1);
 
 // combine.hip
 // Yrows2 (optional): second K-split partial of the rows, added to Yrows.
