@@ -1215,49 +1215,62 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   wait_vm_lgkm<0>();
   fenced_barrier();
   if (gp == 1) fenced_barrier();
-  for (int S = 0; S < nk; ++S) {
-    const u32x4* ba = la + (S % R::NA) * R::HS;
-    const u32x4* bb = lb + (S % R::NB) * R::HS;
+  // The K loop for a wave with NV live 32-row blocks (compile time, so a
+  // full tile's compute phases are straight runs of MFMAs); every wave runs
+  // the same copies and barriers whatever its NV.
+  auto kloop = [&](auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
+    for (int S = 0; S < nk; ++S) {
+      const u32x4* ba = la + (S % R::NA) * R::HS;
+      const u32x4* bb = lb + (S % R::NB) * R::HS;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      // ---- memory phase: fragments of k16 substeps 2 hh, 2 hh + 1
+      for (int hh = 0; hh < 2; ++hh) {
+        // ---- memory phase: fragments of k16 substeps 2 hh, 2 hh + 1
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int cs = csw[2 * hh + q];
+        for (int q = 0; q < 2; ++q) {
+          const int cs = csw[2 * hh + q];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[q][i] = ba[(ra + 32 * i) * 8 + cs];
-        fb[q][0] = bb[rb * 8 + cs];
-        fb[q][1] = bb[(rb + 32) * 8 + cs];
+          for (int i = 0; i < 4; ++i) fa[q][i] = ba[(ra + 32 * i) * 8 + cs];
+          fb[q][0] = bb[rb * 8 + cs];
+          fb[q][1] = bb[(rb + 32) * 8 + cs];
+        }
+        // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
+        // the B buffer of stage S - 1: both were last read in the previous
+        // phase of the other group, before the barrier that ended it.
+        if (hh == 0) {
+          if (S + 1 < nk) copy_a(S + 1);
+          wait_vm_lgkm<8>();                    // LDS reads done; copies fly on
+        } else if (S + 2 < nk) {
+          copy_b(S + 2);
+          wait_vm_lgkm<4>();                    // all but B(S + 2): stage S + 1 landed
+        } else {
+          wait_vm_lgkm<0>();
+        }
+        fenced_barrier();
+        // ---- compute phase
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < NV) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, fb[q][j]), __builtin_bit_cast(bf16x8, fa[q][i]),
+                    acc[i][j], 0, 0, 0);
+            }
+        __builtin_amdgcn_s_setprio(0);
+        fenced_barrier();
       }
-      // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
-      // the B buffer of stage S - 1: both were last read in the previous
-      // phase of the other group, before the barrier that ended it.
-      if (hh == 0) {
-        if (S + 1 < nk) copy_a(S + 1);
-        wait_vm_lgkm<8>();                    // LDS reads done; copies fly on
-      } else if (S + 2 < nk) {
-        copy_b(S + 2);
-        wait_vm_lgkm<4>();                    // all but B(S + 2): stage S + 1 landed
-      } else {
-        wait_vm_lgkm<0>();
-      }
-      fenced_barrier();
-      // ---- compute phase
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i < nv) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, fb[q][j]), __builtin_bit_cast(bf16x8, fa[q][i]),
-                  acc[i][j], 0, 0, 0);
-          }
-      __builtin_amdgcn_s_setprio(0);
-      fenced_barrier();
     }
+  };
+  switch (nv) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
   }
   if (gp == 0) fenced_barrier();              // both groups end on the same barrier count
   store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false>(acc, out, out2, ks, max_rows, N, rbeg, rows,
