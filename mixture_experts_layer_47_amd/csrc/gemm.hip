@@ -17,14 +17,14 @@
 //   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
 //     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
 //     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
-//   * three kernels share the tile logic.  k_moe_gemm_dma (bf16 and FP8
-//     prefill, FP8 decode) copies each stage from global memory straight
+//   * three kernels share the tile logic.  k_moe_gemm_dma (FP8 weights,
+//     bf16 medium tiles) copies each stage from global memory straight
 //     into LDS rings (global_load_lds), described at the kernel.
 //     k_moe_gemm (bf16 decode, fp32) stages through registers: BK = 128
 //     bytes of K per stage, two LDS stages and two register staging sets,
-//     stage k+2 fetched while stage k+1 is stored to LDS.  k_moe_down_pp
-//     (the bf16 down projection of large tiles) runs eight waves as two
-//     groups that alternate memory and compute phases (ping-pong);
+//     stage k+2 fetched while stage k+1 is stored to LDS.  k_moe_pp (both
+//     projections of the large bf16 tiles) runs eight waves as two groups
+//     that alternate memory and compute phases (ping-pong);
 //   * in both, a software pipeline over k16 substeps reads each substep's
 //     fragments while the previous substep's MFMAs run; scheduling groups
 //     pin the interleave;
@@ -666,27 +666,6 @@ __device__ __forceinline__ void dma_b(u32x4* buf, const PtrSrc<TB, N>& pb, int k
                                      (void*)(buf + ((wave * G::CB + i) * G::RPB) * G::CPB), 16,
                                      0, 0);
 }
-// The same copies from buffer-form sources (bf16 operands).
-template <int BM, int BNT, int KB, bool Q8, typename AL, int N>
-__device__ __forceinline__ void dma_a(u32x4* buf, const BufSrc<N>& pa, int koff, int wave,
-                                      AL alive) {
-  using G = StageGeo<BM, BNT, KB, Q8>;
-  static_assert(N == G::CA && !Q8, "bf16 A copies");
-#pragma unroll
-  for (int i = 0; i < G::CA; ++i)
-    if ((uint32_t)alive & (1u << i))
-      buf_lds16(pa.base[i], pa.off[i], (uint32_t)koff * 2u,
-                (void*)(buf + ((wave * G::CA + i) * G::RPA) * G::CPA));
-}
-template <int BM, int BNT, int KB, bool Q8, typename TB, int N>
-__device__ __forceinline__ void dma_b(u32x4* buf, const BufSrc<N>& pb, int koff, int wave) {
-  using G = StageGeo<BM, BNT, KB, Q8>;
-  static_assert(N == G::CB && !Q8, "bf16 B copies");
-#pragma unroll
-  for (int i = 0; i < G::CB; ++i)
-    buf_lds16(pb.base[i], pb.off[i], (uint32_t)koff * 2u,
-              (void*)(buf + ((wave * G::CB + i) * G::RPB) * G::CPB));
-}
 
 // Eight E4M3 bytes -> eight bf16 in MFMA operand order (byte i is element i),
 // two per v_cvt_scalef32_pk_bf16_fp8 with scale 1 (exact: every E4M3 value
@@ -876,7 +855,7 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
 // sc0/sc1 [G][N] and sc0l/sc1l [N] for group g_last).
 // DENSE: one group of max_rows rows and no work list (the router logits).
 template <int BM, int BN, int WM, int WN, bool GLU, int KB, int NBUF, bool Q8, int NBB,
-          bool DENSE, bool BUF = false>
+          bool DENSE>
 __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
@@ -955,22 +934,13 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   // This lane's source of each copy: row (w C + i) RP + lane / CP of the
   // tile, chunk (lane % CP) ^ swz(row).  Rows past the tile's end re-read its
   // first row: their outputs are never stored.
-  // BUF: byte offsets from A + kbeg and from the weight matrix (+ kbeg),
-  // below 2^32 (checked by the launcher)
-  static_assert(!BUF || !Q8, "buffer-form copies for bf16 operands");
-  std::conditional_t<BUF, BufSrc<G::CA>, PtrSrc<T, G::CA>> pa;
+  PtrSrc<T, G::CA> pa;
 #pragma unroll
   for (int i = 0; i < G::CA; ++i) {
     const int r = (wave * G::CA + i) * G::RPA + lane / G::CPA;
     int src = rbeg + (r < rows ? r : 0);
     if (row_token) src = row_token[src];
-    const size_t e = (size_t)src * K + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
-    if constexpr (BUF) {
-      pa.base[i] = A + kbeg;
-      pa.off[i] = (uint32_t)(e * sizeof(T));
-    } else {
-      pa.p[i] = A + kbeg + e;
-    }
+    pa.p[i] = A + (size_t)src * K + kbeg + (((lane % G::CPA) ^ swz_rb<G::RBA>(r & 31)) * 8);
   }
   // A copies whose rows all lie past the tile's end are not issued (their
   // LDS rows feed only outputs that are never stored).  The wait counts stay
@@ -992,22 +962,15 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   }
   alive = __builtin_amdgcn_readfirstlane(alive);
   constexpr int EPC_B = 16 / sizeof(TB);             // B elements per 16-B chunk
-  std::conditional_t<BUF, BufSrc<G::CB>, PtrSrc<TB, G::CB>> pb;
+  PtrSrc<TB, G::CB> pb;
 #pragma unroll
   for (int i = 0; i < G::CB; ++i) {
-    // a copy's rows lie in one half (W1 or W3) of a gate/up tile
-    const int r0 = (wave * G::CB + i) * G::RPB;
-    const int r = r0 + lane / G::CPB;
+    const int r = (wave * G::CB + i) * G::RPB + lane / G::CPB;
     const int c = ((lane % G::CPB) ^ swz_rb<G::RBB>(r & 31)) * EPC_B;
-    const bool lo = !GLU || r0 < BN;
-    const TB* wb = lo ? w0 : w1;
-    const size_t e = (size_t)(n0 + (lo ? r : r - BN)) * K + c;
-    if constexpr (BUF) {
-      pb.base[i] = wb;
-      pb.off[i] = (uint32_t)(e * sizeof(TB));
-    } else {
-      pb.p[i] = wb + e;
-    }
+    if constexpr (GLU)
+      pb.p[i] = (r < BN ? w0 + (size_t)(n0 + r) * K : w1 + (size_t)(n0 + r - BN) * K) + c;
+    else
+      pb.p[i] = w0 + (size_t)(n0 + r) * K + c;
   }
 
   f32x16 acc[FM][FN];
@@ -1077,11 +1040,12 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 }
 
 // ------------------------------------------------------- ping-pong variant
-// Down projection of the large tiles (experts with hundreds of rows, bf16
-// weights): 256 rows x 256 output columns per block, eight waves in two
-// groups of four (one wave of each group per SIMD).  Group gp owns rows
-// [128 gp, +128), wave wi the columns [64 wi, +64): 4 x 2 accumulator blocks
-// of 32x32 (128 registers), so two waves share a SIMD.
+// Both projections of the large tiles (experts with hundreds of rows, bf16
+// weights): 256 rows x 256 B rows per block (256 output columns of the down
+// projection, or 128 gate and the 128 matching up columns), eight waves in
+// two groups of four (one wave of each group per SIMD).  Group gp owns rows
+// [128 gp, +128), wave wi 64 of the B rows: 4 x 2 accumulator blocks of
+// 32x32 (128 registers), so two waves share a SIMD.
 //
 // The two groups alternate between a memory phase (read the next 32 K of
 // fragments from LDS into registers, issue global->LDS copies, wait) and a
@@ -1096,10 +1060,10 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 // (160 KB): A(S + 1) is issued in the first memory phase of stage S, B(S + 2)
 // in the second, so the address unit sees an even load and the weight rows
 // get two stages of lead.  Every wave copies 32 A rows and 32 B rows of each
-// stage.  (The same loop with a gate/up epilogue was 16 % faster than the
-// 4-wave kernel on one dense product, but on Mixtral-shaped grouped layers,
-// whose ragged last M-tiles stream a full weight slice for a few rows, it
-// was 7 % slower, so the gate/up projection keeps the 4-wave kernel.)
+// stage.  Its 128 x 64 wave tile reads 1.5 times the LDS bytes per MFMA of
+// the 4-wave kernel's 128 x 128; the alternation hides the copies better
+// than the 4-wave kernel's single wave per SIMD can (Mixtral-shaped gate/up
+// 7 % faster, grouped and dense alike).
 struct PPRing {
   static constexpr int BM = 256, BN = 256;    // token rows, output columns per tile
   static constexpr int NA = 2, NB = 3;        // ring depths (64-K stages)
@@ -1114,14 +1078,21 @@ __device__ __forceinline__ void fenced_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// out = Y (fp32), y = A W2^T, N = d; K-split entries write slab ks - 1 of out2.
+// GLU = false: out = Y (fp32), y = A W2^T, N = d; K-split entries write slab
+//              ks - 1 of out2.  Tiles of 256 output columns.
+// GLU = true:  out = H (bf16), h = silu(A W1^T) * (A W3^T), N = F; tiles of
+//              128 columns, the B tile holding their 128 W1 rows then their
+//              128 W3 rows; wave wi owns gate columns 32 wi .. 32 wi + 31 and
+//              the matching up columns, so SwiGLU runs on its accumulators.
 // BUF: copies in buffer form (byte offsets below 2^32, checked by the launcher).
-template <bool BUF>
-__global__ __launch_bounds__(512) void k_moe_down_pp(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const int2* __restrict__ work, const int32_t* __restrict__ nwork,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B0l, int g_last, int K, int N,
-    int max_rows, int ksplit, int round, float* __restrict__ out, float* __restrict__ out2) {
+template <bool GLU, bool BUF>
+__global__ __launch_bounds__(512) void k_moe_pp(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, const int2* __restrict__ work,
+    const int32_t* __restrict__ nwork, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B0l,
+    const uint16_t* __restrict__ B1l, int g_last, int K, int N, int max_rows, int ksplit,
+    int round, void* __restrict__ out, float* __restrict__ out2) {
   using R = PPRing;
   __shared__ u32x4 la[R::NA * R::HS];
   __shared__ u32x4 lb[R::NB * R::HS];
@@ -1136,7 +1107,8 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   if (t >= nwork[0]) return;
   const int2 wk = work[t];
   const int g = wk.x & 1023;
-  const int n0 = ((wk.x >> 10) & 16383) * R::BN;
+  constexpr int TBN = GLU ? R::BN / 2 : R::BN;   // output columns per tile
+  const int n0 = ((wk.x >> 10) & 16383) * TBN;
   const int ks = (int)((uint32_t)wk.x >> 24);
   const int Kc = K / ksplit;
   const int kbeg = ks * Kc;
@@ -1146,33 +1118,40 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   const int gend = min(max(offsets[g + 1], gbeg), max_rows);
   const int rows = min(tile_height(gend - gbeg, R::BM), gend - rbeg);
   const uint16_t* w0 = ((g == g_last) ? B0l : B0 + (size_t)g * N * K) + kbeg;
+  const uint16_t* w1 = GLU ? ((g == g_last) ? B1l : B1 + (size_t)g * N * K) + kbeg : w0;
 
   // This wave's copies: A and B rows wave * 32 + 8 i + lane / 8, chunk
-  // (lane % 8) ^ swz(row) of each 128-B row.  A rows past the tile's end
-  // re-read its first row (their outputs are never stored).
-  // element offsets of this lane's copies from A + kbeg and from w0
+  // (lane % 8) ^ swz(row) of each 128-B row (a copy's 8 B rows lie in one
+  // of the W1 / W3 halves).  A rows past the tile's end re-read its first
+  // row (their outputs are never stored).
+  // element offsets of this lane's copies from A + kbeg and from w0 / w1
   size_t ea[4], eb[4];
   int dslot[4];
+  bool bhi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + lane / 8;
     const int c = ((lane % 8) ^ swz(r & 31)) * 8;
-    ea[i] = (size_t)(rbeg + (r < rows ? r : 0)) * K + c;
-    eb[i] = (size_t)(n0 + r) * K + c;
+    int src = rbeg + (r < rows ? r : 0);
+    if (GLU && row_token) src = row_token[src];
+    ea[i] = (size_t)src * K + c;
+    bhi[i] = GLU && wave * 32 + i * 8 >= TBN;
+    eb[i] = (size_t)(n0 + (bhi[i] ? r - TBN : r)) * K + c;
     dslot[i] = (wave * 32 + i * 8) * 8;
   }
   const uint16_t* abase = A + kbeg;
   std::conditional_t<BUF, BufSrc<4>, PtrSrc<uint16_t, 4>> sa, sb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const uint16_t* wb = bhi[i] ? w1 : w0;
     if constexpr (BUF) {
       sa.base[i] = abase;
       sa.off[i] = (uint32_t)(ea[i] * 2);
-      sb.base[i] = w0;
+      sb.base[i] = wb;
       sb.off[i] = (uint32_t)(eb[i] * 2);
     } else {
       sa.p[i] = abase + ea[i];
-      sb.p[i] = w0 + eb[i];
+      sb.p[i] = wb + eb[i];
     }
   }
   // stage S: K elements [64 S, 64 S + 64) of the split
@@ -1188,10 +1167,12 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
   };
   auto copy_a = [&](int S) { copy(sa, la + (S % R::NA) * R::HS, S); };
   auto copy_b = [&](int S) { copy(sb, lb + (S % R::NB) * R::HS, S); };
-  // fragments: A rows 128 gp + 32 i + lane % 32, B rows 64 wi + 32 j + lane
-  // % 32; chunk 2 q + lane / 32 of k16 substep q, swizzled
+  // fragments: A rows 128 gp + 32 i + lane % 32; B rows 64 wi + 32 j + lane
+  // % 32 (GLU: 32 wi + lane % 32 and 128 + 32 wi + lane % 32); chunk
+  // 2 q + lane / 32 of k16 substep q, swizzled
   const int ra = 128 * gp + (lane & 31);
-  const int rb = 64 * wi + (lane & 31);
+  const int rb0 = (GLU ? 32 * wi : 64 * wi) + (lane & 31);
+  const int rb1 = GLU ? TBN + 32 * wi + (lane & 31) : rb0 + 32;
   int csw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) csw[q] = (2 * q + (lane >> 5)) ^ swz(lane & 31);
@@ -1231,8 +1212,8 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
           const int cs = csw[2 * hh + q];
 #pragma unroll
           for (int i = 0; i < 4; ++i) fa[q][i] = ba[(ra + 32 * i) * 8 + cs];
-          fb[q][0] = bb[rb * 8 + cs];
-          fb[q][1] = bb[(rb + 32) * 8 + cs];
+          fb[q][0] = bb[rb0 * 8 + cs];
+          fb[q][1] = bb[rb1 * 8 + cs];
         }
         // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
         // the B buffer of stage S - 1: both were last read in the previous
@@ -1273,8 +1254,12 @@ __global__ __launch_bounds__(512) void k_moe_down_pp(
     default: kloop(std::integral_constant<int, 0>{}); break;
   }
   if (gp == 0) fenced_barrier();              // both groups end on the same barrier count
-  store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false>(acc, out, out2, ks, max_rows, N, rbeg, rows,
-                                                     128 * gp, n0, wi, lane);
+  if constexpr (GLU)
+    store_tile<uint16_t, TBN, R::BN, 4, 4, 2, true>(acc, out, nullptr, 0, max_rows, N, rbeg, rows,
+                                                    128 * gp, n0, wi, lane);
+  else
+    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false>(acc, out, out2, ks, max_rows, N, rbeg,
+                                                       rows, 128 * gp, n0, wi, lane);
 }
 
 // Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles (of
@@ -1516,24 +1501,27 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
-template <bool BUF>
-static void run_down_pp(const GemmArgs& a, hipStream_t s) {
-  const int64_t ub = max_work(a.max_rows, a.G, PPRing::BM, a.N, PPRing::BN, a.ksplit);
+template <bool GLU, bool BUF>
+static void run_pp(const GemmArgs& a, hipStream_t s) {
+  const int64_t ub =
+      max_work(a.max_rows, a.G, PPRing::BM, a.N, GLU ? PPRing::BN / 2 : PPRing::BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
-  hipLaunchKernelGGL(k_moe_down_pp<BUF>, dim3((unsigned)nb), dim3(512), 0, s, (const uint16_t*)a.A,
-                     a.offsets, a.work, a.nwork, (const uint16_t*)a.B0, (const uint16_t*)a.B0l,
-                     a.g_last, a.K, a.N, a.max_rows, a.ksplit, round, (float*)a.out, a.out2);
+  hipLaunchKernelGGL((k_moe_pp<GLU, BUF>), dim3((unsigned)nb), dim3(512), 0, s,
+                     (const uint16_t*)a.A, a.row_token, a.offsets, a.work, a.nwork,
+                     (const uint16_t*)a.B0, (const uint16_t*)a.B1, (const uint16_t*)a.B0l,
+                     (const uint16_t*)a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
+                     a.out, a.out2);
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
-          int NBB = NBUF, bool DENSE = false, bool BUF = false>
+          int NBB = NBUF, bool DENSE = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
   const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
-  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB, DENSE, BUF>), dim3((unsigned)nb),
+  hipLaunchKernelGGL((k_moe_gemm_dma<BM, BN, WM, WN, GLU, KB, NBUF, Q8, NBB, DENSE>), dim3((unsigned)nb),
                      dim3(kThreads), 0, s, (const T*)a.A, a.row_token, a.offsets, a.work, a.nwork,
                      a.B0, a.B1, a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
                      a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
@@ -1661,10 +1649,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     using T = uint16_t;
     switch (p.cfg) {
       case 0:
-        if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 2))
-          run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB, false, true>(up, s);
-        else
-          run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, false, MOE_CFG0_NBB>(up, s);
+        if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 2)) run_pp<true, true>(up, s);
+        else run_pp<true, false>(up, s);
         break;
       case 1: run_gemm_dma<256, 128, 1, 4, true, 128, 2, false, 3>(up, s); break;
       default: run_gemm<T, 32, 128, 1, 4, true>(up, s); break;
@@ -1673,8 +1659,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256 && buf_fits(max_rows, F, 2) && buf_fits(d, F, 2)) run_down_pp<true>(dn, s);
-        else if (b256) run_down_pp<false>(dn, s);
+        if (b256 && buf_fits(max_rows, F, 2) && buf_fits(d, F, 2)) run_pp<false, true>(dn, s);
+        else if (b256) run_pp<false, false>(dn, s);
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
         break;
       case 1:
