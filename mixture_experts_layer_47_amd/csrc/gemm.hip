@@ -1086,17 +1086,27 @@ __device__ __forceinline__ void fenced_barrier() {
 //              128 W3 rows; wave wi owns gate columns 32 wi .. 32 wi + 31 and
 //              the matching up columns, so SwiGLU runs on its accumulators.
 // BUF: copies in buffer form (byte offsets below 2^32, checked by the launcher).
-template <bool GLU, bool BUF>
+// Q8: the weights are E4M3 codes (64-B rows per stage, 16 rows per copy
+// instruction), widened to bf16 in registers; the per-output-channel scales
+// sc0 (W1 or W2) and sc1 (W3) multiply the accumulators in the epilogue.
+template <bool GLU, bool BUF, bool Q8>
 __global__ __launch_bounds__(512) void k_moe_pp(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
-    const int32_t* __restrict__ nwork, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B0l,
-    const uint16_t* __restrict__ B1l, int g_last, int K, int N, int max_rows, int ksplit,
-    int round, void* __restrict__ out, float* __restrict__ out2) {
+    const int32_t* __restrict__ nwork, const void* __restrict__ B0v,
+    const void* __restrict__ B1v, const void* __restrict__ B0lv,
+    const void* __restrict__ B1lv, int g_last, int K, int N, int max_rows, int ksplit,
+    int round, void* __restrict__ out, float* __restrict__ out2,
+    const float* __restrict__ sc0, const float* __restrict__ sc1,
+    const float* __restrict__ sc0l, const float* __restrict__ sc1l) {
   using R = PPRing;
+  using TB = typename std::conditional<Q8, uint8_t, uint16_t>::type;
+  constexpr int CPB = Q8 ? 4 : 8;        // 16-B chunks per B row and stage
+  constexpr int RPB = 64 / CPB;          // B rows per copy instruction
+  constexpr int NCB = 32 / RPB;          // B copies per wave and stage
+  constexpr int HSB = R::BM * CPB;       // 16-B slots per B buffer
   __shared__ u32x4 la[R::NA * R::HS];
-  __shared__ u32x4 lb[R::NB * R::HS];
+  __shared__ u32x4 lb[R::NB * HSB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gp = wave >> 2, wi = wave & 3;
@@ -1118,17 +1128,20 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   const int rbeg = gbeg + wk.y;
   const int gend = min(max(offsets[g + 1], gbeg), max_rows);
   const int rows = min(tile_height(gend - gbeg, R::BM), gend - rbeg);
-  const uint16_t* w0 = ((g == g_last) ? B0l : B0 + (size_t)g * N * K) + kbeg;
-  const uint16_t* w1 = GLU ? ((g == g_last) ? B1l : B1 + (size_t)g * N * K) + kbeg : w0;
+  const TB* B0 = (const TB*)B0v;
+  const TB* B1 = (const TB*)B1v;
+  const TB* w0 = ((g == g_last) ? (const TB*)B0lv : B0 + (size_t)g * N * K) + kbeg;
+  const TB* w1 = GLU ? ((g == g_last) ? (const TB*)B1lv : B1 + (size_t)g * N * K) + kbeg : w0;
 
-  // This wave's copies: A and B rows wave * 32 + 8 i + lane / 8, chunk
-  // (lane % 8) ^ swz(row) of each 128-B row (a copy's 8 B rows lie in one
-  // of the W1 / W3 halves).  A rows past the tile's end re-read its first
-  // row (their outputs are never stored).
+  // This wave's copies: A rows wave * 32 + 8 i + lane / 8, chunk (lane % 8)
+  // ^ swz(row) of each 128-B row; B rows wave * 32 + RPB i + lane / CPB,
+  // chunk (lane % CPB) ^ swz_rb(row) (a copy's B rows lie in one of the
+  // W1 / W3 halves).  A rows past the tile's end re-read its first row
+  // (their outputs are never stored).
   // element offsets of this lane's copies from A + kbeg and from w0 / w1
-  size_t ea[4], eb[4];
-  int dslot[4];
-  bool bhi[4];
+  size_t ea[4], eb[NCB];
+  int dsa[4], dsb[NCB];
+  bool bhi[NCB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + lane / 8;
@@ -1136,47 +1149,76 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     int src = rbeg + (r < rows ? r : 0);
     if (GLU && row_token) src = row_token[src];
     ea[i] = (size_t)src * K + c;
-    bhi[i] = GLU && wave * 32 + i * 8 >= TBN;
+    dsa[i] = (wave * 32 + i * 8) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int r = wave * 32 + i * RPB + lane / CPB;
+    const int c = ((lane % CPB) ^ swz_rb<CPB * 16>(r & 31)) * (16 / (int)sizeof(TB));
+    bhi[i] = GLU && wave * 32 + i * RPB >= TBN;
     eb[i] = (size_t)(n0 + (bhi[i] ? r - TBN : r)) * K + c;
-    dslot[i] = (wave * 32 + i * 8) * 8;
+    dsb[i] = (wave * 32 + i * RPB) * CPB;
   }
   const uint16_t* abase = A + kbeg;
-  std::conditional_t<BUF, BufSrc<4>, PtrSrc<uint16_t, 4>> sa, sb;
+  std::conditional_t<BUF, BufSrc<4>, PtrSrc<uint16_t, 4>> sa;
+  std::conditional_t<BUF, BufSrc<NCB>, PtrSrc<TB, NCB>> sb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint16_t* wb = bhi[i] ? w1 : w0;
     if constexpr (BUF) {
       sa.base[i] = abase;
       sa.off[i] = (uint32_t)(ea[i] * 2);
-      sb.base[i] = wb;
-      sb.off[i] = (uint32_t)(eb[i] * 2);
     } else {
       sa.p[i] = abase + ea[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const TB* wb = bhi[i] ? w1 : w0;
+    if constexpr (BUF) {
+      sb.base[i] = wb;
+      sb.off[i] = (uint32_t)(eb[i] * sizeof(TB));
+    } else {
       sb.p[i] = wb + eb[i];
     }
   }
-  // stage S: K elements [64 S, 64 S + 64) of the split
-  auto copy = [&](const auto& src, u32x4* buf, int S) {
+  // stage S: K elements [64 S, 64 S + 64) of the split (64 elements of
+  // each row: 128 B of A, 64 sizeof(TB) B of W)
+  auto copy_a = [&](int S) {
+    u32x4* buf = la + (S % R::NA) * R::HS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (BUF)
-        buf_lds16(src.base[i], src.off[i], (uint32_t)S * 128u, (void*)(buf + dslot[i]));
+        buf_lds16(sa.base[i], sa.off[i], (uint32_t)S * 128u, (void*)(buf + dsa[i]));
       else
-        __builtin_amdgcn_global_load_lds((const void*)(src.p[i] + S * 64),
-                                         (void*)(buf + dslot[i]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(sa.p[i] + S * 64),
+                                         (void*)(buf + dsa[i]), 16, 0, 0);
     }
   };
-  auto copy_a = [&](int S) { copy(sa, la + (S % R::NA) * R::HS, S); };
-  auto copy_b = [&](int S) { copy(sb, lb + (S % R::NB) * R::HS, S); };
+  auto copy_b = [&](int S) {
+    u32x4* buf = lb + (S % R::NB) * HSB;
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) {
+      if constexpr (BUF)
+        buf_lds16(sb.base[i], sb.off[i], (uint32_t)S * (64u * (uint32_t)sizeof(TB)),
+                  (void*)(buf + dsb[i]));
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(sb.p[i] + S * 64),
+                                         (void*)(buf + dsb[i]), 16, 0, 0);
+    }
+  };
   // fragments: A rows 128 gp + 32 i + lane % 32; B rows 64 wi + 32 j + lane
   // % 32 (GLU: 32 wi + lane % 32 and 128 + 32 wi + lane % 32); chunk
   // 2 q + lane / 32 of k16 substep q, swizzled
   const int ra = 128 * gp + (lane & 31);
   const int rb0 = (GLU ? 32 * wi : 64 * wi) + (lane & 31);
   const int rb1 = GLU ? TBN + 32 * wi + (lane & 31) : rb0 + 32;
-  int csw[4];
+  int csw[4], csb[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) csw[q] = (2 * q + (lane >> 5)) ^ swz(lane & 31);
+  for (int q = 0; q < 4; ++q) {
+    csw[q] = (2 * q + (lane >> 5)) ^ swz(lane & 31);
+    // FP8 rows: chunk q holds the substep's 16 codes, lane / 32 picks 8
+    csb[q] = Q8 ? q ^ swz_rb<64>(lane & 31) : csw[q];
+  }
   // live 32-row blocks of this wave's 128 rows: the rest skip their MFMAs
   const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * gp + 31) >> 5)));
 
@@ -1204,7 +1246,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     constexpr int NV = decltype(nv_c)::value;
     for (int S = 0; S < nk; ++S) {
       const u32x4* ba = la + (S % R::NA) * R::HS;
-      const u32x4* bb = lb + (S % R::NB) * R::HS;
+      const u32x4* bb = lb + (S % R::NB) * HSB;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         // ---- memory phase: fragments of k16 substeps 2 hh, 2 hh + 1
@@ -1213,18 +1255,24 @@ __global__ __launch_bounds__(512) void k_moe_pp(
           const int cs = csw[2 * hh + q];
 #pragma unroll
           for (int i = 0; i < 4; ++i) fa[q][i] = ba[(ra + 32 * i) * 8 + cs];
-          fb[q][0] = bb[rb0 * 8 + cs];
-          fb[q][1] = bb[rb1 * 8 + cs];
+          if constexpr (Q8) {
+            const int cb = csb[2 * hh + q];
+            fb[q][0] = widen_e4m3(*((const uint2*)(bb + rb0 * CPB + cb) + (lane >> 5)));
+            fb[q][1] = widen_e4m3(*((const uint2*)(bb + rb1 * CPB + cb) + (lane >> 5)));
+          } else {
+            fb[q][0] = bb[rb0 * 8 + cs];
+            fb[q][1] = bb[rb1 * 8 + cs];
+          }
         }
         // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
         // the B buffer of stage S - 1: both were last read in the previous
         // phase of the other group, before the barrier that ended it.
         if (hh == 0) {
           if (S + 1 < nk) copy_a(S + 1);
-          wait_vm_lgkm<8>();                    // LDS reads done; copies fly on
+          wait_vm_lgkm<NCB + 4>();              // LDS reads done; copies fly on
         } else if (S + 2 < nk) {
           copy_b(S + 2);
-          wait_vm_lgkm<4>();                    // all but B(S + 2): stage S + 1 landed
+          wait_vm_lgkm<NCB>();                  // all but B(S + 2): stage S + 1 landed
         } else {
           wait_vm_lgkm<0>();
         }
@@ -1255,12 +1303,19 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     default: kloop(std::integral_constant<int, 0>{}); break;
   }
   if (gp == 0) fenced_barrier();              // both groups end on the same barrier count
+  const float* s0p = nullptr;
+  const float* s1p = nullptr;
+  if constexpr (Q8) {
+    s0p = (g == g_last) ? sc0l : sc0 + (size_t)g * N;
+    s1p = GLU ? ((g == g_last) ? sc1l : sc1 + (size_t)g * N) : nullptr;
+  }
   if constexpr (GLU)
-    store_tile<uint16_t, TBN, R::BN, 4, 4, 2, true>(acc, out, nullptr, 0, max_rows, N, rbeg, rows,
-                                                    128 * gp, n0, wi, lane);
+    store_tile<uint16_t, TBN, R::BN, 4, 4, 2, true, Q8>(acc, out, nullptr, 0, max_rows, N, rbeg,
+                                                        rows, 128 * gp, n0, wi, lane, s0p, s1p);
   else
-    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false>(acc, out, out2, ks, max_rows, N, rbeg,
-                                                       rows, 128 * gp, n0, wi, lane);
+    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false, Q8>(acc, out, out2, ks, max_rows, N, rbeg,
+                                                           rows, 128 * gp, n0, wi, lane, s0p,
+                                                           s1p);
 }
 
 // Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles (of
@@ -1513,17 +1568,16 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
                      a.max_rows, a.ksplit, round, a.out, a.out2);
 }
 
-template <bool GLU, bool BUF>
+template <bool GLU, bool BUF, bool Q8 = false>
 static void run_pp(const GemmArgs& a, hipStream_t s) {
   const int64_t ub =
       max_work(a.max_rows, a.G, PPRing::BM, a.N, GLU ? PPRing::BN / 2 : PPRing::BN, a.ksplit);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
-  hipLaunchKernelGGL((k_moe_pp<GLU, BUF>), dim3((unsigned)nb), dim3(512), 0, s,
-                     (const uint16_t*)a.A, a.row_token, a.offsets, a.work, a.nwork,
-                     (const uint16_t*)a.B0, (const uint16_t*)a.B1, (const uint16_t*)a.B0l,
-                     (const uint16_t*)a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round,
-                     a.out, a.out2);
+  hipLaunchKernelGGL((k_moe_pp<GLU, BUF, Q8>), dim3((unsigned)nb), dim3(512), 0, s,
+                     (const uint16_t*)a.A, a.row_token, a.offsets, a.work, a.nwork, a.B0, a.B1,
+                     a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round, a.out, a.out2,
+                     a.sc0, a.sc1, a.sc0l, a.sc1l);
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
@@ -1639,7 +1693,10 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     // large tiles, three for the medium); decode tiles use 128-K stages
     // (256-B A rows, 128-B weight rows: whole cache lines per copy).
     switch (p.cfg) {
-      case 0: run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, true, 128, 2, true>(up, s); break;
+      case 0:
+        if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 1)) run_pp<true, true, true>(up, s);
+        else run_pp<true, false, true>(up, s);
+        break;
       case 1: run_gemm_dma<256, 128, 1, 4, true, 128, 2, true, 3>(up, s); break;
       default: run_gemm_dma<32, 128, 1, 4, true, 256, 2, true>(up, s); break;
     }
@@ -1647,7 +1704,8 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     const bool b256 = down_bn(p.cfg, d) == 256;
     switch (p.cfg) {
       case 0:
-        if (b256) run_gemm_dma<MOE_CFG0_BM, 256, 2, 2, false, 128, 2, true>(dn, s);
+        if (b256 && buf_fits(max_rows, F, 2) && buf_fits(d, F, 1)) run_pp<false, true, true>(dn, s);
+        else if (b256) run_pp<false, false, true>(dn, s);
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, true>(dn, s);
         break;
       case 1:
