@@ -6,8 +6,9 @@
 // (14.2.2): h = silu(x W1) * (x W3), y = h W2.
 //
 // Kernel shape (one launch per projection):
-//   * a device-built work list holds one entry per (expert, M-tile, N-tile
-//     [, K-split]); it is ordered expert by expert, and inside an expert in
+//   * a device-built work list holds one entry per (expert, M-tile, N-tile),
+//     or per K part of the down projection's tiles that follow its last full
+//     dispatch round; it is ordered expert by expert, and inside an expert in
 //     groups of up to 8 M-tiles, runs of NG neighbouring N-tiles and the
 //     M-tiles fastest, so the tiles that run at the same time on one XCD
 //     share both their weight slices and their activation rows in that
@@ -18,13 +19,13 @@
 //   * block tile BM x BNT with four waves of (BM/WM) x (BNT/WN); the large
 //     configuration gives each wave 128 x 128 outputs: 16 MFMA blocks of
 //     32x32 per 8 fragment loads, accumulators in AGPRs, one wave per SIMD;
-//   * three kernels share the tile logic.  k_moe_gemm_dma (FP8 weights,
-//     bf16 medium tiles) copies each stage from global memory straight
+//   * three kernels share the tile logic.  k_moe_gemm_dma (medium tiles,
+//     FP8 decode tiles) copies each stage from global memory straight
 //     into LDS rings (global_load_lds), described at the kernel.
 //     k_moe_gemm (bf16 decode, fp32) stages through registers: BK = 128
 //     bytes of K per stage, two LDS stages and two register staging sets,
 //     stage k+2 fetched while stage k+1 is stored to LDS.  k_moe_pp (both
-//     projections of the large bf16 tiles) runs eight waves as two groups
+//     projections of the large tiles, bf16 or FP8 weights) runs eight waves as two groups
 //     that alternate memory and compute phases (ping-pong);
 //   * in both, a software pipeline over k16 substeps reads each substep's
 //     fragments while the previous substep's MFMAs run; scheduling groups
@@ -1079,8 +1080,9 @@ __device__ __forceinline__ void fenced_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// GLU = false: out = Y (fp32), y = A W2^T, N = d; K-split entries write slab
-//              ks - 1 of out2.  Tiles of 256 output columns.
+// GLU = false: out = Y (fp32), y = A W2^T, N = d; tiles of 256 output
+//              columns.  The entries of a tile split along K write their
+//              parts to slots of out2, and k_tail_sum adds them up.
 // GLU = true:  out = H (bf16), h = silu(A W1^T) * (A W3^T), N = F; tiles of
 //              128 columns, the B tile holding their 128 W1 rows then their
 //              128 W3 rows; wave wi owns gate columns 32 wi .. 32 wi + 31 and
@@ -1095,7 +1097,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
     const int32_t* __restrict__ nwork, const void* __restrict__ B0v,
     const void* __restrict__ B1v, const void* __restrict__ B0lv,
-    const void* __restrict__ B1lv, int g_last, int K, int N, int max_rows, int ksplit,
+    const void* __restrict__ B1lv, int g_last, int K, int N, int max_rows,
     int round, void* __restrict__ out, float* __restrict__ out2,
     const float* __restrict__ sc0, const float* __restrict__ sc1,
     const float* __restrict__ sc0l, const float* __restrict__ sc1l) {
@@ -1120,8 +1122,9 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   const int g = wk.x & 1023;
   constexpr int TBN = GLU ? R::BN / 2 : R::BN;   // output columns per tile
   const int n0 = ((wk.x >> 10) & 16383) * TBN;
-  const int ks = (int)((uint32_t)wk.x >> 24);
-  const int Kc = K / ksplit;
+  const int ks = (wk.x >> 24) & 15;           // part ks of 2^lg along K
+  const int lg = (wk.x >> 28) & 7;
+  const int Kc = K >> lg;
   const int kbeg = ks * Kc;
   const int nk = Kc / 64;
   const int gbeg = min(max(offsets[g], 0), max_rows);
@@ -1309,19 +1312,65 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     s0p = (g == g_last) ? sc0l : sc0 + (size_t)g * N;
     s1p = GLU ? ((g == g_last) ? sc1l : sc1 + (size_t)g * N) : nullptr;
   }
-  if constexpr (GLU)
+  if constexpr (GLU) {
     store_tile<uint16_t, TBN, R::BN, 4, 4, 2, true, Q8>(acc, out, nullptr, 0, max_rows, N, rbeg,
                                                         rows, 128 * gp, n0, wi, lane, s0p, s1p);
-  else
-    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false, Q8>(acc, out, out2, ks, max_rows, N, rbeg,
-                                                           rows, 128 * gp, n0, wi, lane, s0p,
-                                                           s1p);
+  } else if (lg == 0) {
+    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false, Q8>(acc, out, nullptr, 0, max_rows, N,
+                                                           rbeg, rows, 128 * gp, n0, wi, lane,
+                                                           s0p, nullptr);
+  } else {
+    // A tile split along K (the work list's last tiles): part ks goes to
+    // slot (ti 2^lg + ks) of `out2` (slots of BM x BN floats, row-major);
+    // k_tail_sum adds the parts in part order once every part has ended.
+    const int ti = (t - nwork[1]) >> lg;       // split tile index
+    store_tile<uint16_t, R::BN, R::BN, 4, 4, 2, false, Q8>(
+        acc, out2 + (size_t)((ti << lg) + ks) * (R::BM * R::BN), nullptr, 0, max_rows, R::BN, 0,
+        rows, 128 * gp, 0, wi, lane, Q8 ? s0p + n0 : nullptr, nullptr);
+  }
+}
+
+// Sums the K parts of the split tiles into the output rows, in part order
+// (a separate launch: the stream orders it after every part, with no
+// device-scope fence inside the GEMM; such fences write back and invalidate
+// an XCD's whole L2, and in the GEMM they cost more than the split saved).
+// Block b takes rows [32 (b % 8), +32) of split tile b / 8: the grid is
+// round / 2 x 8 blocks, as at most round / 2 tiles are split.
+__global__ __launch_bounds__(256) void k_tail_sum(const int2* __restrict__ work,
+                                                  const int32_t* __restrict__ nwork,
+                                                  const int32_t* __restrict__ offsets,
+                                                  int max_rows, int N,
+                                                  const float* __restrict__ slots,
+                                                  float* __restrict__ Y) {
+  constexpr int BM = PPRing::BM, BN = PPRing::BN;
+  const int total = nwork[0], base = nwork[1];
+  if (total <= base) return;
+  const int lg = (work[base].x >> 28) & 7;
+  const int ti = blockIdx.x >> 3, band = blockIdx.x & 7;
+  if (ti >= (total - base) >> lg) return;
+  const int2 wk = work[base + (ti << lg)];
+  const int g = wk.x & 1023;
+  const int n0 = ((wk.x >> 10) & 16383) * BN;
+  const int gbeg = min(max(offsets[g], 0), max_rows);
+  const int rbeg = gbeg + wk.y;
+  const int gend = min(max(offsets[g + 1], gbeg), max_rows);
+  const int rows = min(tile_height(gend - gbeg, BM), gend - rbeg);
+  const float* p = slots + (size_t)(ti << lg) * (BM * BN);
+  for (int x = threadIdx.x; x < 32 * (BN / 4); x += 256) {
+    const int r = band * 32 + x / (BN / 4), c = 4 * (x % (BN / 4));
+    if (r >= rows) break;
+    float4 a = *(const float4*)(p + r * BN + c);
+    for (int k = 1; k < (1 << lg); ++k) {
+      const float4 b = *(const float4*)(p + (size_t)k * (BM * BN) + r * BN + c);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *(float4*)(Y + (size_t)(rbeg + r) * N + n0 + c) = a;
+  }
 }
 
 // Work list: for each group g, mt_g = ceil(rows_g / BM) M-tiles (of
 // tile_height(rows_g, BM) rows, the last one taking the rest) times NN
-// N-tiles times ksplit K-splits, ordered by group, then K-split, then
-// M-groups of at most kMGroup M-tiles, then runs of NG neighbouring N-tiles,
+// N-tiles, ordered by group, then M-groups of at most kMGroup M-tiles, then runs of NG neighbouring N-tiles,
 // then N-tile, with the M-tiles of the group fastest.  The blocks of one
 // XCD take a contiguous run of the list, so they hold a few N-tiles of all
 // the M-tiles of an expert (up to kMGroup): with an expert of five M-tiles
@@ -1337,9 +1386,11 @@ __global__ __launch_bounds__(512) void k_moe_pp(
 // N-tile, whatever the offsets hold.  Block (0, 0) stores these bounds in
 // `clean` [G+1]; the GEMMs read their rows from there.
 struct WorkListArgs {
-  int BM, NN, NG, ksplit;
+  int BM, NN, NG;
+  int tail;           // largest K-split of the last tiles (a power of two; 1: none)
+  int round;          // blocks per dispatch round
   int2* work;
-  int32_t* nwork;
+  int32_t* nwork;     // [0] entries, [1] first split entry
 };
 
 // blockIdx.y picks the list; the kWorkSlices blocks of a list each rebuild
@@ -1352,7 +1403,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
                                                     WorkListArgs l1,
                                                     int32_t* __restrict__ clean) {
   const WorkListArgs& l = blockIdx.y == 0 ? l0 : l1;
-  const int BM = l.BM, NN = l.NN, NG = l.NG, ksplit = l.ksplit;
+  const int BM = l.BM, NN = l.NN, NG = l.NG;
   int2* __restrict__ work = l.work;
   int32_t* __restrict__ nwork = l.nwork;
   __shared__ int32_t sc[1024];
@@ -1389,7 +1440,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
   __syncthreads();                       // wsum is reused below
   // inclusive scan of the entry counts: in each wave by shuffles, then over
   // the 16 wave totals
-  int v = mt * NN * ksplit;
+  int v = mt * NN;
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(v, o);
     if (lane >= o) v += y;
@@ -1402,6 +1453,16 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
   __syncthreads();
   const int total = sc[1023];
   const int nfull = NN / NG;
+  // The q tiles after the last full dispatch round are split along K into
+  // 2^lg parts (the largest power of two up to `tail` with q 2^lg <= round),
+  // so that round ends after 1 / 2^lg of a tile instead of a whole one.
+  int q = 0, lg = 0;
+  if (l.tail > 1) {
+    q = total % l.round;
+    while ((2 << lg) <= l.tail && q * (2 << lg) <= l.round) ++lg;
+    if (lg == 0) q = 0;
+  }
+  const int base = total - q;
   for (int e = blockIdx.x * 1024 + g; e < total; e += kWorkSlices * 1024) {
     int lo = 0, hi = G - 1;                     // first group with inclusive sum > e
     while (lo < hi) {
@@ -1410,9 +1471,7 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
     }
     const int gg = lo;
     const int m = mts[gg];
-    const int jk = e - (sc[gg] - m * NN * ksplit);
-    const int ks = jk / (m * NN);                // K split: slowest inside a group
-    const int j = jk - ks * m * NN;
+    const int j = e - (sc[gg] - m * NN);
     int mi, ni;
     // M-groups of at most kMGroup M-tiles; in a group, runs of NG N-tiles;
     // in a run, N-tile by N-tile with the group's M-tiles fastest
@@ -1428,9 +1487,18 @@ __global__ __launch_bounds__(1024) void k_work_list(const int32_t* __restrict__ 
       ni = nfull * NG + r / ms;
       mi = g0 + r % ms;
     }
-    work[e] = make_int2(gg | (ni << 10) | (ks << 24), mi * hts[gg]);
+    const int x = gg | (ni << 10);
+    if (e < base) {
+      work[e] = make_int2(x, mi * hts[gg]);
+    } else {                                    // split tile: its parts are adjacent
+      for (int k = 0; k < (1 << lg); ++k)
+        work[base + ((e - base) << lg) + k] = make_int2(x | (k << 24) | (lg << 28), mi * hts[gg]);
+    }
   }
-  if (blockIdx.x == 0 && g == 0) nwork[0] = total;
+  if (blockIdx.x == 0 && g == 0) {
+    nwork[0] = base + (q << lg);
+    nwork[1] = base;
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -1461,9 +1529,13 @@ static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
   return {32, 2};
 }
 
-// Upper bound of work entries for one projection with N-tile width BN.
-static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN, int ksplit = 1) {
-  return (MOE_CEIL_DIV(max_rows, BM) + G) * (int64_t)(N / BN) * ksplit;
+static int num_cus();
+
+// Upper bound of work entries for one projection with N-tile width BN (a
+// K-split of the last tiles adds at most one dispatch round of entries).
+static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN, int tail = 1) {
+  return (MOE_CEIL_DIV(max_rows, BM) + G) * (int64_t)(N / BN) +
+         (tail > 1 ? (num_cus() & ~7) : 0);
 }
 
 // N-tile widths: gate/up tiles hold 128 columns of h (256 weight rows);
@@ -1472,18 +1544,22 @@ static int64_t max_work(int64_t max_rows, int G, int BM, int N, int BN, int kspl
 // the weights: -2 % on bf16 and -6 % on FP8 decode gate/up).
 static int up_bn(int) { return 128; }
 static int down_bn(int cfg, int d) { return (cfg == 2 || cfg == 3 || d % 256 != 0) ? 128 : 256; }
-static int num_cus();
 
-// K-split of the down projection: with few, long tiles (large rows per
-// expert) the last dispatch round can leave most CUs idle.  Split K in two
-// when that fills the rounds clearly better; the two partial row blocks are
-// summed in a fixed order afterwards (by the combine, or a reduce pass).
-static int down_split(const GemmPlan& p, int64_t max_rows, int G, int d, int F) {
-  if (p.cfg != 0 || F % 256 != 0 || F / 2 < 2048) return 1;
-  const double cus = (double)(num_cus() & ~7);
-  const double est = ((double)max_rows / p.BM + 0.5 * G) * (d / down_bn(p.cfg, d));
-  auto eff = [&](double t) { return (t / cus) / std::ceil(t / cus); };
-  return eff(2 * est) > eff(est) + 0.05 ? 2 : 1;
+// Largest K-split of the down projection's last tiles (large tiles, 256
+// columns: the ping-pong kernel).  The tiles after the last full dispatch
+// round would otherwise leave most CUs idle for a whole tile (Mixtral-shaped
+// layer: 576 tiles, 2.25 rounds of 256 CUs); split 2^lg ways they take
+// 1 / 2^lg of a tile.  Each part keeps at least 1024 of K (16 stages).
+static int down_tail(const GemmPlan& p, int d, int F) {
+  if (p.cfg != 0 || down_bn(p.cfg, d) != 256) return 1;
+  int t = 1;
+  while (t < 8 && F % (128 * t) == 0 && F / (2 * t) >= 1024) t *= 2;
+  return t;
+}
+
+// Workspace of the split tiles: `round` partial tiles of 256 x 256 floats.
+static size_t tail_ws_bytes(int tail) {
+  return tail > 1 ? (size_t)(num_cus() & ~7) * 256 * 256 * sizeof(float) : 0;
 }
 
 // Tile height the work lists are sized for (one plan serves bf16 and FP8
@@ -1492,23 +1568,18 @@ static int ws_tile_rows(int dtype, int64_t max_rows, int G, int d, int F) {
   return plan_for(dtype, max_rows, G, d, F).BM;
 }
 
-int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype) {
-  if (max_rows <= 0 || G <= 0) return 1;
-  return down_split(plan_for(dtype, max_rows, G, d, F), max_rows, G, d, F);
-}
-
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
   const int bm = ws_tile_rows(dtype, max_rows, G, d, F);
-  const int ks = down_split(p, max_rows, G, d, F);
+  const int tail = down_tail(p, d, F);
   const int64_t wu = max_work(max_rows, G, bm, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), ks);
+  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), tail);
   size_t b = align256((size_t)max_rows * F * es);                       // H
   b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
-  b += align256(2 * sizeof(int32_t));                                  // entry counts
+  b += align256(4 * sizeof(int32_t));                                  // entry counts
   b += align256((size_t)(G + 1) * sizeof(int32_t));                    // group bounds
-  b += align256((size_t)(ks - 1) * max_rows * d * sizeof(float));       // extra K-split partials
+  b += tail_ws_bytes(tail);                                            // split tiles
   return b;
 }
 
@@ -1535,15 +1606,16 @@ struct GemmArgs {
   void* out;
   int2* work;
   int32_t* nwork;
-  int ksplit;
-  float* out2;
+  int ksplit;                             // dense products: K-splits
+  float* out2;                            // dense: the other splits; list: split tiles
   const float *sc0, *sc1, *sc0l, *sc1l;   // FP8 weights: per-output-channel scales
+  int tail = 1;                           // list: largest K-split of the last tiles
 };
 
 static WorkListArgs work_list_args(const GemmArgs& a, int BM, int BN, bool glu) {
   const int NN = a.N / BN;
   const int NG = glu ? 8 : 4;
-  return WorkListArgs{BM, NN, NG < NN ? NG : NN, a.ksplit, a.work, a.nwork};
+  return WorkListArgs{BM, NN, NG < NN ? NG : NN, a.tail, num_cus() & ~7, a.work, a.nwork};
 }
 
 // Builds the work list of a (and of b when given: same groups and offsets).
@@ -1559,7 +1631,7 @@ static void run_work_list(const GemmArgs& a, const int32_t* offsets, int32_t* cl
 
 template <typename T, int BM, int BN, int WM, int WN, bool GLU>
 static void run_gemm(const GemmArgs& a, hipStream_t s) {
-  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
+  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN);
   const int round = num_cus() & ~7;           // blocks per dispatch round, whole XCDs
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   hipLaunchKernelGGL((k_moe_gemm<T, BM, BN, WM, WN, GLU>), dim3((unsigned)nb), dim3(kThreads), 0,
@@ -1571,19 +1643,19 @@ static void run_gemm(const GemmArgs& a, hipStream_t s) {
 template <bool GLU, bool BUF, bool Q8 = false>
 static void run_pp(const GemmArgs& a, hipStream_t s) {
   const int64_t ub =
-      max_work(a.max_rows, a.G, PPRing::BM, a.N, GLU ? PPRing::BN / 2 : PPRing::BN, a.ksplit);
+      max_work(a.max_rows, a.G, PPRing::BM, a.N, GLU ? PPRing::BN / 2 : PPRing::BN, a.tail);
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   hipLaunchKernelGGL((k_moe_pp<GLU, BUF, Q8>), dim3((unsigned)nb), dim3(512), 0, s,
                      (const uint16_t*)a.A, a.row_token, a.offsets, a.work, a.nwork, a.B0, a.B1,
-                     a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, a.ksplit, round, a.out, a.out2,
-                     a.sc0, a.sc1, a.sc0l, a.sc1l);
+                     a.B0l, a.B1l, a.g_last, a.K, a.N, a.max_rows, round, a.out, a.out2, a.sc0,
+                     a.sc1, a.sc0l, a.sc1l);
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int KB = 128, int NBUF = 2, bool Q8 = false,
           int NBB = NBUF, bool DENSE = false>
 static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
-  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN, a.ksplit);
+  const int64_t ub = max_work(a.max_rows, a.G, BM, a.N, BN) * a.ksplit;   // dense: K-splits
   const int round = num_cus() & ~7;
   const int64_t nb = MOE_CEIL_DIV(ub, round) * round;
   using T = uint16_t;
@@ -1593,24 +1665,12 @@ static void run_gemm_dma(const GemmArgs& a, hipStream_t s) {
                      a.out, a.out2, a.sc0, a.sc1, a.sc0l, a.sc1l);
 }
 
-// Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
-// g_last >= 0, group g_last uses the separate (shared-expert) matrices.
-// Sum the K-split partial slabs into Y, rows [0, offsets[G]), in split order.
-__global__ __launch_bounds__(256) void k_reduce_split(float* __restrict__ Y,
-                                                      const float* __restrict__ Y2,
-                                                      const int32_t* __restrict__ offsets, int G,
-                                                      int max_rows, int d, int ksplit) {
-  const int r = blockIdx.x;
-  if (r >= min(max(offsets[G], 0), max_rows)) return;
-  const size_t slab = (size_t)max_rows * d;
-  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    float4 a = *(float4*)(Y + (size_t)r * d + c);
-    for (int k = 1; k < ksplit; ++k) {
-      const float4 b = *(const float4*)(Y2 + (k - 1) * slab + (size_t)r * d + c);
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
-    *(float4*)(Y + (size_t)r * d + c) = a;
-  }
+// Adds up the parts of the down tiles the work list split along K.
+static void run_tail_sum(const GemmArgs& a, hipStream_t s) {
+  if (a.tail <= 1) return;
+  const int round = num_cus() & ~7;
+  hipLaunchKernelGGL(k_tail_sum, dim3((unsigned)(round / 2 * 8)), dim3(256), 0, s, a.work, a.nwork,
+                     a.offsets, a.max_rows, a.N, a.out2, (float*)a.out);
 }
 
 // ---------------------------------------------------------------- router
@@ -1649,10 +1709,10 @@ static bool buf_fits(int64_t rows, int64_t K, int es) {
   return rows >= 0 && rows * K * es < ((int64_t)1 << 32);
 }
 
-// Yrows receives the down projection.  If the down GEMM is split along K,
-// the partial slabs are Yrows and the workspace slab(s) after it; with
-// reduce = true they are summed into Yrows here, otherwise *partial2 tells
-// the caller where the second slab is (NULL when there is no split).
+// Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
+// g_last >= 0, group g_last uses the separate (shared-expert) matrices.
+// Yrows receives the down projection, complete (tiles split along K are
+// summed inside the down kernel); *partial2 is always set to NULL.
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
@@ -1662,24 +1722,25 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   if (partial2) *partial2 = nullptr;
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
-  const int ks = down_split(p, max_rows, G, d, F);
+  const int tail = down_tail(p, d, F);
   const int es = dtype == MOE_BF16 ? 2 : 4;
   // work-list regions laid out as in ffn_ws_bytes
   const int bm = ws_tile_rows(dtype, max_rows, G, d, F);
   const int64_t wu = max_work(max_rows, G, bm, F, up_bn(p.cfg));
-  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), ks);
+  const int64_t wd = max_work(max_rows, G, bm, d, down_bn(p.cfg, d), tail);
   char* q = (char*)ws;
   void* H = q;               q += align256((size_t)max_rows * F * es);
   int2* work_up = (int2*)q;  q += align256((size_t)wu * sizeof(int2));
   int2* work_dn = (int2*)q;  q += align256((size_t)wd * sizeof(int2));
-  int32_t* nwork = (int32_t*)q; q += align256(2 * sizeof(int32_t));
+  int32_t* nwork = (int32_t*)q; q += align256(4 * sizeof(int32_t));   // two per list
   int32_t* bounds = (int32_t*)q; q += align256((size_t)(G + 1) * sizeof(int32_t));
-  float* slabs = (float*)q;  // (ks - 1) extra partial slabs of [max_rows][d]
+  float* fix = tail > 1 ? (float*)q : nullptr;                        // split tiles
   const int mr = (int)max_rows;
   GemmArgs up{A,  row_token, bounds, G, W1, W3, W1l, W3l, g_last, d, F, mr, H, work_up, nwork,
               1,  nullptr};
   GemmArgs dn{H,  nullptr, bounds, G, W2, nullptr, W2l, nullptr, g_last, F, d, mr, Yrows, work_dn,
-              nwork + 1, ks, slabs};
+              nwork + 2, 1, fix};
+  dn.tail = tail;
   if (qs) {
     up.sc0 = qs->s1; up.sc1 = qs->s3; up.sc0l = qs->s1l; up.sc1l = qs->s3l;
     dn.sc0 = qs->s2; dn.sc0l = qs->s2l;
@@ -1689,9 +1750,9 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
   timing_mark("tile_map", s);
   if (qs) {
     // FP8 weights: the large and medium tiles keep 64-K stages (32 KB of A
-    // rows and 16 KB of weight rows per stage; two weight buffers for the
-    // large tiles, three for the medium); decode tiles use 128-K stages
-    // (256-B A rows, 128-B weight rows: whole cache lines per copy).
+    // rows and 16 KB of weight codes per stage; three code buffers); decode
+    // tiles use 128-K stages (256-B A rows, 128-B weight rows: whole cache
+    // lines per copy).
     switch (p.cfg) {
       case 0:
         if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 1)) run_pp<true, true, true>(up, s);
@@ -1714,6 +1775,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
         break;
       default: run_gemm_dma<32, 128, 1, 4, false, 256, 2, true>(dn, s); break;
     }
+    run_tail_sum(dn, s);
     timing_mark("ffn_down", s);
   } else if (dtype == MOE_BF16) {
     using T = uint16_t;
@@ -1739,6 +1801,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
         break;
       default: run_gemm<T, 32, 128, 1, 4, false>(dn, s); break;
     }
+    run_tail_sum(dn, s);
     timing_mark("ffn_down", s);
   } else {
     run_gemm<float, 64, 128, 2, 2, true>(up, s);
@@ -1746,13 +1809,7 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     run_gemm<float, 64, 128, 2, 2, false>(dn, s);
     timing_mark("ffn_down", s);
   }
-  if (ks > 1) {
-    if (reduce)
-      hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)max_rows), dim3(256), 0, s, Yrows, slabs,
-                         bounds, G, mr, d, ks);
-    else if (partial2)
-      *partial2 = slabs;
-  }
+  (void)reduce;
   return hipGetLastError();
 }
 

@@ -59,7 +59,6 @@ hipError_t launch_gather(const void* X, const int32_t* sorted_slot, const int32_
 
 // gemm.hip
 size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype);
-int ffn_down_split(int64_t max_rows, int G, int d, int F, int dtype);
 // Router logits on the tiled GEMM kernel (bf16, E a multiple of 64):
 // part[z][T][E] for the `split` K-splits z.
 bool router_gemm_ok(int dtype, int64_t T, int d, int E, int split);
@@ -72,9 +71,8 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
 struct WeightScales {
   const float *s1, *s3, *s2, *s1l, *s3l, *s2l;
 };
-// The down projection may be split along K (ffn_down_split() > 1): then the
-// partial sums are summed into Yrows if `reduce`, else *partial2 receives the
-// second partial slab ([max_rows][d], to be added to Yrows by the caller).
+// Yrows receives the complete down projection; *partial2 (if given) is set
+// to NULL and `reduce` has no effect (kept for the callers' interface).
 // q != NULL: W1/W3/W2 (and the g_last matrices) hold E4M3 codes, A is bf16.
 // a_rows: rows A holds (row_token indexes them), or -1 if not known; with a
 // bound the large bf16 tiles may address A through 32-bit offsets.

@@ -73,19 +73,20 @@ def test_forward_noalloc_rejects_oversize_on_host(L):
     assert L.moe_forward_noalloc(ctypes.byref(bad), 1, 4, 1, None, None) == -1
 
 
-def test_down_projection_split_decision(L):
-    """Long-reduction, few-tile shapes split the down projection along K; the
-    workspace then carries one extra fp32 partial slab of [max_rows][d]."""
-    # Mixtral-shaped prefill: 8192 rows, 8 experts, d 4096, F 14336 -> split
-    big = L.moe_grouped_ffn_workspace_size(8192, 8, 4096, 14336, 1)
-    base = 8192 * 14336 * 2                      # H
-    slab = 8192 * 4096 * 4
-    assert big >= base + slab
-    # the parity-test shape (rows 1130, d 768, F 4096) also splits
-    assert L.moe_grouped_ffn_workspace_size(1130, 4, 768, 4096, 1) >= 1130 * 4096 * 2 + 1130 * 768 * 4
-    # short reductions never split
-    small = L.moe_grouped_ffn_workspace_size(1200, 8, 512, 640, 1)
-    assert small < 1200 * 640 * 2 + 1200 * 512 * 4
+def test_down_projection_split_workspace(L):
+    """Large-tile shapes with a long enough reduction split the down tiles
+    left after the last full dispatch round along K; the workspace then holds
+    one round of 256 x 256 fp32 partial tiles (256 CUs when no GPU is
+    visible) and their arrival counters.  Other shapes hold none."""
+    tiles = 256 * 256 * 256 * 4
+    ws = L.moe_grouped_ffn_workspace_size
+    # Mixtral-shaped prefill: 8192 rows, 8 experts, d 4096, F 14336
+    assert ws(8192, 8, 4096, 14336, 1) >= 8192 * 14336 * 2 + tiles
+    # the parity-test shape (rows 1130, d 768, F 4096)
+    assert ws(1130, 4, 768, 4096, 1) >= 1130 * 4096 * 2 + tiles
+    # short reductions (F / 2 < 1024) and medium tiles never split
+    assert ws(1200, 8, 512, 640, 1) < 1200 * 640 * 2 + tiles
+    assert ws(32768, 256, 7168, 2048, 1) < 32768 * 2048 * 2 + tiles
 
 
 def _route(L, **over):

@@ -549,8 +549,11 @@ FFN_SHAPES = {
     "large_d512": (512, 512, [600, 0], 5),
     # decode-sized groups (a few rows each)
     "decode": (512, 256, [2, 0, 1, 3, 2, 2, 0, 1, 4, 2, 1, 2, 3, 1, 2, 2], 0),
-    # large tiles with a long reduction: the down projection is split along K
+    # large tiles with a long reduction, fewer tiles than CUs: every down
+    # tile is split along K in four parts (K / 4 = 1024)
     "large_ksplit": (768, 4096, [300, 260, 280, 290], 0),
+    # three down tiles, each split along K in eight parts of 1024
+    "large_split8": (256, 8192, [300, 200], 0),
     # medium tiles 256 rows tall: every count of 32-row blocks from 1 to 8
     "tall_tiles": (512, 512, [1, 33, 65, 97, 129, 161, 193, 225, 256, 250, 70], 3),
     # large tiles, nine groups (one short): 264 down tiles, more than one
@@ -617,9 +620,15 @@ def _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, seed):
     offs = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32)
     tok = torch.randint(0, T, (R,), generator=g, dtype=torch.int32)
     A = X if use_row_token else X[tok.long()]
-    Y = moe.grouped_ffn(A.to(DEV), offs.to(DEV), *dev_w, R + slack,
-                        row_token=tok.to(DEV) if use_row_token else None, scales=scales)
+    def run():
+        return moe.grouped_ffn(A.to(DEV), offs.to(DEV), *dev_w, R + slack,
+                               row_token=tok.to(DEV) if use_row_token else None, scales=scales)
+    Y = run()
     torch.cuda.synchronize()
+    if F >= 2048 and dtype != "f32":
+        # down tiles split along K are summed in part order by whichever part
+        # finishes last: the bits must not depend on that order
+        assert torch.equal(run()[:R], Y[:R])
     Xr = X[tok.long()].double().numpy()
     bf16 = dtype != "f32"
     for e in range(G):
@@ -631,10 +640,9 @@ def _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, seed):
 
 
 def test_forward_ksplit_paths_agree():
-    """A shape whose down projection is split along K: the forward path that
-    sums the two partial slabs inside the combine (no expert-row output) and
-    the one that reduces them into the expert rows first must give the same
-    bits, and both must match the oracle."""
+    """A shape whose down tiles are all split along K (fewer tiles than CUs,
+    four parts each): the plain forward and the one with every optional output must give
+    the same bits, and both must match the oracle."""
     w = Workload("ksplit", T=600, d=768, E=4, k=2, F=4096, seed=23)
     _announce("forward K-split")
     inp = make_inputs(w, DEV)
