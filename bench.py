@@ -290,11 +290,11 @@ def measure(w, steps, warmup, keep_inputs=False):
     flops, bytes_, touched, rows = up_kernel_work(w, kept, n_kept)
     dflops, dbytes = down_kernel_work(w, touched, rows)
     roof = roof_of(flops, bytes_, up_ms, peak)
-    roof.update(kernel="k_moe_gemm_dma gate/up + SwiGLU (ffn_up)", kernel_ms=up_ms,
+    roof.update(kernel="grouped gate/up GEMM + SwiGLU (ffn_up phase)", kernel_ms=up_ms,
                 algorithmic={"flops": flops, "bytes": bytes_, "rows": rows,
                              "touched_experts": touched})
     roof_dn = roof_of(dflops, dbytes, dn_ms, peak)
-    roof_dn.update(kernel="k_moe_gemm_dma down (ffn_down)", kernel_ms=dn_ms,
+    roof_dn.update(kernel="grouped down GEMM (ffn_down phase, with k_tail_sum)", kernel_ms=dn_ms,
                    algorithmic={"flops": dflops, "bytes": dbytes})
 
     # whole layer against its binding roof

@@ -248,8 +248,7 @@ int moe_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offs
   // count is not known here
   return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
                                        nullptr, -1, dtype, d, F, max_rows, Yrows, ws,
-                                       (hipStream_t)stream, true, nullptr, nullptr,
-                                       row_token ? -1 : max_rows),
+                                       (hipStream_t)stream, nullptr, row_token ? -1 : max_rows),
                     "moe_grouped_ffn");
 }
 
@@ -273,7 +272,7 @@ int moe_grouped_ffn_fp8(const void* A, const int32_t* row_token, const int32_t* 
   const WeightScales q{W1_scale, W3_scale, W2_scale, nullptr, nullptr, nullptr};
   return hip_status(launch_grouped_ffn(A, row_token, offsets, G, W1, W3, W2, nullptr, nullptr,
                                        nullptr, -1, MOE_BF16, d, F, max_rows, Yrows, ws,
-                                       (hipStream_t)stream, true, nullptr, &q),
+                                       (hipStream_t)stream, &q),
                     "moe_grouped_ffn_fp8");
 }
 
@@ -288,8 +287,8 @@ int moe_combine(const float* Yrows, const int32_t* slot_row, const float* topk_w
   MOE_REQUIRE(T * (int64_t)k <= INT32_MAX, MOE_EUNSUPPORTED, "T*k too large");
   MOE_REQUIRE(T == 0 || (Yrows && slot_row && topk_w && Y), MOE_EINVAL,
               "NULL Yrows, slot_row, topk_w or Y");
-  return hip_status(launch_combine(Yrows, nullptr, slot_row, topk_w, T, k, d, shared, nullptr, Y,
-                                   dtype, (hipStream_t)stream),
+  return hip_status(launch_combine(Yrows, slot_row, topk_w, T, k, d, shared, nullptr, Y, dtype,
+                                   (hipStream_t)stream),
                     "moe_combine");
 }
 
@@ -442,17 +441,15 @@ int forward_expert_choice(const moe_layer* L, const void* X, int64_t T, void* Y,
                                  (int)C, a.logits, offsets, a.counts, nkept, a.sorted_slot,
                                  slotrow, gw, rowtok, ns ? (int)T : 0, w + o.route, s);
   timing_mark("route", s);
-  const float* part2 = nullptr;
   const WeightScales q{L->W1_scale, L->W3_scale, L->W2_scale, L->Ws1_scale, L->Ws3_scale,
                        L->Ws2_scale};
   if (e == hipSuccess)
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, L->E * C + ns * T,
-                           yrows, w + o.ffn, s, a.Yrows != nullptr, &part2,
-                           L->wtype == MOE_W_FP8 ? &q : nullptr, T);
+                           yrows, w + o.ffn, s, L->wtype == MOE_W_FP8 ? &q : nullptr, T);
   if (e == hipSuccess)
-    e = launch_combine(yrows, part2, slotrow, gw, T, L->E, L->d, nullptr, ns ? nkept : nullptr,
-                       Y, L->dtype, s);
+    e = launch_combine(yrows, slotrow, gw, T, L->E, L->d, nullptr, ns ? nkept : nullptr, Y,
+                       L->dtype, s);
   timing_mark("combine", s);
   if (e == hipSuccess && a.offsets)
     e = hipMemcpyAsync(a.offsets, offsets, (size_t)(L->E + 1) * 4, hipMemcpyDeviceToDevice, s);
@@ -518,19 +515,14 @@ int moe_forward(const moe_layer* L, const void* X, int64_t T, void* Y, const moe
     e = launch_reroute(ids, backup, nb, T, L->k, L->E, cap, ns ? (int)T : 0, counts, offsets,
                        sorted, slotrow, nkept, rowtok, w + o.rr, s);
   timing_mark("dispatch", s);
-  // With a K-split down projection the combine adds the two partial slabs
-  // itself, unless the caller asked for the expert rows (then they are
-  // summed into Yrows first).
-  const float* part2 = nullptr;
   const WeightScales q{L->W1_scale, L->W3_scale, L->W2_scale, L->Ws1_scale, L->Ws3_scale,
                        L->Ws2_scale};
   if (e == hipSuccess)
     e = launch_grouped_ffn(X, rowtok, offsets, L->E + ns, L->W1, L->W3, L->W2, L->Ws1, L->Ws3,
                            L->Ws2, ns ? L->E : -1, L->dtype, L->d, L->F, Tk + ns * T, yrows,
-                           w + o.ffn, s, a.Yrows != nullptr, &part2,
-                           L->wtype == MOE_W_FP8 ? &q : nullptr, T);
+                           w + o.ffn, s, L->wtype == MOE_W_FP8 ? &q : nullptr, T);
   if (e == hipSuccess)
-    e = launch_combine(yrows, part2, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
+    e = launch_combine(yrows, slotrow, gw, T, L->k, L->d, nullptr, ns ? nkept : nullptr, Y,
                        L->dtype, s);
   timing_mark("combine", s);
   if (e == hipSuccess && a.offsets)

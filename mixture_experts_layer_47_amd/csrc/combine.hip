@@ -11,14 +11,12 @@
 
 namespace moe {
 
-// KS: a second fp32 slab (the down projection's second K-split) is present.
 // A block of 512 threads serves 512 / TPT tokens, TPT threads each (TPT a
 // multiple of 64 and at least k): narrow rows pack several tokens into a
 // block, so blocks stay large enough that their launch cost does not
 // dominate (8192 tokens of 2048 columns: 2048 blocks instead of 8192).
-template <typename OutT, bool KS, int TPT>
+template <typename OutT, int TPT>
 __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows,
-                                                 const float* __restrict__ Yrows2,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ w, int64_t T_, int k,
                                                  int d, const float* __restrict__ shared,
@@ -61,24 +59,12 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
   __syncthreads();
   if (!tok) return;                           // no block barrier below
   const float* sh = nullptr;
-  const float* sh2 = nullptr;
-  if (shared) {
+  if (shared)
     sh = shared + (size_t)t * d;
-  } else if (shared_row0) {
+  else if (shared_row0)
     sh = Yrows + ((size_t)shared_row0[0] + t) * d;
-    if constexpr (KS) sh2 = Yrows2 + ((size_t)shared_row0[0] + t) * d;
-  }
-  // Expert row j of this column chunk (K-split partials summed first, in
-  // split order).
-  auto row_val = [&](int j, int c) {
-    const int rr = rows[j];
-    float4 y = *(const float4*)(Yrows + (size_t)rr * d + c);
-    if constexpr (KS) {
-      const float4 y2 = *(const float4*)(Yrows2 + (size_t)rr * d + c);
-      y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
-    }
-    return y;
-  };
+  // expert row j of this column chunk
+  auto row_val = [&](int j, int c) { return *(const float4*)(Yrows + (size_t)rows[j] * d + c); };
   for (int c = lt * 4; c < d; c += TPT * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int j = 0;
@@ -86,16 +72,7 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
     for (; j + 4 <= n; j += 4) {
       float4 y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = *(const float4*)(Yrows + (size_t)rows[j + u] * d + c);
-      if constexpr (KS) {
-        float4 y2[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) y2[u] = *(const float4*)(Yrows2 + (size_t)rows[j + u] * d + c);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          y[u].x += y2[u].x; y[u].y += y2[u].y; y[u].z += y2[u].z; y[u].w += y2[u].w;
-        }
-      }
+      for (int u = 0; u < 4; ++u) y[u] = row_val(j + u, c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float gj = gw[j + u];
@@ -115,11 +92,7 @@ __global__ __launch_bounds__(512) void k_combine(const float* __restrict__ Yrows
       acc.x += gj * y.x; acc.y += gj * y.y; acc.z += gj * y.z; acc.w += gj * y.w;
     }
     if (sh) {
-      float4 y = *(const float4*)(sh + c);
-      if (sh2) {
-        const float4 y2 = *(const float4*)(sh2 + c);
-        y.x += y2.x; y.y += y2.y; y.z += y2.z; y.w += y2.w;
-      }
+      const float4 y = *(const float4*)(sh + c);
       acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
     }
     if constexpr (sizeof(OutT) == 2) {
@@ -141,14 +114,14 @@ static int combine_tpt(int64_t k, int d) {
   return tpt;
 }
 
-template <typename OutT, bool KS>
-static void run_combine(int tpt, const float* Yrows, const float* Yrows2, const int32_t* slot_row,
-                        const float* w, int64_t T, int k, int d, const float* shared,
-                        const int32_t* shared_row0, OutT* Y, hipStream_t s) {
+template <typename OutT>
+static void run_combine(int tpt, const float* Yrows, const int32_t* slot_row, const float* w,
+                        int64_t T, int k, int d, const float* shared, const int32_t* shared_row0,
+                        OutT* Y, hipStream_t s) {
   const unsigned nb = (unsigned)MOE_CEIL_DIV(T, 512 / tpt);
 #define MOE_COMBINE(TPT_)                                                                      \
-  hipLaunchKernelGGL((k_combine<OutT, KS, TPT_>), dim3(nb), dim3(512), 0, s, Yrows, Yrows2,  \
-                     slot_row, w, T, k, d, shared, shared_row0, Y)
+  hipLaunchKernelGGL((k_combine<OutT, TPT_>), dim3(nb), dim3(512), 0, s, Yrows, slot_row, w, T, \
+                     k, d, shared, shared_row0, Y)
   switch (tpt) {
     case 64: MOE_COMBINE(64); break;
     case 128: MOE_COMBINE(128); break;
@@ -158,26 +131,15 @@ static void run_combine(int tpt, const float* Yrows, const float* Yrows2, const 
 #undef MOE_COMBINE
 }
 
-hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t* slot_row,
-                          const float* w, int64_t T, int k, int d, const float* shared,
-                          const int32_t* shared_row0, void* Y, int dtype, hipStream_t s) {
+hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
+                          int k, int d, const float* shared, const int32_t* shared_row0, void* Y,
+                          int dtype, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int tpt = combine_tpt(k, d);
-  if (dtype == MOE_BF16) {
-    if (Yrows2)
-      run_combine<uint16_t, true>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
-                                  (uint16_t*)Y, s);
-    else
-      run_combine<uint16_t, false>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
-                                   (uint16_t*)Y, s);
-  } else {
-    if (Yrows2)
-      run_combine<float, true>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
-                               (float*)Y, s);
-    else
-      run_combine<float, false>(tpt, Yrows, Yrows2, slot_row, w, T, k, d, shared, shared_row0,
-                                (float*)Y, s);
-  }
+  if (dtype == MOE_BF16)
+    run_combine<uint16_t>(tpt, Yrows, slot_row, w, T, k, d, shared, shared_row0, (uint16_t*)Y, s);
+  else
+    run_combine<float>(tpt, Yrows, slot_row, w, T, k, d, shared, shared_row0, (float*)Y, s);
   return hipGetLastError();
 }
 

@@ -1711,15 +1711,13 @@ static bool buf_fits(int64_t rows, int64_t K, int es) {
 
 // Runs both projections.  Groups [0, G) use W1/W3/W2 + g * stride; if
 // g_last >= 0, group g_last uses the separate (shared-expert) matrices.
-// Yrows receives the down projection, complete (tiles split along K are
-// summed inside the down kernel); *partial2 is always set to NULL.
+// Yrows receives the down projection (tiles split along K are summed by
+// k_tail_sum before this returns to the stream's next launch).
 hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int32_t* offsets,
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s, bool reduce, const float** partial2,
-                              const WeightScales* qs, int64_t a_rows) {
-  if (partial2) *partial2 = nullptr;
+                              hipStream_t s, const WeightScales* qs, int64_t a_rows) {
   if (max_rows <= 0 || G <= 0) return hipSuccess;
   const GemmPlan p = plan_for(dtype, max_rows, G, d, F);
   const int tail = down_tail(p, d, F);
@@ -1809,7 +1807,6 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
     run_gemm<float, 64, 128, 2, 2, false>(dn, s);
     timing_mark("ffn_down", s);
   }
-  (void)reduce;
   return hipGetLastError();
 }
 

@@ -71,8 +71,7 @@ hipError_t launch_router_gemm(const void* X, const void* Wg, int64_t T, int d, i
 struct WeightScales {
   const float *s1, *s3, *s2, *s1l, *s3l, *s2l;
 };
-// Yrows receives the complete down projection; *partial2 (if given) is set
-// to NULL and `reduce` has no effect (kept for the callers' interface).
+// Yrows receives the complete down projection.
 // q != NULL: W1/W3/W2 (and the g_last matrices) hold E4M3 codes, A is bf16.
 // a_rows: rows A holds (row_token indexes them), or -1 if not known; with a
 // bound the large bf16 tiles may address A through 32-bit offsets.
@@ -80,14 +79,13 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
                               int G, const void* W1, const void* W3, const void* W2,
                               const void* W1l, const void* W3l, const void* W2l, int g_last,
                               int dtype, int d, int F, int64_t max_rows, float* Yrows, void* ws,
-                              hipStream_t s, bool reduce, const float** partial2,
-                              const WeightScales* q = nullptr, int64_t a_rows = -1);
+                              hipStream_t s, const WeightScales* q = nullptr,
+                              int64_t a_rows = -1);
 
 // combine.hip
-// Yrows2 (optional): second K-split partial of the rows, added to Yrows.
-hipError_t launch_combine(const float* Yrows, const float* Yrows2, const int32_t* slot_row,
-                          const float* w, int64_t T, int k, int d, const float* shared,
-                          const int32_t* shared_row0, void* Y, int dtype, hipStream_t s);
+hipError_t launch_combine(const float* Yrows, const int32_t* slot_row, const float* w, int64_t T,
+                          int k, int d, const float* shared, const int32_t* shared_row0, void* Y,
+                          int dtype, hipStream_t s);
 
 // timing.hip: records a phase-boundary event when timing is enabled.
 void timing_mark(const char* name, hipStream_t s, int first = 0);
