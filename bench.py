@@ -233,11 +233,9 @@ def parse_marks(marks):
     return {k: float(np.mean(v)) for k, v in phases.items()}, steps_ms
 
 
-def measure(w, steps, warmup, keep_inputs=False):
-    """Time `steps` moe_forward calls of workload w with no instrumentation,
-    then `steps` more with phase events; returns the measurement dict (and
-    the inputs when asked)."""
-    import numpy as np
+def prepare(w):
+    """Inputs of workload w on the GPU, its layer, and one call with the
+    optional outputs for the per-expert row counts (untimed)."""
     import torch
     import mixture_experts_layer_47_amd as moe
     from mixture_experts_layer_47_amd.workloads import make_inputs
@@ -260,6 +258,23 @@ def measure(w, steps, warmup, keep_inputs=False):
                           (float(v) for v in probe.aux["health"].cpu().tolist())))
     del probe
     torch.cuda.empty_cache()
+    return {"w": w, "inp": inp, "layer": layer, "kept": kept, "n_kept": n_kept,
+            "balance": balance, "health": health}
+
+
+def measure(w, steps, warmup, keep_inputs=False, ctx=None):
+    """Time `steps` moe_forward calls of workload w with no instrumentation,
+    then `steps` more with phase events; returns the measurement dict (and
+    the inputs when asked).  ctx: the result of prepare(w), if done before."""
+    import numpy as np
+    import torch
+    import mixture_experts_layer_47_amd as moe
+
+    if ctx is None:
+        ctx = prepare(w)
+    inp, layer, kept, n_kept = ctx["inp"], ctx["layer"], ctx["kept"], ctx["n_kept"]
+    balance, health = ctx["balance"], ctx["health"]
+    del ctx
     fwd = moe.Forward(layer, inp["X"], aux=False)
     for _ in range(warmup):
         fwd()
@@ -366,7 +381,21 @@ def main():
 
     torch.cuda.set_device(torch.device("cuda:0"))
     w = WORKLOADS[args.workload]
-    head, inp = measure(w, args.steps, args.warmup, keep_inputs=not args.no_cpu_baseline)
+    ctx = prepare(w)
+    # The other layer shapes are timed first, so the headline's warm-up and
+    # timed steps run on a GPU that is already under load: started from idle,
+    # the first tens of steps run a few % slower while the clocks ramp up.
+    configs = {}
+    if not args.no_configs:
+        for tag, name in SUITE:
+            if name != w.name:
+                configs[tag], _ = measure(WORKLOADS[name], args.steps, args.warmup)
+    head, inp = measure(w, args.steps, args.warmup, keep_inputs=not args.no_cpu_baseline,
+                        ctx=ctx)
+    del ctx
+    if configs:
+        configs = {tag: (head if name == w.name else configs[tag]) for tag, name in SUITE
+                   if name == w.name or tag in configs}
     roof = dict(head["ffn_up"])
     roof["traffic"] = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
@@ -380,14 +409,6 @@ def main():
         cpu = cpu_baseline(w, inp, args.cpu_target_s)
         del inp
         torch.cuda.empty_cache()
-
-    configs = {}
-    if not args.no_configs:
-        for tag, name in SUITE:
-            if name == w.name:
-                configs[tag] = head
-                continue
-            configs[tag], _ = measure(WORKLOADS[name], args.steps, args.warmup)
 
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
