@@ -446,7 +446,13 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
         const int row = w * WROWS + 32 * i + rr;
         if (row < rows) {
           const u32x4 v = *(const u32x4*)(R2 + rr * E::RB + ((cc ^ (rr & 7)) << 4));
-          *(u32x4*)(obase + ((size_t)(rbeg + row) * N + n0) * E::ES + cc * 16) = v;
+          u32x4* dst = (u32x4*)(obase + ((size_t)(rbeg + row) * N + n0) * E::ES + cc * 16);
+          // fp32 y is read back only by the combine, after the whole
+          // projection: non-temporal stores (DeepSeek-V3 down -3 %)
+          if constexpr (GLU)
+            *dst = v;
+          else
+            __builtin_nontemporal_store(v, dst);
         }
       }
     }
