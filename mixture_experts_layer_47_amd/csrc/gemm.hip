@@ -1049,7 +1049,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 
 // ------------------------------------------------------- ping-pong variant
 // Both projections of the large tiles (experts with hundreds of rows, bf16
-// weights): 256 rows x 256 B rows per block (256 output columns of the down
+// or E4M3 weights): 256 rows x 256 B rows per block (256 output columns of the down
 // projection, or 128 gate and the 128 matching up columns), eight waves in
 // two groups of four (one wave of each group per SIMD).  Group gp owns rows
 // [128 gp, +128), wave wi 64 of the B rows: 4 x 2 accumulator blocks of
