@@ -1563,9 +1563,14 @@ static int down_tail(const GemmPlan& p, int d, int F) {
   return t;
 }
 
-// Workspace of the split tiles: `round` partial tiles of 256 x 256 floats.
-static size_t tail_ws_bytes(int tail) {
-  return tail > 1 ? (size_t)(num_cus() & ~7) * 256 * 256 * sizeof(float) : 0;
+// Workspace of the split tiles: partial tiles of BM x BN floats, one per
+// part; at most one dispatch round of parts, and at most `tail` parts per
+// tile the list can hold (few-tile shapes need few slots).
+static size_t tail_ws_bytes(int tail, int64_t max_rows, int G, int d) {
+  if (tail <= 1) return 0;
+  const int64_t tiles = max_work(max_rows, G, PPRing::BM, d, PPRing::BN);
+  const int64_t slots = std::min<int64_t>(num_cus() & ~7, tiles * tail);
+  return (size_t)slots * PPRing::BM * PPRing::BN * sizeof(float);
 }
 
 // Tile height the work lists are sized for (one plan serves bf16 and FP8
@@ -1585,7 +1590,7 @@ size_t ffn_ws_bytes(int64_t max_rows, int G, int d, int F, int dtype) {
   b += align256((size_t)wu * sizeof(int2)) + align256((size_t)wd * sizeof(int2));  // work lists
   b += align256(4 * sizeof(int32_t));                                  // entry counts
   b += align256((size_t)(G + 1) * sizeof(int32_t));                    // group bounds
-  b += tail_ws_bytes(tail);                                            // split tiles
+  b += tail_ws_bytes(tail, max_rows, G, d);                           // split tiles
   return b;
 }
 

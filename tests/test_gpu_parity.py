@@ -597,6 +597,58 @@ def test_grouped_ffn_random(seed):
     _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, 7000 + seed)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_down_tail_split_after_full_rounds(dtype):
+    """272 large down tiles (d 2048: 8 N-tiles; 8 experts of 1024 rows and
+    one of 512): on 256 CUs one full dispatch round runs whole tiles and the
+    last 16 (the 512-row expert's) are split along K in four parts of 1024.
+    Every row of that expert and sampled rows of the others against the
+    oracle, and the bits of two runs."""
+    _announce(f"moe_grouped_ffn tail split after full rounds {dtype}")
+    d, F = 2048, 4096
+    counts = [1024] * 8 + [512]
+    G = len(counts)
+    g = torch.Generator().manual_seed(41)
+    T = 1024
+    X = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    Ws = [torch.randn((G, F, d), generator=g) / d ** 0.5,
+          torch.randn((G, F, d), generator=g) / d ** 0.5,
+          torch.randn((G, d, F), generator=g) / F ** 0.5]
+    if dtype == "fp8":
+        q = [quantize_e4m3_rows(w) for w in Ws]
+        dev_w = [c.to(DEV) for c, _ in q]
+        scales = tuple(sc.to(DEV) for _, sc in q)
+        ref_w = [(c, sc) for c, sc in q]
+    else:
+        Ws = [w.to(torch.bfloat16) for w in Ws]
+        dev_w = [w.to(DEV) for w in Ws]
+        scales = None
+    R = sum(counts)
+    offs = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32)
+    tok = torch.randint(0, T, (R,), generator=g, dtype=torch.int32)
+    A = X[tok.long()].to(DEV)
+
+    def run():
+        return moe.grouped_ffn(A, offs.to(DEV), *dev_w, R, scales=scales)
+    Y = run()
+    torch.cuda.synchronize()
+    assert torch.equal(run(), Y)
+    Yh = H.np64(Y)
+    Xr = X[tok.long()].double().numpy()
+    for e in range(G):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if e == G - 1:
+            rows = np.arange(a, b)
+        else:
+            rows = np.unique(np.concatenate([[a, b - 1], np.random.default_rng(e).integers(a, b, 16)]))
+        if dtype == "fp8":
+            w1, w3, w2 = (O.dequantize_rows(c[e].numpy(), sc[e].numpy()) for c, sc in ref_w)
+        else:
+            w1, w3, w2 = (w[e].double().numpy() for w in Ws)
+        ref = O.expert_ffn(Xr[rows], w1.T, w3.T, w2.T, bf16_h=True)
+        H.check_rows(Yh[rows], ref, True)
+
+
 def _check_grouped_ffn(dtype, use_row_token, d, F, counts, slack, seed):
     G = len(counts)
     g = torch.Generator().manual_seed(seed)
