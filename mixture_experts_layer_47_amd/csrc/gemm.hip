@@ -35,8 +35,9 @@
 //     are bank-conflict free whether the LDS serves 8 or 16 lanes per cycle;
 //   * a wave skips the MFMAs of its 32-row blocks that lie past the tile's
 //     last row (a ragged last M-tile of an expert computes only live rows);
-//   * bf16: v_mfma_f32_32x32x16_bf16, each lane feeds 8 K-contiguous values
-//     per operand; fp32: four v_mfma_f32_32x32x2f32 per 16-B fragment;
+//   * bf16: v_mfma_f32_32x32x16_bf16 in the four-wave kernels and
+//     v_mfma_f32_16x16x32_bf16 in k_moe_pp, each lane feeding 8 K-contiguous
+//     values per operand; fp32: four v_mfma_f32_32x32x2f32 per 16-B fragment;
 //   * gate/up fusion: the B tile holds BN rows of W1 then BN rows of W3, a
 //     wave owns matching gate and up columns, and SwiGLU runs on the fp32
 //     accumulators before one rounding of h to the storage type;
