@@ -1135,6 +1135,15 @@ __device__ __forceinline__ void store_tile_pp(const f32x4 (&acc)[8][4], void* __
   }
 }
 
+// LDS swizzle of the ping-pong kernel's 128-B rows: chunk c of row r at slot
+// c ^ ((r >> 1) & 7).  Its 16x16x32 fragment reads put 16 lanes on 16
+// consecutive rows at one chunk and four chunks in one instruction; with
+// swz() that pattern measured 128 B/clk per CU on gfx950 (two-way bank
+// conflicts), with this form 256 B/clk, the rate of contiguous reads.  Rows
+// 2m and 2m + 1 share a slot and sit in opposite 128-B halves of a 256-B
+// bank line.
+__device__ __forceinline__ int swz_pp(int r) { return (r >> 1) & 7; }
+
 // A barrier that no instruction is scheduled across (the compiler may
 // otherwise hoist it past the MFMAs of a compute phase).
 __device__ __forceinline__ void fenced_barrier() {
@@ -1200,9 +1209,9 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   const TB* w1 = GLU ? ((g == g_last) ? (const TB*)B1lv : B1 + (size_t)g * N * K) + kbeg : w0;
 
   // This wave's copies: A rows wave * 32 + 8 i + lane / 8, chunk (lane % 8)
-  // ^ swz(row) of each 128-B row; B rows wave * 32 + RPB i + lane / CPB,
-  // chunk (lane % CPB) ^ swz_rb(row) (a copy's B rows lie in one of the
-  // W1 / W3 halves).  A rows past the tile's end re-read its first row
+  // ^ swz_pp(row) of each 128-B row; B rows wave * 32 + RPB i + lane / CPB,
+  // chunk (lane % CPB) ^ swz_pp(row) (bf16) or ^ swz_rb<64>(row) (FP8 codes)
+  // (a copy's B rows lie in one of the W1 / W3 halves).  A rows past the tile's end re-read its first row
   // (their outputs are never stored).
   // element offsets of this lane's copies from A + kbeg and from w0 / w1
   size_t ea[4], eb[NCB];
@@ -1211,7 +1220,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + lane / 8;
-    const int c = ((lane % 8) ^ swz(r & 31)) * 8;
+    const int c = ((lane % 8) ^ swz_pp(r)) * 8;
     int src = rbeg + (r < rows ? r : 0);
     if (GLU && row_token) src = row_token[src];
     ea[i] = (size_t)src * K + c;
@@ -1220,7 +1229,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
 #pragma unroll
   for (int i = 0; i < NCB; ++i) {
     const int r = wave * 32 + i * RPB + lane / CPB;
-    const int c = ((lane % CPB) ^ swz_rb<CPB * 16>(r & 31)) * (16 / (int)sizeof(TB));
+    const int c = ((lane % CPB) ^ (Q8 ? swz_rb<64>(r & 31) : swz_pp(r))) * (16 / (int)sizeof(TB));
     bhi[i] = GLU && wave * 32 + i * RPB >= TBN;
     eb[i] = (size_t)(n0 + (bhi[i] ? r - TBN : r)) * K + c;
     dsb[i] = (wave * 32 + i * RPB) * CPB;
@@ -1277,23 +1286,24 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   // 4 hh + l / 16 of the 64-K stage for substep hh, swizzled).  A blocks i:
   // rows 128 gp + 16 i; B blocks j: rows 64 wi + 16 j (GLU: j = 0, 1 gate
   // rows 32 wi + 16 j, j = 2, 3 the matching up rows TBN + 32 wi + 16 (j -
-  // 2)).  Every block starts at a multiple of 16, so its swizzle depends on
-  // the block's parity only.
+  // 2)).  Every block starts at a multiple of 16: the bf16 swizzle of a
+  // lane's rows depends on lane % 16 only, the FP8 one also on the block's
+  // parity.
   const int ra = 128 * gp + (lane & 15);
   int rb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     rb[j] = (GLU ? (j < 2 ? 32 * wi + 16 * j : TBN + 32 * wi + 16 * (j - 2)) : 64 * wi + 16 * j) +
             (lane & 15);
-  int csw[2][2], csb[2][2];
+  int csw[2], csb[2][2];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int hh = 0; hh < 2; ++hh) {
+    csw[hh] = (4 * hh + (lane >> 4)) ^ swz_pp(lane & 15);
+    // FP8 rows (64 B): chunk 2 hh + l / 32 holds 16 codes, half (l / 16) % 2 the lane's 8
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      csw[hh][p] = (4 * hh + (lane >> 4)) ^ swz(16 * p + (lane & 15));
-      // FP8 rows (64 B): chunk 2 hh + l / 32 holds 16 codes, half (l / 16) % 2 the lane's 8
-      csb[hh][p] = Q8 ? (2 * hh + (lane >> 5)) ^ swz_rb<64>(16 * p + (lane & 15)) : csw[hh][p];
-    }
+    for (int p = 0; p < 2; ++p)
+      csb[hh][p] = (2 * hh + (lane >> 5)) ^ swz_rb<64>(16 * p + (lane & 15));
+  }
   const int half = (lane >> 4) & 1;
   // live 32-row blocks of this wave's 128 rows: the rest skip their MFMAs
   const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * gp + 31) >> 5)));
@@ -1327,13 +1337,13 @@ __global__ __launch_bounds__(512) void k_moe_pp(
       for (int hh = 0; hh < 2; ++hh) {
         // ---- memory phase: fragments of k32 substep hh (live A blocks only)
 #pragma unroll
-        for (int i = 0; i < 2 * NV; ++i) fa[i] = ba[(ra + 16 * i) * 8 + csw[hh][i & 1]];
+        for (int i = 0; i < 2 * NV; ++i) fa[i] = ba[(ra + 16 * i) * 8 + csw[hh]];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (Q8)
             fb[j] = widen_e4m3(*((const uint2*)(bb + rb[j] * CPB + csb[hh][j & 1]) + half));
           else
-            fb[j] = bb[rb[j] * 8 + csw[hh][j & 1]];
+            fb[j] = bb[rb[j] * 8 + csw[hh]];
         }
         // A(S + 1) goes into the A buffer stage S - 1 used, B(S + 2) into
         // the B buffer of stage S - 1: both were last read in the previous
