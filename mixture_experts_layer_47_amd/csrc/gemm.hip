@@ -1087,7 +1087,8 @@ struct PPRing {
 // column cb + 16 j + r with cb the wave's first column + 4 (lane >> 4), so
 // every lane stores runs of four consecutive outputs of one row and the 16
 // lanes of one row offset together write 64 contiguous bytes of fp32 y (32
-// of bf16 h).  Rows past the tile's last row are masked per lane.
+// of bf16 h).  Rows at or past `rows` (one past the last row this group
+// owns) are masked per lane.
 //   GLU : gate blocks j = 0, 1 and the matching up blocks j + 2; h =
 //         silu(gate) * up, rounded once to bf16
 //   else: y in fp32
@@ -1289,7 +1290,15 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   // 2)).  Every block starts at a multiple of 16: the bf16 swizzle of a
   // lane's rows depends on lane % 16 only, the FP8 one also on the block's
   // parity.
-  const int ra = 128 * gp + (lane & 15);
+  // The tile's rows are split evenly between the groups in 16-row blocks:
+  // group 0 takes rows [0, hrow), group 1 rows [hrow, rows), hrow = 16
+  // ceil(rows / 32) (128 on a full tile).  On a partial tile both compute
+  // phases then stay about equally long, so neither waits on the other's
+  // memory phase more than the tile's rows require.
+  const int hrow = min(128, ((rows + 31) >> 5) << 4);
+  const int g0 = gp * hrow;                    // this group's first row
+  const int ghi = min(rows, g0 + hrow);        // one past its last row
+  const int ra = g0 + (lane & 15);
   int rb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -1305,8 +1314,8 @@ __global__ __launch_bounds__(512) void k_moe_pp(
       csb[hh][p] = (2 * hh + (lane >> 5)) ^ swz_rb<64>(16 * p + (lane & 15));
   }
   const int half = (lane >> 4) & 1;
-  // live 32-row blocks of this wave's 128 rows: the rest skip their MFMAs
-  const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 128 * gp + 31) >> 5)));
+  // live 16-row blocks of this group's rows: the rest skip their MFMAs
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, ghi - g0 + 15) >> 4);
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -1325,7 +1334,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
   wait_vm_lgkm<0>();
   fenced_barrier();
   if (gp == 1) fenced_barrier();
-  // The K loop for a wave with NV live 32-row blocks (compile time, so a
+  // The K loop for a wave with NV live 16-row blocks (compile time, so a
   // full tile's compute phases are straight runs of MFMAs); every wave runs
   // the same copies and barriers whatever its NV.
   auto kloop = [&](auto nv_c) {
@@ -1337,7 +1346,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
       for (int hh = 0; hh < 2; ++hh) {
         // ---- memory phase: fragments of k32 substep hh (live A blocks only)
 #pragma unroll
-        for (int i = 0; i < 2 * NV; ++i) fa[i] = ba[(ra + 16 * i) * 8 + csw[hh]];
+        for (int i = 0; i < NV; ++i) fa[i] = ba[(ra + 16 * i) * 8 + csw[hh]];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (Q8)
@@ -1361,7 +1370,7 @@ __global__ __launch_bounds__(512) void k_moe_pp(
         // ---- compute phase
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int i = 0; i < 2 * NV; ++i)
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1373,6 +1382,10 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     }
   };
   switch (nv) {
+    case 8: kloop(std::integral_constant<int, 8>{}); break;
+    case 7: kloop(std::integral_constant<int, 7>{}); break;
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
     case 4: kloop(std::integral_constant<int, 4>{}); break;
     case 3: kloop(std::integral_constant<int, 3>{}); break;
     case 2: kloop(std::integral_constant<int, 2>{}); break;
@@ -1387,16 +1400,16 @@ __global__ __launch_bounds__(512) void k_moe_pp(
     s1p = GLU ? ((g == g_last) ? sc1l : sc1 + (size_t)g * N) : nullptr;
   }
   if constexpr (GLU) {
-    store_tile_pp<true, Q8>(acc, out, N, rbeg, rows, 128 * gp, n0 + 32 * wi, lane, s0p, s1p);
+    store_tile_pp<true, Q8>(acc, out, N, rbeg, ghi, g0, n0 + 32 * wi, lane, s0p, s1p);
   } else if (lg == 0) {
-    store_tile_pp<false, Q8>(acc, out, N, rbeg, rows, 128 * gp, n0 + 64 * wi, lane, s0p, nullptr);
+    store_tile_pp<false, Q8>(acc, out, N, rbeg, ghi, g0, n0 + 64 * wi, lane, s0p, nullptr);
   } else {
     // A tile split along K (the work list's last tiles): part ks goes to
     // slot (ti 2^lg + ks) of `out2` (slots of BM x BN floats, row-major);
     // k_tail_sum adds the parts in part order once every part has ended.
     const int ti = (t - nwork[1]) >> lg;       // split tile index
     store_tile_pp<false, Q8>(acc, out2 + (size_t)((ti << lg) + ks) * (R::BM * R::BN), R::BN, 0,
-                             rows, 128 * gp, 64 * wi, lane, Q8 ? s0p + n0 : nullptr, nullptr);
+                             ghi, g0, 64 * wi, lane, Q8 ? s0p + n0 : nullptr, nullptr);
   }
 }
 
