@@ -562,6 +562,10 @@ FFN_SHAPES = {
     # large tiles, groups just above a multiple of 256 rows: their M-tiles are
     # of equal height (1045 rows: five tiles of 224 rows, the last 149)
     "large_uneven": (512, 512, [1045, 1069, 513, 289, 257, 33], 2),
+    # large tiles, groups of 1, 16, 17 and 48 rows beside full ones: the two
+    # wave groups split a tile's rows in 16-row blocks, so the second group
+    # has no row (1, 16), one partial block (17) or one full block (48)
+    "large_small_groups": (512, 512, [1000, 1, 16, 17, 48, 513], 2),
 }
 
 
