@@ -1052,9 +1052,10 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
 // Both projections of the large tiles (experts with hundreds of rows, bf16
 // or E4M3 weights): 256 rows x 256 B rows per block (256 output columns of the down
 // projection, or 128 gate and the 128 matching up columns), eight waves in
-// two groups of four (one wave of each group per SIMD).  Group gp owns rows
-// [128 gp, +128), wave wi 64 of the B rows: 8 x 4 accumulator blocks of
-// 16x16 (128 registers), so two waves share a SIMD.  The products run on
+// two groups of four (one wave of each group per SIMD).  Group 0 owns rows
+// [0, h) and group 1 rows [h, 2 h) of the tile, h = 16 ceil(rows / 32) (128
+// on a full tile); wave wi owns 64 of the B rows: up to 8 x 4 accumulator
+// blocks of 16x16 (128 registers), so two waves share a SIMD.  The products run on
 // v_mfma_f32_16x16x32_bf16: under the power limit that sets the clock of a
 // fully loaded GPU it sustains 6-10 % more than the 32x32x16 form at the
 // same LDS bytes per product (it moves fewer accumulator bytes per flop).
