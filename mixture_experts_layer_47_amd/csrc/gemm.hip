@@ -1613,6 +1613,19 @@ static GemmPlan plan_for(int dtype, int64_t max_rows, int G, int d, int F) {
   return {32, 2};
 }
 
+// Medium-plan projections with bf16 weights and a long reduction (K >= 4096,
+// 64 or more 64-K stages) run on the ping-pong kernel: the medium tiles' work
+// lists (256-row M-tiles, 128 gate/up and 256 down columns) are the
+// ping-pong kernel's, and with the rows of a ~128-row tile split 64 + 64
+// between its wave groups it streams the weights faster there (same GPU,
+// alternating builds: DeepSeek-V3 gate/up, K = 7168, 2991 -> 2863 us;
+// Switch down, K = 4096, 110 -> 109 us).  With K = 2048 its prologue and
+// epilogue weigh more and the four-wave kernel stays (DeepSeek-V3 down
+// 1879 us against 1935, Switch gate/up 240 against 249), and so it does for
+// FP8 weights, where the ping-pong kernel was slower on both shapes
+// (DeepSeek-V3 gate/up 2456 -> 2686 us, Switch down 92 -> 103 us).
+static bool medium_on_pp(int K) { return K >= 4096; }
+
 static int num_cus();
 
 // Upper bound of work entries for one projection with N-tile width BN (a
@@ -1871,7 +1884,11 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
         if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 2)) run_pp<true, true>(up, s);
         else run_pp<true, false>(up, s);
         break;
-      case 1: run_gemm_dma<256, 128, 1, 4, true, 128, 2, false, 3>(up, s); break;
+      case 1:
+        if (!medium_on_pp(d)) run_gemm_dma<256, 128, 1, 4, true, 128, 2, false, 3>(up, s);
+        else if (buf_fits(a_rows, d, 2) && buf_fits(F, d, 2)) run_pp<true, true>(up, s);
+        else run_pp<true, false>(up, s);
+        break;
       default: run_gemm<T, 32, 128, 1, 4, true>(up, s); break;
     }
     timing_mark("ffn_up", s);
@@ -1883,7 +1900,10 @@ hipError_t launch_grouped_ffn(const void* A, const int32_t* row_token, const int
         else run_gemm_dma<MOE_CFG0_BM, 128, 2, 2, false, 128, 2, false, MOE_CFG0_NBB>(dn, s);
         break;
       case 1:
-        if (b256) run_gemm_dma<256, 256, 1, 4, false, 128, 2, false, 3>(dn, s);
+        if (b256 && medium_on_pp(F) && buf_fits(max_rows, F, 2) && buf_fits(d, F, 2))
+          run_pp<false, true>(dn, s);
+        else if (b256 && medium_on_pp(F)) run_pp<false, false>(dn, s);
+        else if (b256) run_gemm_dma<256, 256, 1, 4, false, 128, 2, false, 3>(dn, s);
         else run_gemm_dma<256, 128, 1, 4, false, 128, 2, false, 3>(dn, s);
         break;
       default: run_gemm<T, 32, 128, 1, 4, false>(dn, s); break;

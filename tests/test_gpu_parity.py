@@ -566,6 +566,10 @@ FFN_SHAPES = {
     # wave groups split a tile's rows in 16-row blocks, so the second group
     # has no row (1, 16), one partial block (17) or one full block (48)
     "large_small_groups": (512, 512, [1000, 1, 16, 17, 48, 513], 2),
+    # medium tiles with a long reduction (bf16 on the ping-pong kernel):
+    # gate/up with K = d = 4096, then the down projection with K = F = 4096
+    "medium_long_d": (4096, 256, [0, 1, 150, 31, 64, 129, 7, 250], 3),
+    "medium_long_f": (256, 4096, [0, 1, 150, 31, 64, 129, 7, 250], 3),
 }
 
 
