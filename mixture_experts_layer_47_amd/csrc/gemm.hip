@@ -713,6 +713,7 @@ __device__ __forceinline__ void load_frags_dma(u32x4* f, const u32x4* pa, const 
 // slots of their region), swizzled chunk per substep.
 struct FragAddr {
   int fa, fb, half;
+  int rot;                  // first K stage of the tile's loop (stages taken cyclically)
   int cs[8], csb[8];
 };
 
@@ -764,6 +765,11 @@ __device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cu
 
 constexpr int gcd_i(int a, int b) { return b ? gcd_i(b, a % b) : a; }
 
+// K stage that the loop's stage x reads: x + rot taken modulo nk (x, rot < nk).
+__device__ __forceinline__ int kstage(int x, int rot, int nk) {
+  return x + rot >= nk ? x + rot - nk : x + rot;
+}
+
 // One iteration of the ring (see above) for stage s = s0 + h, h a
 // compile-time position in the ring period.
 template <int NV, int BM, int BN, int BNT, int FM, int FN, bool GLU, int KB, int NBA, int NBB,
@@ -787,12 +793,15 @@ __device__ __forceinline__ void ring_step(f32x16 (&acc)[FM][FN], const Ring& ra,
   __builtin_amdgcn_s_barrier();
   const int ta = s + NBA - 1, tb = s + NBB - 1;
   if constexpr (NBA > NBB)
-    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
+    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb,
+                               kstage(tb < nk ? tb : nk - 1, fr.rot, nk) * BK,
                                wave);
-  dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa, (ta < nk ? ta : nk - 1) * BK, wave,
+  dma_a<BM, BNT, KB, Q8>(ring((H + NBA - 1) % NBA, ra), pa,
+                         kstage(ta < nk ? ta : nk - 1, fr.rot, nk) * BK, wave,
                          alive);
   if constexpr (NBA <= NBB)
-    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb, (tb < nk ? tb : nk - 1) * BK,
+    dma_b<BM, BNT, KB, Q8, TB>(ring((H + NBB - 1) % NBB, rb), pb,
+                               kstage(tb < nk ? tb : nk - 1, fr.rot, nk) * BK,
                                wave);
   if constexpr (NV > 0)
     stage_mma<NV, BM, BN, BNT, FM, FN, GLU, KB, Q8>(acc, ring(H % NBA, ra), ring(H % NBB, rb),
@@ -837,12 +846,15 @@ __device__ __forceinline__ void main_loop_dma(f32x16 (&acc)[FM][FN], const Ring&
     const int sa = i + NBA - 1, sb = i + NBB - 1;
     if constexpr (NBA > NBB)
       dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
-                                 (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
+                                 kstage(sb < 0 ? 0 : (sb < nk ? sb : nk - 1), fr.rot, nk) * BK,
+                                 wave);
     dma_a<BM, BNT, KB, Q8>(ring(((sa % NBA) + NBA) % NBA, ra), pa,
-                           (sa < 0 ? 0 : (sa < nk ? sa : nk - 1)) * BK, wave, alive);
+                           kstage(sa < 0 ? 0 : (sa < nk ? sa : nk - 1), fr.rot, nk) * BK, wave,
+                           alive);
     if constexpr (NBA <= NBB)
       dma_b<BM, BNT, KB, Q8, TB>(ring(((sb % NBB) + NBB) % NBB, rb), pb,
-                                 (sb < 0 ? 0 : (sb < nk ? sb : nk - 1)) * BK, wave);
+                                 kstage(sb < 0 ? 0 : (sb < nk ? sb : nk - 1), fr.rot, nk) * BK,
+                                 wave);
   }
   u32x4 f0[NF], f1[NF];
 #pragma unroll
@@ -929,6 +941,16 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm_dma(
   const int nk = Kc / (KB / 2);
   const int g = wi.x & 1023;
   const int n0 = ((wi.x >> 10) & 16383) * BN;
+  // bf16 weights: N-tile n starts its K loop at stage n mod nk and takes the
+  // stages cyclically (the same sum in another order), so the tiles running
+  // at once read different 128-B pieces of their weight rows.  With every
+  // tile at the same K offset, rows a multiple of 4 KB apart crowded a few
+  // HBM channels, depending on where the weights sit in physical memory:
+  // the Switch-shaped gate/up took 239 or 202 us by allocation, 204 us
+  // rotated; the DeepSeek-V3 down projection 1832 -> 1704 us.  FP8 codes
+  // keep the plain order (rotated: DeepSeek-V3 down and FP8 decode down
+  // 1-2 % slower, the Switch shape 3-5 % faster).
+  fr.rot = (DENSE || Q8) ? 0 : ((wi.x >> 10) & 16383) % nk;
   const int ks = (int)((uint32_t)wi.x >> 24);
   const int kbeg = ks * Kc;
   const int gbeg = DENSE ? 0 : min(max(offsets[g], 0), max_rows);
