@@ -100,6 +100,11 @@ __device__ __forceinline__ void gload_tile(u32x4 (&ra)[CA], u32x4 (&rb)[CB],
 // distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
+// K stage that the loop's stage x reads: x + rot taken modulo nk (x, rot < nk).
+__device__ __forceinline__ int kstage(int x, int rot, int nk) {
+  return x + rot >= nk ? x + rot - nk : x + rot;
+}
+
 // Height of the M-tiles of a group of n rows: ceil(n / BM) tiles of equal
 // height rounded up to whole 32-row blocks (the last tile takes the rest).
 // A group slightly larger than a multiple of BM then gets a few slightly
@@ -205,8 +210,9 @@ __device__ __forceinline__ void sched_substep() {
 //                                          kt+1) to LDS buffer (kt+1)&1
 //   MFMA substep 2 (slot 0)             | read substep 3 (slot 1)
 //   barrier
-// so every global load has about 1.6 stages to arrive.  Loads past the last
-// stage re-fetch the last stage (in bounds, never used).  Slot 1 starts as
+// so every global load has about 1.6 stages to arrive.  Loop stage kt reads
+// K stage (kt + rot) mod nk.  Loads past the last stage re-fetch the last
+// stage (in bounds, never used).  Slot 1 starts as
 // zeros: the first iteration's leading MFMAs add 0.  nk is even (K is a
 // multiple of 128 elements), so the loop advances two stages at a time and
 // the staging sets keep fixed names.
@@ -214,15 +220,16 @@ template <typename T, int NV, int BM, int BN, int CA, int CB, int FM, int FN, bo
 __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1],
                                           const T* const (&oa)[CA], const T* pb0, const T* pb1,
                                           size_t bstep, int nk, int fa, int fb,
-                                          const int (&cs)[4], int tid) {
+                                          const int (&cs)[4], int tid, int rot) {
   constexpr int NF = FM + FN;
   constexpr int EPC = 16 / sizeof(T);
   constexpr int BK = 8 * EPC;
   u32x4* sm0 = smem[0];
   u32x4* sm1 = sm0 + (BM + (GLU ? 2 * BN : BN)) * 8;
   u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
-  gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, oa, pb0, pb1, bstep, 0);
-  gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, oa, pb0, pb1, bstep, (nk > 1 ? 1 : 0) * BK);
+  gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, oa, pb0, pb1, bstep, kstage(0, rot, nk) * BK);
+  gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, oa, pb0, pb1, bstep,
+                                 kstage(nk > 1 ? 1 : 0, rot, nk) * BK);
   lstore_tile<BM, CA, CB>(sm0, ra1, rb1, tid);
   __syncthreads();
   u32x4 f0[NF], f1[NF];
@@ -233,7 +240,7 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], u32x4 (*smem)[1
     for (int h = 0; h < 2; ++h) {
       const int k = kt + h;
       const u32x4* sm = h ? sm1 : sm0;
-      const int kn = (k + 2 < nk ? k + 2 : nk - 1) * BK;
+      const int kn = kstage(k + 2 < nk ? k + 2 : nk - 1, rot, nk) * BK;
       if (h == 0) gload_tile<T, CA, CB, GLU, BN>(ra1, rb1, oa, pb0, pb1, bstep, kn);
       else        gload_tile<T, CA, CB, GLU, BN>(ra0, rb0, oa, pb0, pb1, bstep, kn);
       if constexpr (NV > 0) {
@@ -514,6 +521,9 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     const int2 wi = work[t];
     const int g = wi.x & 1023;
     const int n0 = ((wi.x >> 10) & 16383) * BN;
+    // bf16: N-tile n starts its K loop at stage n mod nk, as in the LDS-direct
+    // kernel (decode-shaped down projection, 4-KB weight rows: 1159 -> 1113 us)
+    const int rot = sizeof(T) == 2 ? ((wi.x >> 10) & 16383) % nk : 0;
     const int ks = (int)((uint32_t)wi.x >> 24);   // K split of this entry
     const int kbeg = ks * Kc;
     const int gbeg = min(max(offsets[g], 0), max_rows);
@@ -550,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_gemm(
     auto* sm2 = reinterpret_cast<u32x4 (*)[1]>(&smem[0][0]);
 #define MOE_MAIN_LOOP(NV_)                                                                   \
   main_loop<T, NV_, BM, BN, CA, CB, FM, FN, GLU>(acc, sm2, oa, pb0, pb1, bstep, nk, fa, fb, cs, \
-                                                 tid)
+                                                 tid, rot)
     if (nv >= FM) {
       MOE_MAIN_LOOP(FM);
     } else if (nv == 0) {
@@ -765,10 +775,6 @@ __device__ __forceinline__ void stage_mma(f32x16 (&acc)[FM][FN], const u32x4* cu
 
 constexpr int gcd_i(int a, int b) { return b ? gcd_i(b, a % b) : a; }
 
-// K stage that the loop's stage x reads: x + rot taken modulo nk (x, rot < nk).
-__device__ __forceinline__ int kstage(int x, int rot, int nk) {
-  return x + rot >= nk ? x + rot - nk : x + rot;
-}
 
 // One iteration of the ring (see above) for stage s = s0 + h, h a
 // compile-time position in the ring period.
